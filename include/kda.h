@@ -1,0 +1,160 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * One operation is exported: the chunked (16-token) forward pass of Kimi Delta
+ * Attention with a 128 x 128 state per (sequence, head). It computes, for each
+ * sequence and head, token by token (Doubleword page "You Could Have Come Up
+ * with Kimi Delta Attention", section 4, boxed KDA equations):
+ *
+ *     S~ = S Diag(alpha_t);  e = beta_t (v_t - S~ k_t);  S = S~ + e k_t^T;
+ *     o_t = S (scale * q_t)
+ *
+ * after the activations the FlashKDA pages describe (instagit FlashKDA summary,
+ * "Chunked Token Processing"; DocSearch FlashKDA digest, "Configure
+ * fla_chunk_kda"): alpha_t = exp(lower_bound * sigmoid(g_raw_t)) per key
+ * channel, beta_t = sigmoid(beta_raw_t), and q_t, k_t L2-normalised per token
+ * as x / sqrt(sum x^2 + 1e-6). It is evaluated with the chunkwise method of the
+ * same Doubleword page, section 6, split into a chunk-parallel kernel and a
+ * per-(sequence, head) recurrence kernel.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named "device" point to GPU memory; all others to host memory.
+ *  - The caller owns every buffer. The library never allocates, frees or
+ *    synchronises, and keeps no global mutable state: calls are reentrant and
+ *    thread-safe as long as they do not share output or workspace buffers.
+ *  - Work is enqueued on the caller's HIP stream (passed as void*, NULL = the
+ *    null stream) and the call returns after enqueueing.
+ *  - All arguments are checked before anything is enqueued; a call that
+ *    returns an error has launched nothing and written nothing.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Head dimension K = V (the only one supported; DocSearch FlashKDA digest,
+ * "flash_kda.fwd API reference": K = V = 128). */
+#define KDA_HEAD_DIM 128
+/* Tokens per chunk (FlashKDA v1 deep-dive, section 1, "Chunk Size Selection"). */
+#define KDA_CHUNK 16
+/* Required alignment of the workspace base, in bytes (instagit FlashKDA
+ * summary, "State Management and Workspace Allocation": 128-byte aligned
+ * intermediate buffers). */
+#define KDA_WORKSPACE_ALIGN 128
+/* Accepted lower_bound range (the gate is g = lower_bound * sigmoid(g_raw);
+ * the pages use -5, FlashKDA review section 2.1). */
+#define KDA_LOWER_BOUND_MIN (-10.0f)
+#define KDA_LOWER_BOUND_MAX (0.0f)
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL_ARG = 1,    /* a required pointer is NULL                          */
+    KDA_ERR_BAD_SHAPE = 2,   /* head_dim != 128, H < 1, B/T/N out of range           */
+    KDA_ERR_BAD_DTYPE = 3,   /* unknown dtype code                                  */
+    KDA_ERR_BAD_SEQLENS = 4, /* cu_seqlens given with batch != 1, or N < 1           */
+    KDA_ERR_BAD_ARG = 5,     /* lower_bound / scale out of range or non-finite,
+                                unknown flag bits, or out aliasing an input        */
+    KDA_ERR_WORKSPACE = 6,   /* workspace NULL, too small, or not 128-B aligned     */
+    KDA_ERR_MISALIGNED = 7,  /* a tensor base address is not 16-B aligned           */
+    KDA_ERR_HIP = 8          /* a kernel launch failed (HIP runtime error)          */
+} kda_status_t;
+
+/* Element types. */
+typedef enum kda_dtype {
+    KDA_DTYPE_BF16 = 0,
+    KDA_DTYPE_FP32 = 1
+} kda_dtype_t;
+
+/* Flag bits for kda_desc_t.flags. */
+enum {
+    /* Use the fp32 reference kernels (no bf16 matrix-core operands) even for
+     * bf16 I/O. fp32 I/O always uses them. */
+    KDA_FLAG_FP32_COMPUTE = 1u
+};
+
+/*
+ * Problem description (host memory).
+ *
+ * Layouts (all row-major, DocSearch FlashKDA digest "flash_kda.fwd API
+ * reference"; instagit FlashKDA summary "Chunked Token Processing"):
+ *   q, k, g_raw, v, out : [B*T][H][128]  (batch rows flattened; with
+ *                          cu_seqlens B = 1 and the T_tot tokens are packed)
+ *   beta_raw            : [B*T][H]
+ *   initial/final state : [N][H][128 (value channel V)][128 (key channel K)]
+ *
+ * Without cu_seqlens every batch row is an independent sequence of length
+ * seqlen and num_seqs must equal batch. With cu_seqlens, batch must be 1,
+ * seqlen is T_tot and cu_seqlens holds num_seqs + 1 int32 token offsets.
+ */
+typedef struct kda_desc {
+    int64_t batch;       /* B >= 1                                           */
+    int64_t seqlen;      /* T >= 0 per batch row, or T_tot with cu_seqlens    */
+    int64_t num_seqs;    /* N >= 1 (== batch without cu_seqlens)              */
+    int32_t num_heads;   /* H >= 1                                            */
+    int32_t head_dim;    /* must be KDA_HEAD_DIM                              */
+    int32_t io_dtype;    /* kda_dtype_t of q, k, v, g_raw, beta_raw and out   */
+    int32_t state_dtype; /* kda_dtype_t of initial_state and final_state      */
+    float scale;         /* read scale s, finite and > 0 (usually 128^-1/2)   */
+    uint32_t flags;      /* KDA_FLAG_* bits                                   */
+} kda_desc_t;
+
+/*
+ * Bytes of device workspace kda_fwd needs for this description (a pure host
+ * function; no GPU call). The size is an upper bound computed from B, T, N
+ * and H only, because the chunk count of a packed batch depends on device-side
+ * cu_seqlens: at most (T_tot + 15 N) / 16 chunks. Returns 0 if the description
+ * itself is invalid (NULL, bad shape or dtype).
+ */
+size_t kda_fwd_workspace_size(const kda_desc_t *desc);
+
+/*
+ * Forward pass.
+ *   q, k, v, g_raw : device, io_dtype, [B*T][H][128]
+ *   beta_raw       : device, io_dtype, [B*T][H]
+ *   cu_seqlens     : device int32 [N+1] token offsets, or NULL (batch mode).
+ *                    Contents are the caller's contract (cu_seqlens[0] = 0,
+ *                    non-decreasing, cu_seqlens[N] = T_tot). The kernels clamp
+ *                    them into that form before use, so bad contents can give
+ *                    wrong results but never out-of-bounds accesses; the first
+ *                    int32 of the workspace is set to 1 if the offsets were
+ *                    valid and 0 if they had to be clamped.
+ *   initial_state  : device, state_dtype, [N][H][128][128], or NULL (= zeros)
+ *   out            : device, io_dtype, like v; must not overlap any input
+ *   final_state    : device, state_dtype, [N][H][128][128], or NULL (not
+ *                    written). May be the same buffer as initial_state
+ *                    (in-place streaming); partial overlap is not allowed.
+ *   lower_bound    : gate bound in [KDA_LOWER_BOUND_MIN, KDA_LOWER_BOUND_MAX]
+ *   desc           : host, problem description
+ *   workspace      : device, >= kda_fwd_workspace_size(desc) bytes, 128-B
+ *                    aligned; contents on entry are ignored
+ *   stream         : hipStream_t, or NULL for the null stream
+ * Tensor bases must be 16-B aligned (beta_raw: element-aligned).
+ * A sequence of length 0 gets final_state = initial_state (or zeros).
+ * B*T = 0 with batch mode is a no-op apart from writing final_state.
+ */
+kda_status_t kda_fwd(const void *q, const void *k, const void *v,
+                     const void *g_raw, const void *beta_raw,
+                     const int32_t *cu_seqlens,
+                     const void *initial_state,
+                     void *out, void *final_state,
+                     float lower_bound,
+                     const kda_desc_t *desc,
+                     void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *kda_status_str(kda_status_t status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

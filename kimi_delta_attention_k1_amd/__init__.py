@@ -1,0 +1,177 @@
+"""Kimi Delta Attention forward on MI355X (gfx950): Python binding.
+
+This module only marshals arguments into the C ABI of libkda.so (declared in
+include/kda.h). Every step of the computation runs in the library's HIP
+kernels; PyTorch provides device memory and the current stream. There is no
+CPU or PyTorch fallback: if the library is missing the calls raise.
+
+    out, final_state = fwd(q, k, v, g_raw, beta_raw, lower_bound=-5.0,
+                           initial_state=None, output_final_state=True,
+                           cu_seqlens=None)
+
+Layouts follow the FlashKDA API (DocSearch FlashKDA digest, "flash_kda.fwd API
+reference"): q, k, v, g_raw are [B, T, H, 128] (or packed [T_tot, H, 128]),
+beta_raw is [B, T, H] (or [T_tot, H]); states are [N, H, 128 (V), 128 (K)];
+with cu_seqlens (int32, N+1 offsets) B must be 1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["fwd", "workspace_size", "KdaError", "load_library", "library_path", "seqlens_flag",
+           "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE"]
+
+HEAD_DIM = 128
+CHUNK = 16
+FLAG_FP32_COMPUTE = 1
+DTYPE_BF16 = 0
+DTYPE_FP32 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+_lib = None
+
+
+class KdaDesc(ctypes.Structure):
+    """Mirror of kda_desc_t."""
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("num_seqs", ctypes.c_int64),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("state_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"kda_fwd failed with status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libkda.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it first (python -m kimi_delta_attention_k1_amd.build "
+                           "or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(KdaDesc)]
+    lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.POINTER(KdaDesc),
+                            vp, ctypes.c_size_t, vp]
+    lib.kda_status_str.restype = ctypes.c_char_p
+    lib.kda_status_str.argtypes = [ctypes.c_int]
+    lib.kda_version.restype = ctypes.c_int
+    lib.kda_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def make_desc(batch, seqlen, num_seqs, num_heads, io_dtype, state_dtype, scale, flags=0,
+              head_dim=HEAD_DIM) -> KdaDesc:
+    return KdaDesc(int(batch), int(seqlen), int(num_seqs), int(num_heads), int(head_dim), int(io_dtype),
+                   int(state_dtype), float(scale), int(flags))
+
+
+def status_str(status: int) -> str:
+    return load_library().kda_status_str(int(status)).decode()
+
+
+def workspace_size(batch, seqlen, num_seqs, num_heads, io_dtype=DTYPE_BF16, state_dtype=DTYPE_FP32,
+                   fp32_compute=False) -> int:
+    d = make_desc(batch, seqlen, num_seqs, num_heads, io_dtype, state_dtype, HEAD_DIM ** -0.5,
+                  FLAG_FP32_COMPUTE if fp32_compute else 0)
+    return int(load_library().kda_fwd_workspace_size(ctypes.byref(d)))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}: bf16 or fp32 expected")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def fwd(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | None = None,
+        initial_state=None, output_final_state: bool = True, cu_seqlens=None, out=None, final_state=None,
+        workspace=None, fp32_compute: bool = False, stream=None):
+    """KDA forward through kda_fwd. Returns (out, final_state or None).
+
+    All tensors must be contiguous and on the same GPU. `stream` is a
+    torch.cuda.Stream (default: the current stream). `workspace` may be a
+    preallocated uint8 tensor of at least workspace_size(...) bytes.
+    """
+    import torch
+    lib = load_library()
+    tensors = (q, k, v, g_raw, beta_raw)
+    for t in tensors:
+        if not t.is_contiguous():
+            raise ValueError("kda.fwd needs contiguous inputs")
+    if q.dim() == 4:
+        B, T, H, D = q.shape
+    elif q.dim() == 3:
+        B, (T, H, D) = 1, q.shape
+    else:
+        raise ValueError("q must be [B,T,H,128] or [T_tot,H,128]")
+    for t in (k, v, g_raw):
+        if t.shape != q.shape:
+            raise ValueError("q, k, v and g_raw must have the same shape")
+    if tuple(beta_raw.shape) != tuple(q.shape[:-1]):
+        raise ValueError("beta_raw must have the shape of q without the last dimension")
+    io = _dtype_code(q)
+    if any(_dtype_code(t) != io for t in tensors):
+        raise TypeError("q, k, v, g_raw and beta_raw must share one dtype")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
+        N = cu_seqlens.shape[0] - 1
+        seqlen = B * T
+    else:
+        N = B
+        seqlen = T
+    if initial_state is not None and final_state is not None and initial_state.dtype != final_state.dtype:
+        raise TypeError("initial_state and final_state must have the same dtype")
+    st_t = initial_state if initial_state is not None else final_state
+    st_code = _dtype_code(st_t) if st_t is not None else DTYPE_FP32
+    for s in (initial_state, final_state):
+        if s is not None and (tuple(s.shape) != (N, H, D, D) or not s.is_contiguous()):
+            raise ValueError(f"states must be contiguous [{N}, {H}, {D}, {D}]")
+    if out is None:
+        out = torch.empty_like(v)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, D, D), dtype=st_t.dtype if st_t is not None else torch.float32,
+                                  device=q.device)
+    if scale is None:
+        scale = D ** -0.5
+    flags = FLAG_FP32_COMPUTE if fp32_compute else 0
+    desc = make_desc(B, seqlen, N, H, io, st_code, scale, flags, head_dim=D)
+    need = int(lib.kda_fwd_workspace_size(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace too small: {workspace.numel()} < {need} bytes")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(cu_seqlens),
+                     _ptr(initial_state), _ptr(out), _ptr(final_state), float(lower_bound), ctypes.byref(desc),
+                     _ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise KdaError(st, lib.kda_status_str(st).decode())
+    return out, final_state
+
+
+def seqlens_flag(workspace) -> int:
+    """1 if the cu_seqlens of the last call on this workspace were well formed
+    (reads the workspace's first int32; synchronises on it)."""
+    return int(workspace[:4].view(dtype=__import__("torch").int32).item())

@@ -1,0 +1,156 @@
+// kda_api.hip -- host side of the C ABI declared in include/kda.h: argument
+// validation (pure host code, nothing touches the GPU before it passes),
+// workspace carve-up and the kernel launches on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+using kda::Problem;
+using kda::WsLayout;
+
+constexpr int kVersion = 100;  // 0.1.0
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
+};
+Range range_of(const void *p, size_t bytes)
+{
+    uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, p ? a + bytes : a};
+}
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Shape {
+    int64_t T_tot, n_c_max;
+    bool f32_path;
+};
+
+// Shape-level checks shared by the size query and the forward call.
+kda_status_t check_desc(const kda_desc_t *d, bool varlen, Shape *out)
+{
+    if (!d) return KDA_ERR_NULL_ARG;
+    if (d->head_dim != KDA_HEAD_DIM || d->num_heads < 1 || d->batch < 1 || d->seqlen < 0 || d->num_seqs < 1)
+        return KDA_ERR_BAD_SHAPE;
+    if ((d->io_dtype != KDA_DTYPE_BF16 && d->io_dtype != KDA_DTYPE_FP32) ||
+        (d->state_dtype != KDA_DTYPE_BF16 && d->state_dtype != KDA_DTYPE_FP32))
+        return KDA_ERR_BAD_DTYPE;
+    if (d->flags & ~(uint32_t)KDA_FLAG_FP32_COMPUTE) return KDA_ERR_BAD_ARG;
+    int64_t T_tot, n_c_max;
+    const int64_t lim = (int64_t)1 << 30;  // tokens and sequences addressed with int32 on the device
+    if (varlen) {
+        if (d->batch != 1) return KDA_ERR_BAD_SEQLENS;
+        if (d->seqlen >= lim || d->num_seqs >= lim) return KDA_ERR_BAD_SHAPE;
+        T_tot = d->seqlen;
+        n_c_max = (T_tot + (int64_t)(KDA_CHUNK - 1) * d->num_seqs) / KDA_CHUNK;
+    } else {
+        if (d->num_seqs != d->batch) return KDA_ERR_BAD_SHAPE;
+        if (d->batch >= lim || d->seqlen >= lim || d->batch * d->seqlen >= lim) return KDA_ERR_BAD_SHAPE;
+        T_tot = d->batch * d->seqlen;
+        n_c_max = d->batch * ((d->seqlen + KDA_CHUNK - 1) / KDA_CHUNK);
+    }
+    if (n_c_max * (int64_t)d->num_heads >= ((int64_t)1 << 31)) return KDA_ERR_BAD_SHAPE;
+    out->T_tot = T_tot;
+    out->n_c_max = n_c_max;
+    out->f32_path = d->io_dtype == KDA_DTYPE_FP32 || (d->flags & KDA_FLAG_FP32_COMPUTE);
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc)
+{
+    // Whether cu_seqlens will be passed is not part of the description, so
+    // take the larger bound over the readings the description allows.
+    size_t best = 0;
+    for (int varlen = 0; varlen < 2; ++varlen) {
+        Shape s;
+        if (check_desc(desc, varlen != 0, &s) != KDA_OK) continue;
+        size_t b = kda::ws_layout(desc->num_seqs, desc->num_heads, s.n_c_max, s.f32_path).total;
+        if (b > best) best = b;
+    }
+    return best;
+}
+
+extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g_raw,
+                                const void *beta_raw, const int32_t *cu_seqlens, const void *initial_state,
+                                void *out, void *final_state, float lower_bound, const kda_desc_t *desc,
+                                void *workspace, size_t workspace_bytes, void *stream)
+{
+    Shape s;
+    const bool varlen = cu_seqlens != nullptr;
+    kda_status_t st = check_desc(desc, varlen, &s);
+    if (st != KDA_OK) return st;
+    if (!isfinite(lower_bound) || lower_bound < KDA_LOWER_BOUND_MIN || lower_bound > KDA_LOWER_BOUND_MAX)
+        return KDA_ERR_BAD_ARG;
+    if (!isfinite(desc->scale) || !(desc->scale > 0.f)) return KDA_ERR_BAD_ARG;
+
+    const int64_t H = desc->num_heads, N = desc->num_seqs;
+    const size_t esz = desc->io_dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const size_t ssz = desc->state_dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const size_t tens = (size_t)s.T_tot * H * KDA_HEAD_DIM * esz;
+    const size_t bet = (size_t)s.T_tot * H * esz;
+    const size_t sts = (size_t)N * H * KDA_HEAD_DIM * KDA_HEAD_DIM * ssz;
+
+    if (s.T_tot > 0 && (!q || !k || !v || !g_raw || !beta_raw || !out)) return KDA_ERR_NULL_ARG;
+    if (!workspace) return KDA_ERR_WORKSPACE;
+    const WsLayout lay = kda::ws_layout(N, H, s.n_c_max, s.f32_path);
+    if (workspace_bytes < lay.total || !aligned(workspace, KDA_WORKSPACE_ALIGN)) return KDA_ERR_WORKSPACE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g_raw, 16) || !aligned(out, 16) ||
+        !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(beta_raw, esz))
+        return KDA_ERR_MISALIGNED;
+    if (varlen && !aligned(cu_seqlens, 4)) return KDA_ERR_MISALIGNED;
+
+    // Overlap rules: out and the workspace touch nothing else; final_state may
+    // only coincide exactly with initial_state.
+    const Range rq = range_of(q, tens), rk = range_of(k, tens), rv = range_of(v, tens), rg = range_of(g_raw, tens);
+    const Range rb = range_of(beta_raw, bet), ro = range_of(out, tens);
+    const Range r0 = range_of(initial_state, sts), r1 = range_of(final_state, sts);
+    const Range rw = range_of(workspace, lay.total);
+    const Range rc = range_of(cu_seqlens, varlen ? sizeof(int32_t) * (size_t)(N + 1) : 0);
+    const Range others[] = {rq, rk, rv, rg, rb, rc};
+    for (const Range &r : others)
+        if (overlap(ro, r) || overlap(rw, r) || overlap(r1, r)) return KDA_ERR_BAD_ARG;
+    if (overlap(ro, r0) || overlap(rw, r0) || overlap(ro, rw) || overlap(ro, r1) || overlap(rw, r1))
+        return KDA_ERR_BAD_ARG;
+    if (overlap(r0, r1) && r0.lo != r1.lo) return KDA_ERR_BAD_ARG;  // equal sizes: same base = same buffer
+
+    Problem p;
+    p.q = q; p.k = k; p.v = v; p.g = g_raw; p.beta = beta_raw;
+    p.cu = cu_seqlens; p.s0 = initial_state; p.out = out; p.s1 = final_state;
+    p.lb = lower_bound; p.scale = desc->scale;
+    p.B = desc->batch; p.T = desc->seqlen; p.N = N; p.T_tot = s.T_tot; p.n_c_max = s.n_c_max;
+    p.H = (int)H;
+    p.io_bf16 = desc->io_dtype == KDA_DTYPE_BF16;
+    p.st_bf16 = desc->state_dtype == KDA_DTYPE_BF16;
+    p.f32_path = s.f32_path;
+    p.ws = static_cast<char *>(workspace);
+    p.lay = lay;
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (kda::launch_chunk_map(p, hs) != hipSuccess) return KDA_ERR_HIP;
+    hipError_t e = p.f32_path ? kda::launch_ref(p, hs) : kda::launch_mfma(p, hs);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+extern "C" const char *kda_status_str(kda_status_t status)
+{
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case KDA_ERR_BAD_SHAPE: return "bad shape (head_dim must be 128; H, B, N >= 1; T >= 0; sizes in range)";
+    case KDA_ERR_BAD_DTYPE: return "unknown dtype code";
+    case KDA_ERR_BAD_SEQLENS: return "cu_seqlens requires batch == 1";
+    case KDA_ERR_BAD_ARG: return "bad argument (lower_bound, scale, flags, or overlapping buffers)";
+    case KDA_ERR_WORKSPACE: return "workspace missing, too small or not 128-byte aligned";
+    case KDA_ERR_MISALIGNED: return "a tensor base address is not 16-byte aligned";
+    case KDA_ERR_HIP: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+extern "C" int kda_version(void) { return kVersion; }

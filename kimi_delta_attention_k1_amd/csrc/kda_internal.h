@@ -1,0 +1,125 @@
+// kda_internal.h -- shared definitions of the KDA forward library (not part of
+// the public ABI). Workspace layout, launch parameters and small device helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kD = 128;     // head dimension K = V
+constexpr int kC = 16;      // tokens per chunk
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kL2Eps = 1e-6f;  // L2-norm epsilon: x / sqrt(sum x^2 + eps)
+
+// ---------------------------------------------------------------------------
+// Workspace layout.
+//
+//   [header 128 B] [tok_off: (N+1) int32] [chunk_off: (N+1) int32] [units]
+//
+// tok_off[n]  : first token of sequence n (sanitised copy of cu_seqlens).
+// chunk_off[n]: first global chunk of sequence n; chunk_off[N] = chunks in use.
+// A "unit" is one (chunk, head). Unit u = h * n_c_max + global_chunk holds what
+// the chunk-parallel kernel hands the recurrence kernel; the chunks of one
+// (sequence, head) are therefore contiguous.
+//
+// bf16 path unit (14848 B), every block in the lane order the recurrence
+// kernel's matrix-core instructions consume (64 lanes x 16 B per 1 KB slab):
+//   KB   4096  K_b  = khat * exp(G_i)           bf16, 16x16x32 A-operand order
+//   QB   4096  Q_b  = s qhat * exp(G_i)         bf16, same order
+//   KE   4096  K_end= khat * exp(G_last - G_i)  bf16, 16x16x16 A-operand order
+//   AB   1024  (A^kk Diag(beta))^T              fp32, lane-major float4
+//   AQ   1024  (A^qk)^T                         fp32, lane-major float4
+//   GM    512  gamma = exp(G_last)              fp32 [128]
+// fp32 path unit (27136 B), plain row-major:
+//   KB 8192 [16][128], QB 8192, KE 8192, AB 1024 [16][16] (A^kk Diag(beta)),
+//   AQ 1024 [16][16] (A^qk), GM 512.
+// ---------------------------------------------------------------------------
+constexpr size_t kHeaderBytes = 128;
+
+struct UnitLayout {
+    size_t kb, qb, ke, ab, aq, gm, bytes;
+};
+constexpr UnitLayout kUnitBf16 = {0, 4096, 8192, 12288, 13312, 14336, 14848};
+constexpr UnitLayout kUnitF32 = {0, 8192, 16384, 24576, 25600, 26624, 27136};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+    size_t tok_off, chunk_off, units, unit_bytes, total;
+    int64_t n_c_max;
+};
+
+inline WsLayout ws_layout(int64_t N, int64_t H, int64_t n_c_max, bool f32_path)
+{
+    WsLayout L;
+    L.tok_off = kHeaderBytes;
+    L.chunk_off = align_up(L.tok_off + sizeof(int32_t) * (size_t)(N + 1), 128);
+    L.units = align_up(L.chunk_off + sizeof(int32_t) * (size_t)(N + 1), 128);
+    L.unit_bytes = f32_path ? kUnitF32.bytes : kUnitBf16.bytes;
+    L.n_c_max = n_c_max;
+    L.total = L.units + L.unit_bytes * (size_t)H * (size_t)n_c_max;
+    return L;
+}
+
+// Everything a launch needs (device pointers and sizes, already validated).
+struct Problem {
+    const void *q, *k, *v, *g, *beta;
+    const int32_t *cu;      // device or nullptr
+    const void *s0;         // device or nullptr
+    void *out, *s1;         // out device; s1 device or nullptr
+    float lb, scale;
+    int64_t B, T, N, T_tot, n_c_max;
+    int H;
+    bool io_bf16, st_bf16, f32_path;
+    char *ws;
+    WsLayout lay;
+};
+
+hipError_t launch_chunk_map(const Problem &p, hipStream_t s);
+hipError_t launch_ref(const Problem &p, hipStream_t s);
+hipError_t launch_mfma(const Problem &p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b)
+{
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float ld_elem(const T *p, int64_t i);
+template <> __device__ __forceinline__ float ld_elem<float>(const float *p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t *p, int64_t i)
+{
+    return bf16_bits_to_f32(p[i]);
+}
+template <typename T> __device__ __forceinline__ void st_elem(T *p, int64_t i, float x);
+template <> __device__ __forceinline__ void st_elem<float>(float *p, int64_t i, float x) { p[i] = x; }
+template <> __device__ __forceinline__ void st_elem<uint16_t>(uint16_t *p, int64_t i, float x)
+{
+    p[i] = f32_to_bf16_bits(x);
+}
+
+// Sequence owning global chunk c: largest n in [0, N) with chunk_off[n] <= c.
+__device__ __forceinline__ int find_seq(const int32_t *chunk_off, int N, int c)
+{
+    int lo = 0, hi = N;  // invariant: chunk_off[lo] <= c < chunk_off[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (chunk_off[mid] <= c) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+}  // namespace kda

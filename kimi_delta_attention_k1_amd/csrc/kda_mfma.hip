@@ -1,0 +1,457 @@
+// kda_mfma.hip -- bf16 matrix-core path of the KDA forward for gfx950 (CDNA4).
+//
+// Method: the chunkwise form of the KDA recurrence on the Doubleword page "You
+// Could Have Come Up with Kimi Delta Attention", section 6, with 16-token
+// chunks (FlashKDA v1 deep-dive, section 1) and the two-kernel split of the
+// FlashKDA pages (deep-dive section 2): a chunk-parallel kernel (K1) and a
+// per-(sequence, head) recurrence (K2).
+//
+// Per chunk c of one (sequence, head), with G the in-chunk prefix sum of the
+// log-decay (section 6.6), K_b rows khat_i exp(G_i), Q_b rows s qhat_i exp(G_i),
+// K_end rows khat_j exp(G_last - G_j) (section 6.4), R and A^qk the causal
+// coefficient matrices rho, chi (sections 6.3, 6.5) and A^kk = (I+R)^-1:
+//   K1:  G, R, A^kk Diag(beta), A^qk, K_b, Q_b, K_end, gamma = exp(G_last)
+//   K2:  Ebar = V - K_b S_c^T               (rows v_i - S_c D_{0:i} k_i)
+//        E    = A^kk Diag(beta) Ebar        (section 6.3, E = Ebar A^kk^T in columns)
+//        O    = Q_b S_c^T + A^qk E          (section 6.5)
+//        S_{c+1}^T = Diag(gamma) S_c^T + K_end^T E   (section 6.4)
+//
+// Matrix-core instruction layouts relied on (64 lanes, lane l, g = l/16):
+//   16x16x32 bf16: A lane l = row l%16, 8 k values; B lane l = column l%16,
+//                  the same 8 k labels; D lane l = rows 4g..4g+3, column l%16.
+//   16x16x16 bf16: as above with 4 k values (k = 4g..4g+3 matches D's rows).
+//   16x16x4  f32 : A lane l = row l%16, k = g; B lane l = column l%16, k = g.
+// Because a D fragment has the B-operand layout of a 16x16x16 product, the
+// fp32 state and the error tiles feed the next product from registers. The
+// contraction order inside a 32-wide k step is a free permutation, which K1
+// uses to write K_b and Q_b so that the state accumulators of two 16-row tiles
+// form one 16x16x32 B operand without data movement.
+#include "kda_internal.h"
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
+                                                      0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// x = hi + lo with hi, lo bf16: about 16 significant bits between them.
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo)
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        __bf16 h = (__bf16)x[r];
+        hi[r] = h;
+        lo[r] = (__bf16)(x[r] - (float)h);
+    }
+}
+
+// logistic sigmoid from 2^x and a reciprocal
+__device__ __forceinline__ float sigmoid_fast(float x)
+{
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+
+// value of lane (l - n) of the same 16-lane row, 0 for lanes below n
+template <int N> __device__ __forceinline__ float row_shr(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
+}
+
+// C = X Y for 16x16 fp32 tiles; xt holds X^T and y holds Y, both in D layout.
+__device__ __forceinline__ f32x4 mm16_f32(f32x4 xt, f32x4 y)
+{
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mma4(xt[s], y[s], acc);
+    return acc;
+}
+
+// I + a*X in D layout (row 4g+r, column tok)
+__device__ __forceinline__ f32x4 eye_plus(f32x4 x, float a, int g, int tok)
+{
+    f32x4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = a * x[r] + ((4 * g + r == tok) ? 1.f : 0.f);
+    return y;
+}
+
+// ---------------------------------------------------------------------------
+// K1: one wave per (chunk, head). Lane l holds token l%16 and key channels
+// [32 g, 32 g + 32), g = l/16, so each 16-lane row is one channel group across
+// the 16 tokens of the chunk.
+// ---------------------------------------------------------------------------
+constexpr int kK1MaxWaves = 4;
+
+__global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ graw,
+    const uint16_t *__restrict__ braw, const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off,
+    int N, int H, int64_t n_c_max, float lb, float scale, char *__restrict__ units)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t sKE[kK1MaxWaves][kD][kC];  // K_end as [channel][token]
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c = blockIdx.x;
+    const int h = blockIdx.y * (blockDim.x >> 6) + wv;  // blockDim.x / 64 divides H
+    if (c >= chunk_off[N]) return;                     // uniform over the block
+    const int n = find_seq(chunk_off, N, c);
+    const int t0 = tok_off[n] + (c - chunk_off[n]) * kC;
+    const int len = min(kC, tok_off[n + 1] - t0);
+    const int tok = lane & 15, g = lane >> 4;
+    const bool valid = tok < len;
+
+    // ---- load q, k, g_raw (32 channels each) and beta_raw; padded tokens are absent (all zero)
+    float qf[32], kf[32], gf[32];
+    if (valid) {
+        const int64_t off = ((int64_t)(t0 + tok) * H + h) * kD + 32 * g;
+        const u32x4 *pq = reinterpret_cast<const u32x4 *>(q + off);
+        const u32x4 *pk = reinterpret_cast<const u32x4 *>(k + off);
+        const u32x4 *pg = reinterpret_cast<const u32x4 *>(graw + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u32x4 a = pq[i], b = pk[i], d = pg[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qf[8 * i + 2 * e] = bf_lo(a[e]);
+                qf[8 * i + 2 * e + 1] = bf_hi(a[e]);
+                kf[8 * i + 2 * e] = bf_lo(b[e]);
+                kf[8 * i + 2 * e + 1] = bf_hi(b[e]);
+                gf[8 * i + 2 * e] = bf_lo(d[e]);
+                gf[8 * i + 2 * e + 1] = bf_hi(d[e]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) qf[i] = kf[i] = gf[i] = 0.f;
+    }
+    const float beta =
+        valid ? sigmoid_fast(bf16_bits_to_f32(braw[(int64_t)(t0 + tok) * H + h])) : 0.f;
+
+    // ---- gate (log2 units) and in-chunk inclusive prefix sum over tokens
+    const float lb2 = lb * kLog2e;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        float x = valid ? lb2 * sigmoid_fast(gf[i]) : 0.f;
+        x += row_shr<1>(x);
+        x += row_shr<2>(x);
+        x += row_shr<4>(x);
+        x += row_shr<8>(x);
+        gf[i] = x;  // G_tok (log2)
+    }
+
+    // ---- L2 norms over 128 channels: 32 per lane, 4 lanes per token
+    float nq = 0.f, nk = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        nq += qf[i] * qf[i];
+        nk += kf[i] * kf[i];
+    }
+    nq += __shfl_xor(nq, 16);
+    nq += __shfl_xor(nq, 32);
+    nk += __shfl_xor(nk, 16);
+    nk += __shfl_xor(nk, 32);
+    const float rq = scale * __builtin_amdgcn_rsqf(nq + kL2Eps);  // s folded into qhat
+    const float rk = __builtin_amdgcn_rsqf(nk + kL2Eps);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        qf[i] *= rq;
+        kf[i] *= rk;
+    }
+
+    // ---- R = strict_tril(Diag(beta) K' K''^T), R^T, (A^qk)^T with K' = khat e^{G-Gref},
+    //      K'' = khat e^{Gref-G}, Gref = G at token 7 (keeps both factors within e^{+-8|lb|}).
+    //      bf16 hi/lo split products: fp32-level accuracy from the bf16 matrix cores.
+    f32x4 dR = {0.f, 0.f, 0.f, 0.f}, dRT = dR, dAQT = dR;
+    const int src7 = (lane & 48) | 7;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        bf16x8 kr_h, kr_l, ki_h, ki_l, qr_h, qr_l;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = 8 * s + e;
+            const float gref = __shfl(gf[i], src7);
+            const float up = __builtin_amdgcn_exp2f(gf[i] - gref);
+            const float dn = __builtin_amdgcn_exp2f(gref - gf[i]);
+            const float kr = kf[i] * up, ki = kf[i] * dn, qr = qf[i] * up;
+            kr_h[e] = (__bf16)kr;
+            kr_l[e] = (__bf16)(kr - (float)kr_h[e]);
+            ki_h[e] = (__bf16)ki;
+            ki_l[e] = (__bf16)(ki - (float)ki_h[e]);
+            qr_h[e] = (__bf16)qr;
+            qr_l[e] = (__bf16)(qr - (float)qr_h[e]);
+        }
+        dR = mma32(kr_h, ki_h, dR);
+        dR = mma32(kr_l, ki_h, dR);
+        dR = mma32(kr_h, ki_l, dR);
+        dRT = mma32(ki_h, kr_h, dRT);
+        dRT = mma32(ki_l, kr_h, dRT);
+        dRT = mma32(ki_h, kr_l, dRT);
+        dAQT = mma32(ki_h, qr_h, dAQT);
+        dAQT = mma32(ki_l, qr_h, dAQT);
+        dAQT = mma32(ki_h, qr_l, dAQT);
+    }
+    // D layout: row a = 4g + r, column b = tok.
+    float beta_row[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) beta_row[r] = __shfl(beta, 4 * g + r);
+    f32x4 R, RT, AQT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int a = 4 * g + r;
+        R[r] = (tok < a) ? beta_row[r] * dR[r] : 0.f;  // R[a][tok] = beta_a <k_tok|D|k_a>
+        RT[r] = (a < tok) ? beta * dRT[r] : 0.f;       // R^T[a][tok] = R[tok][a]
+        AQT[r] = (a <= tok) ? dAQT[r] : 0.f;           // (A^qk)^T[a][tok] = chi_{tok,a}
+    }
+
+    // ---- (A^kk)^T = (I + M)^-1 with M = R^T: (I-M)(I+M^2)(I+M^4)(I+M^8), exact since M^16 = 0
+    const f32x4 M2 = mm16_f32(R, RT);
+    const f32x4 M2T = mm16_f32(RT, R);
+    const f32x4 M4 = mm16_f32(M2T, M2);
+    const f32x4 M4T = mm16_f32(M2, M2T);
+    const f32x4 M8T = mm16_f32(M4, M4T);
+    const f32x4 P1 = mm16_f32(eye_plus(R, -1.f, g, tok), eye_plus(M2, 1.f, g, tok));
+    const f32x4 P2 = mm16_f32(eye_plus(M4T, 1.f, g, tok), P1);
+    const f32x4 AT = mm16_f32(eye_plus(M8T, 1.f, g, tok), P2);
+    f32x4 ABT;  // (A^kk Diag(beta))^T[a][tok] = beta_a A^kk[tok][a]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ABT[r] = beta_row[r] * AT[r];
+
+    char *u = units + ((int64_t)h * n_c_max + c) * kUnitBf16.bytes;
+    reinterpret_cast<f32x4 *>(u + kUnitBf16.ab)[lane] = ABT;
+    reinterpret_cast<f32x4 *>(u + kUnitBf16.aq)[lane] = AQT;
+
+    // ---- K_b, Q_b (16x16x32 A-operand order), K_end (via LDS transpose), gamma
+    const int src15 = (lane & 48) | 15;
+    float gl[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) gl[i] = __shfl(gf[i], src15);
+#pragma unroll
+    for (int gp = 0; gp < 4; ++gp) {  // destination lane tok + 16 gp, k step = g
+        bf16x8 kb, qb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = (e < 4) ? (4 * gp + e) : (16 + 4 * gp + e - 4);
+            const float dec = __builtin_amdgcn_exp2f(gf[i]);
+            kb[e] = (__bf16)(kf[i] * dec);
+            qb[e] = (__bf16)(qf[i] * dec);
+        }
+        const int64_t slot = (int64_t)g * 1024 + (tok + 16 * gp) * 16;
+        *reinterpret_cast<bf16x8 *>(u + kUnitBf16.kb + slot) = kb;
+        *reinterpret_cast<bf16x8 *>(u + kUnitBf16.qb + slot) = qb;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const float ke = kf[i] * __builtin_amdgcn_exp2f(gl[i] - gf[i]);
+        sKE[wv][32 * g + i][tok] = __builtin_bit_cast(uint16_t, (__bf16)ke);
+    }
+    if (tok == 15) {
+        float *gm = reinterpret_cast<float *>(u + kUnitBf16.gm) + 32 * g;
+#pragma unroll
+        for (int i = 0; i < 32; i += 4) {
+            f32x4 x = {__builtin_amdgcn_exp2f(gf[i]), __builtin_amdgcn_exp2f(gf[i + 1]),
+                       __builtin_amdgcn_exp2f(gf[i + 2]), __builtin_amdgcn_exp2f(gf[i + 3])};
+            *reinterpret_cast<f32x4 *>(gm + i) = x;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        // lane (kc = tok, g): tiles 2p and 2p+1, channel 32p + kc (+16), tokens 4g..4g+3
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(&sKE[wv][32 * p + tok][4 * g]);
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(&sKE[wv][32 * p + 16 + tok][4 * g]);
+        const u32x4 x = {lo[0], lo[1], hi[0], hi[1]};
+        reinterpret_cast<u32x4 *>(u + kUnitBf16.ke + p * 1024)[lane] = x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K2: one workgroup of 8 waves per (sequence, head); wave w owns value channels
+// [16w, 16w+16). Lane l holds S^T[16t + 4g + r][16w + l%16] in accumulator
+// tile t (t = 0..7, r = 0..3). The value channels evolve independently, so the
+// waves never communicate.
+// ---------------------------------------------------------------------------
+struct ChunkOps {
+    u32x4 kb[4], qb[4], ke[4];
+    f32x4 ab, aq, gm[8];
+    float vin[4];
+};
+
+__device__ __forceinline__ void load_ops(ChunkOps &o, const char *__restrict__ u, const uint16_t *__restrict__ v,
+                                         int64_t vbase, int64_t vstride, int nvalid, int lane, int g)
+{
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        o.kb[p] = reinterpret_cast<const u32x4 *>(u + kUnitBf16.kb + p * 1024)[lane];
+        o.qb[p] = reinterpret_cast<const u32x4 *>(u + kUnitBf16.qb + p * 1024)[lane];
+        o.ke[p] = reinterpret_cast<const u32x4 *>(u + kUnitBf16.ke + p * 1024)[lane];
+    }
+    o.ab = reinterpret_cast<const f32x4 *>(u + kUnitBf16.ab)[lane];
+    o.aq = reinterpret_cast<const f32x4 *>(u + kUnitBf16.aq)[lane];
+    const f32x4 *gm = reinterpret_cast<const f32x4 *>(u + kUnitBf16.gm);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o.gm[t] = gm[4 * t + g];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        o.vin[r] = (4 * g + r < nvalid) ? bf16_bits_to_f32(v[vbase + (int64_t)(4 * g + r) * vstride]) : 0.f;
+}
+
+template <typename TSt>
+__device__ __forceinline__ f32x4 ld_state4(const TSt *p);
+template <> __device__ __forceinline__ f32x4 ld_state4<float>(const float *p)
+{
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+template <> __device__ __forceinline__ f32x4 ld_state4<uint16_t>(const uint16_t *p)
+{
+    const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
+    f32x4 y = {bf_lo(x[0]), bf_hi(x[0]), bf_lo(x[1]), bf_hi(x[1])};
+    return y;
+}
+template <typename TSt>
+__device__ __forceinline__ void st_state4(TSt *p, f32x4 x);
+template <> __device__ __forceinline__ void st_state4<float>(float *p, f32x4 x)
+{
+    *reinterpret_cast<f32x4 *>(p) = x;
+}
+template <> __device__ __forceinline__ void st_state4<uint16_t>(uint16_t *p, f32x4 x)
+{
+    u32x2 y;
+    y[0] = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
+    y[1] = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+    *reinterpret_cast<u32x2 *>(p) = y;
+}
+
+constexpr int kK2Waves = 8;
+
+template <typename TSt>
+__global__ __launch_bounds__(64 * kK2Waves) void k2_mfma(const uint16_t *__restrict__ v, const TSt *s0, TSt *s1,
+                                                          uint16_t *__restrict__ out,
+                                                          const int32_t *__restrict__ tok_off,
+                                                          const int32_t *__restrict__ chunk_off, int H,
+                                                          int64_t n_c_max, const char *__restrict__ units)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = blockIdx.x / H, h = blockIdx.x % H;
+    const int g = lane >> 4, vcol = 16 * w + (lane & 15);
+    const int64_t sbase = (((int64_t)n * H + h) * kD + vcol) * kD + 4 * g;
+
+    f32x4 st[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        if (s0) st[t] = ld_state4(s0 + sbase + 16 * t);
+        else st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int c0 = chunk_off[n], nch = chunk_off[n + 1] - c0;
+    const int tb = tok_off[n], te = tok_off[n + 1];
+    const int64_t vstride = (int64_t)H * kD;
+    const char *ubase = units + ((int64_t)h * n_c_max + c0) * kUnitBf16.bytes;
+
+    ChunkOps cur;
+    if (nch > 0) load_ops(cur, ubase, v, ((int64_t)tb * H + h) * kD + vcol, vstride, te - tb, lane, g);
+    for (int j = 0; j < nch; ++j) {
+        const int t0 = tb + j * kC;
+        const int len = min(kC, te - t0);
+        ChunkOps nxt;
+        if (j + 1 < nch)
+            load_ops(nxt, ubase + (int64_t)(j + 1) * kUnitBf16.bytes, v,
+                     ((int64_t)(t0 + kC) * H + h) * kD + vcol, vstride, te - t0 - kC, lane, g);
+
+        // state -> bf16 B operands (tiles 2p, 2p+1 form k step p)
+        bf16x8 sb[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sb[p][r] = (__bf16)st[2 * p][r];
+                sb[p][4 + r] = (__bf16)st[2 * p + 1][r];
+            }
+        }
+        f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = xk;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            xk = mma32(__builtin_bit_cast(bf16x8, cur.kb[p]), sb[p], xk);
+            xq = mma32(__builtin_bit_cast(bf16x8, cur.qb[p]), sb[p], xq);
+        }
+        // Ebar = V - K_b S^T ; E = (A^kk Diag(beta)) Ebar with split operands
+        f32x4 eb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) eb[r] = cur.vin[r] - xk[r];
+        bf16x4 eb_h, eb_l, ab_h, ab_l, aq_h, aq_l, e_h, e_l;
+        split4(eb, eb_h, eb_l);
+        split4(cur.ab, ab_h, ab_l);
+        f32x4 E = {0.f, 0.f, 0.f, 0.f};
+        E = mma16(ab_h, eb_h, E);
+        E = mma16(ab_l, eb_h, E);
+        E = mma16(ab_h, eb_l, E);
+        split4(E, e_h, e_l);
+        // O = Q_b S^T + A^qk E
+        split4(cur.aq, aq_h, aq_l);
+        f32x4 O = mma16(aq_h, e_h, xq);
+        O = mma16(aq_l, e_h, O);
+        O = mma16(aq_h, e_l, O);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (4 * g + r < len) out[((int64_t)(t0 + 4 * g + r) * H + h) * kD + vcol] = f32_to_bf16_bits(O[r]);
+        // S^T <- Diag(gamma) S^T + K_end^T E
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const u32x4 kq = cur.ke[t >> 1];
+            const u32x2 kh = (t & 1) ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]};
+            const bf16x4 kt = __builtin_bit_cast(bf16x4, kh);
+            f32x4 s = st[t] * cur.gm[t];
+            s = mma16(kt, e_h, s);
+            st[t] = mma16(kt, e_l, s);
+        }
+        if (j + 1 < nch) cur = nxt;
+    }
+    if (s1) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) st_state4(s1 + sbase + 16 * t, st[t]);
+    }
+}
+
+template <typename TSt>
+static hipError_t launch_mfma_t(const Problem &p, hipStream_t s)
+{
+    const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
+    const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
+    char *units = p.ws + p.lay.units;
+    if (p.n_c_max > 0) {
+        const int wpb = (p.H % 4 == 0) ? 4 : (p.H % 2 == 0 ? 2 : 1);
+        hipLaunchKernelGGL(k1_mfma, dim3((unsigned)p.n_c_max, p.H / wpb), dim3(64 * wpb), 0, s,
+                           (const uint16_t *)p.q, (const uint16_t *)p.k, (const uint16_t *)p.g,
+                           (const uint16_t *)p.beta, tok, chk, (int)p.N, p.H, p.n_c_max, p.lb, p.scale, units);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k2_mfma<TSt>), dim3((unsigned)(p.N * p.H)), dim3(64 * kK2Waves), 0, s,
+                       (const uint16_t *)p.v, (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H,
+                       p.n_c_max, (const char *)units);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma(const Problem &p, hipStream_t s)
+{
+    return p.st_bf16 ? launch_mfma_t<uint16_t>(p, s) : launch_mfma_t<float>(p, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,156 @@
+"""Host-side checks of the C ABI (CPU only, no kernel is ever launched).
+
+Every kda_fwd call here carries an argument that validation rejects, so the
+library returns before touching the GPU; the fake addresses are never used.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kimi_delta_attention_k1_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_SEQLENS, BAD_ARG, WORKSPACE, MISALIGNED, HIP = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return kda.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported(lib):
+    names = declared_functions()
+    assert {"kda_fwd", "kda_fwd_workspace_size", "kda_status_str", "kda_version"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in include/kda.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_version() >= 100
+    for code in range(9):
+        assert kda.status_str(code) and kda.status_str(code) != "unknown status"
+    assert kda.status_str(99) == "unknown status"
+
+
+def test_desc_struct_matches_header():
+    # kda_desc_t: 3 x int64, 4 x int32, float, uint32 -> 48 bytes, no padding surprises
+    assert ctypes.sizeof(kda.KdaDesc) == 48
+
+
+def _layout(N, H, n_c, unit):
+    tok = 128
+    chk = (tok + 4 * (N + 1) + 127) // 128 * 128
+    units = (chk + 4 * (N + 1) + 127) // 128 * 128
+    return units + unit * H * n_c
+
+
+def test_workspace_size_arithmetic(lib):
+    # batch mode, one sequence of 64 tokens -> 4 chunks
+    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32) == _layout(1, 1, 4, 27136)
+    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_BF16) == _layout(1, 1, 4, 14848)
+    # batch of 2 rows of 17 tokens -> 2 x 2 chunks
+    assert kda.workspace_size(2, 17, 2, 3) == _layout(2, 3, 4, 14848)
+    # packed: 8 x 8192 tokens (bound (T + 15 N) / 16)
+    assert kda.workspace_size(1, 65536, 8, 32) == _layout(8, 32, (65536 + 15 * 8) // 16, 14848)
+    # fp32 compute flag selects the fp32 unit size
+    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_BF16, fp32_compute=True) == _layout(1, 1, 4, 27136)
+    # invalid descriptions report 0
+    assert kda.workspace_size(1, 64, 1, 0) == 0
+    d = kda.make_desc(1, 64, 1, 1, 0, 1, 0.1, head_dim=64)
+    assert lib.kda_fwd_workspace_size(ctypes.byref(d)) == 0
+    assert lib.kda_fwd_workspace_size(None) == 0
+
+
+class Fake:
+    """Disjoint, 256-B aligned fake addresses (never dereferenced)."""
+    BASE = 0x7F0000000000
+
+    def __init__(self, sizes):
+        self.addr = {}
+        a = self.BASE
+        for name, size in sizes.items():
+            self.addr[name] = a
+            a += (size + (1 << 20)) // 256 * 256 + 256
+
+
+def _call(lib, desc, *, cu=False, drop=(), shift=None, lb=-5.0, ws_bytes=None, overrides=None):
+    d = desc if desc is not None else _desc()
+    T_tot = d.seqlen if cu else d.batch * d.seqlen
+    H, N = max(d.num_heads, 1), max(d.num_seqs, 1)
+    esz = 2 if d.io_dtype == 0 else 4
+    sizes = dict(q=T_tot * H * 128 * esz, k=T_tot * H * 128 * esz, v=T_tot * H * 128 * esz,
+                 g=T_tot * H * 128 * esz, b=T_tot * H * esz, cu=4 * (N + 1), s0=N * H * 128 * 128 * 4,
+                 out=T_tot * H * 128 * esz, s1=N * H * 128 * 128 * 4, ws=1 << 34)
+    f = Fake(sizes)
+    p = {k_: ctypes.c_void_p(v_) for k_, v_ in f.addr.items()}
+    if not cu:
+        p["cu"] = None
+    for name in drop:
+        p[name] = None
+    if shift:
+        for name, off in shift.items():
+            p[name] = ctypes.c_void_p(f.addr[name] + off)
+    if overrides:
+        for name, other in overrides.items():
+            p[name] = ctypes.c_void_p(f.addr[other[0]] + other[1])
+    wsb = (1 << 34) if ws_bytes is None else ws_bytes
+    return lib.kda_fwd(p["q"], p["k"], p["v"], p["g"], p["b"], p["cu"], p["s0"], p["out"], p["s1"],
+                       ctypes.c_float(lb), ctypes.byref(desc) if desc is not None else None, p["ws"],
+                       ctypes.c_size_t(wsb), None)
+
+
+def _desc(**kw):
+    base = dict(batch=1, seqlen=64, num_seqs=1, num_heads=2, io_dtype=0, state_dtype=1, scale=128 ** -0.5)
+    base.update(kw)
+    return kda.make_desc(base["batch"], base["seqlen"], base["num_seqs"], base["num_heads"], base["io_dtype"],
+                         base["state_dtype"], base["scale"], base.get("flags", 0), base.get("head_dim", 128))
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(desc=dict(head_dim=64)), BAD_SHAPE),
+    (dict(desc=dict(num_heads=0)), BAD_SHAPE),
+    (dict(desc=dict(batch=0)), BAD_SHAPE),
+    (dict(desc=dict(seqlen=-1)), BAD_SHAPE),
+    (dict(desc=dict(batch=2, num_seqs=3)), BAD_SHAPE),
+    (dict(desc=dict(io_dtype=7)), BAD_DTYPE),
+    (dict(desc=dict(state_dtype=-1)), BAD_DTYPE),
+    (dict(desc=dict(batch=2, num_seqs=2), cu=True), BAD_SEQLENS),
+    (dict(lb=-10.5), BAD_ARG),
+    (dict(lb=0.5), BAD_ARG),
+    (dict(lb=float("nan")), BAD_ARG),
+    (dict(desc=dict(scale=0.0)), BAD_ARG),
+    (dict(desc=dict(scale=float("inf"))), BAD_ARG),
+    (dict(desc=dict(flags=2)), BAD_ARG),
+    (dict(drop=("q",)), NULL_ARG),
+    (dict(drop=("out",)), NULL_ARG),
+    (dict(drop=("ws",)), WORKSPACE),
+    (dict(ws_bytes=1000), WORKSPACE),
+    (dict(shift=dict(ws=64)), WORKSPACE),
+    (dict(shift=dict(q=2)), MISALIGNED),
+    (dict(shift=dict(s1=8)), MISALIGNED),
+    (dict(overrides=dict(out=("q", 0))), BAD_ARG),          # out aliases q
+    (dict(overrides=dict(s1=("s0", 256))), BAD_ARG),        # partial state overlap
+    (dict(overrides=dict(ws=("v", 0))), BAD_ARG),           # workspace over an input
+])
+def test_validation_rejects_before_launch(lib, case, expect):
+    desc = _desc(**case.get("desc", {}))
+    rc = _call(lib, desc, cu=case.get("cu", False), drop=case.get("drop", ()), shift=case.get("shift"),
+               lb=case.get("lb", -5.0), ws_bytes=case.get("ws_bytes"), overrides=case.get("overrides"))
+    assert rc == expect, kda.status_str(rc)
+
+
+def test_null_desc(lib):
+    assert _call(lib, None) == NULL_ARG
