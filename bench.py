@@ -1,0 +1,189 @@
+"""Benchmark of the KDA forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 30] [--workload c3]
+
+One step = one full forward (chunk map, chunk-parallel kernel, recurrence
+kernel) over the whole seeded synthetic batch, with inputs already resident
+in HBM. W untimed warmup steps, then K timed steps between two device
+synchronisations; HIP events on the launch stream between the two stages give
+each kernel's average duration inside the same timed region. Prints ONE JSON
+line. Default workload c3 (8 packed sequences x 8192 tokens, H=32, D=128,
+bf16), the headline metric's head count.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA fwd tokens/sec at H=32, D=128 bf16; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E peak
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
+UNIT_BYTES = 14848           # workspace bytes per (chunk, head) unit, bf16 path
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "kimi_delta_attention_k1_amd", "csrc", "kda_mfma.hip")
+
+
+def algorithmic_work(w):
+    """Bytes each kernel must move and the recurrence's matrix flops, per launch.
+
+    Per (chunk, head) unit, 16 token rows of 128 channels:
+      chunk-parallel kernel: reads q, k, g_raw (3 x 256 B per token-head) and
+        beta_raw (2 B per token-head), writes one 14848 B workspace unit;
+      recurrence kernel: reads the unit and v (256 B per token-head), writes o
+        (256 B per token-head); per (sequence, head) it reads the 64 KiB fp32
+        initial state (when given) and writes the 64 KiB final state.
+    Recurrence flops per unit: K_b S^T and Q_b S^T (2 x 2*16*128*128), the
+    state update K_end^T E (2*128*16*128), A^kk E and A^qk E (2 x 2*16*16*128)
+    and the decay (128*128).
+    """
+    H = w.H
+    units = sum((L + 15) // 16 for L in w.seq_lens) * H
+    th = w.T_tot * H
+    st = w.N * H * 128 * 128 * 4
+    k1 = th * (3 * 256 + 2) + units * UNIT_BYTES
+    k2 = units * UNIT_BYTES + th * 512 + st * (2 if w.initial_state is not None else 1)
+    flops = units * (3 * 2 * 16 * 128 * 128 + 2 * 2 * 16 * 16 * 128 + 128 * 128)
+    return dict(units=units, k1_bytes=k1, k2_bytes=k2, k2_flops=flops)
+
+
+def src_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(kernel, workload):
+    """Counter-measured HBM bytes per launch, if taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent or ent.get("src_sha256") != src_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, nseq):
+    """The fp64 oracle, untuned, on the first nseq sequences (all heads)."""
+    import numpy as np  # noqa: F401
+    import oracle
+    offs = w.offsets()
+    e = offs[nseq]
+    f = lambda t: t[:e].float().numpy()  # noqa: E731
+    s0 = None if w.initial_state is None else w.initial_state[:nseq].numpy()
+    threads = min(nseq * w.H, oracle.max_threads())
+    t = time.perf_counter()
+    oracle.token_forward(f(w.q), f(w.k), f(w.v), f(w.g_raw), f(w.beta_raw), offs[:nseq + 1], s0,
+                         lower_bound=w.lower_bound, threads=threads)
+    dt = time.perf_counter() - t
+    return {"value": e / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: first {nseq} of {w.N} sequences ({e} tokens x {w.H} heads), fp64 token "
+                      f"recurrence, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU-baseline sample (0: skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kimi_delta_attention_k1_amd as kda
+    from kimi_delta_attention_k1_amd import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.CONFIGS[args.workload]()
+    q, k, v, g, b = (t.to(dev) for t in (w.q, w.k, w.v, w.g_raw, w.beta_raw))
+    s0 = None if w.initial_state is None else w.initial_state.to(dev)
+    cu = w.cu_seqlens().to(dev) if w.packed else None
+    if not w.packed:
+        shp = (w.N, w.seq_lens[0], w.H, 128)
+        q, k, v, g = (t.view(shp) for t in (q, k, v, g))
+        b = b.view(shp[:3])
+    call = kda.prepare_call(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        call.prepare()
+        call.recur()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        call.prepare()
+        ev[i][1].record(stream)
+        call.recur()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k1_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    k2_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    step_ms = sum(e[0].elapsed_time(e[2]) for e in ev) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    work = algorithmic_work(w)
+    kern = {
+        "k1_mfma": dict(ms=k1_ms, bytes=work["k1_bytes"]),
+        "k2_mfma": dict(ms=k2_ms, bytes=work["k2_bytes"], flops=work["k2_flops"]),
+    }
+    dom = max(kern, key=lambda n: kern[n]["ms"])
+    per_kernel = {}
+    for name, kk in kern.items():
+        gbs = kk["bytes"] / (kk["ms"] * 1e-3) / 1e9
+        ent = {"avg_ms": round(kk["ms"], 4), "algorithmic_bytes": kk["bytes"], "achieved_GBps": round(gbs, 1),
+               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if "flops" in kk:
+            tf = kk["flops"] / (kk["ms"] * 1e-3) / 1e12
+            ent.update({"algorithmic_flops": kk["flops"], "achieved_TFLOPs": round(tf, 2),
+                        "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)})
+        per_kernel[name] = ent
+    d = per_kernel[dom]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": d["achieved_GBps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": d["hbm_frac"], "traffic": traffic_for(dom, args.workload)}
+
+    tokens_per_s = w.T_tot / (ms_per_step * 1e-3)
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded CPU torch.Generator, N(0,1) family; see workloads.py)",
+        "config": {"workload": f"{args.workload}: {workloads.DESCRIPTIONS[args.workload]}",
+                   "tokens": w.T_tot, "heads": w.H, "head_dim": 128, "sequences": w.N, "chunk": 16,
+                   "lower_bound": w.lower_bound},
+        "event_ms_per_step": round(step_ms, 4),
+        "kernels": per_kernel,
+        "roofline": roofline,
+    }
+    if args.cpu_seqs > 0:
+        line["cpu_baseline"] = cpu_baseline(w, min(args.cpu_seqs, w.N))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -147,6 +147,38 @@ kda_status_t kda_fwd(const void *q, const void *k, const void *v,
                      void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/*
+ * The two stages of kda_fwd, for callers that time or overlap them: the
+ * chunk-parallel stage (chunk map, gate, in-chunk log-decay prefix sums, L2
+ * norms, the decayed 16 x 16 blocks, the unit-lower-triangular inverse and
+ * the decayed key/query operands; Doubleword KDA page, sections 6.1-6.3 and
+ * 6.6) writes the workspace; the recurrence stage (the chunk-state scan with
+ * outputs, sections 6.4-6.5) reads it and writes out and final_state.
+ * kda_fwd(args) is exactly kda_fwd_prepare(args) followed by
+ * kda_fwd_recur(args). Both take kda_fwd's arguments with the same meaning
+ * and checks; recur must see the workspace written by a prepare call with the
+ * same arguments, ordered before it (same stream, or an event). Each returns
+ * after enqueueing its kernels.
+ */
+kda_status_t kda_fwd_prepare(const void *q, const void *k, const void *v,
+                             const void *g_raw, const void *beta_raw,
+                             const int32_t *cu_seqlens,
+                             const void *initial_state,
+                             void *out, void *final_state,
+                             float lower_bound,
+                             const kda_desc_t *desc,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+kda_status_t kda_fwd_recur(const void *q, const void *k, const void *v,
+                           const void *g_raw, const void *beta_raw,
+                           const int32_t *cu_seqlens,
+                           const void *initial_state,
+                           void *out, void *final_state,
+                           float lower_bound,
+                           const kda_desc_t *desc,
+                           void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_str(kda_status_t status);
 

@@ -19,7 +19,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "workspace_size", "KdaError", "load_library", "library_path", "seqlens_flag",
+__all__ = ["fwd", "prepare_call", "Call", "workspace_size", "KdaError", "load_library", "library_path", "seqlens_flag",
            "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE"]
 
 HEAD_DIM = 128
@@ -62,9 +62,11 @@ def load_library():
     vp = ctypes.c_void_p
     lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(KdaDesc)]
-    lib.kda_fwd.restype = ctypes.c_int
-    lib.kda_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.POINTER(KdaDesc),
-                            vp, ctypes.c_size_t, vp]
+    for name in ("kda_fwd", "kda_fwd_prepare", "kda_fwd_recur"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.POINTER(KdaDesc),
+                       vp, ctypes.c_size_t, vp]
     lib.kda_status_str.restype = ctypes.c_char_p
     lib.kda_status_str.argtypes = [ctypes.c_int]
     lib.kda_version.restype = ctypes.c_int
@@ -103,6 +105,32 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+class Call:
+    """A marshalled kda_fwd argument list; run() / prepare() / recur() enqueue it.
+
+    Holds references to every tensor it points at, so the buffers stay alive
+    while the object does.
+    """
+
+    def __init__(self, lib, args, keep, out, final_state):
+        self._lib, self._args, self._keep = lib, args, keep
+        self.out, self.final_state = out, final_state
+
+    def _go(self, fn):
+        st = fn(*self._args)
+        if st != 0:
+            raise KdaError(st, self._lib.kda_status_str(st).decode())
+
+    def run(self):
+        self._go(self._lib.kda_fwd)
+
+    def prepare(self):
+        self._go(self._lib.kda_fwd_prepare)
+
+    def recur(self):
+        self._go(self._lib.kda_fwd_recur)
+
+
 def fwd(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | None = None,
         initial_state=None, output_final_state: bool = True, cu_seqlens=None, out=None, final_state=None,
         workspace=None, fp32_compute: bool = False, stream=None):
@@ -112,6 +140,18 @@ def fwd(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | N
     torch.cuda.Stream (default: the current stream). `workspace` may be a
     preallocated uint8 tensor of at least workspace_size(...) bytes.
     """
+    c = prepare_call(q, k, v, g_raw, beta_raw, lower_bound=lower_bound, scale=scale, initial_state=initial_state,
+                     output_final_state=output_final_state, cu_seqlens=cu_seqlens, out=out,
+                     final_state=final_state, workspace=workspace, fp32_compute=fp32_compute, stream=stream)
+    c.run()
+    return c.out, c.final_state
+
+
+def prepare_call(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | None = None,
+                 initial_state=None, output_final_state: bool = True, cu_seqlens=None, out=None,
+                 final_state=None, workspace=None, fp32_compute: bool = False, stream=None) -> Call:
+    """Check and marshal fwd's arguments once (allocating out, final_state and
+    the workspace when not given) without launching anything."""
     import torch
     lib = load_library()
     tensors = (q, k, v, g_raw, beta_raw)
@@ -163,12 +203,11 @@ def fwd(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | N
         raise ValueError(f"workspace too small: {workspace.numel()} < {need} bytes")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = lib.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(cu_seqlens),
-                     _ptr(initial_state), _ptr(out), _ptr(final_state), float(lower_bound), ctypes.byref(desc),
-                     _ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream.cuda_stream))
-    if st != 0:
-        raise KdaError(st, lib.kda_status_str(st).decode())
-    return out, final_state
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(cu_seqlens), _ptr(initial_state),
+            _ptr(out), _ptr(final_state), ctypes.c_float(lower_bound), ctypes.byref(desc), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream.cuda_stream))
+    keep = (q, k, v, g_raw, beta_raw, cu_seqlens, initial_state, out, final_state, workspace, desc, stream)
+    return Call(lib, args, keep, out, final_state)
 
 
 def seqlens_flag(workspace) -> int:

@@ -76,10 +76,14 @@ extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc)
     return best;
 }
 
-extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, const void *g_raw,
-                                const void *beta_raw, const int32_t *cu_seqlens, const void *initial_state,
-                                void *out, void *final_state, float lower_bound, const kda_desc_t *desc,
-                                void *workspace, size_t workspace_bytes, void *stream)
+namespace {
+
+enum Stage { kPrepare = 1, kRecur = 2 };
+
+kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw, const void *beta_raw,
+                 const int32_t *cu_seqlens, const void *initial_state, void *out, void *final_state,
+                 float lower_bound, const kda_desc_t *desc, void *workspace, size_t workspace_bytes,
+                 void *stream, int stages)
 {
     Shape s;
     const bool varlen = cu_seqlens != nullptr;
@@ -132,10 +136,31 @@ extern "C" kda_status_t kda_fwd(const void *q, const void *k, const void *v, con
     p.lay = lay;
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (kda::launch_chunk_map(p, hs) != hipSuccess) return KDA_ERR_HIP;
-    hipError_t e = p.f32_path ? kda::launch_ref(p, hs) : kda::launch_mfma(p, hs);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (stages & kPrepare) {
+        if (kda::launch_chunk_map(p, hs) != hipSuccess) return KDA_ERR_HIP;
+        if ((p.f32_path ? kda::launch_prep_ref(p, hs) : kda::launch_prep_mfma(p, hs)) != hipSuccess)
+            return KDA_ERR_HIP;
+    }
+    if (stages & kRecur) {
+        if ((p.f32_path ? kda::launch_recur_ref(p, hs) : kda::launch_recur_mfma(p, hs)) != hipSuccess)
+            return KDA_ERR_HIP;
+    }
+    return KDA_OK;
 }
+
+}  // namespace
+
+#define KDA_ARGS                                                                                          \
+    const void *q, const void *k, const void *v, const void *g_raw, const void *beta_raw,                  \
+        const int32_t *cu_seqlens, const void *initial_state, void *out, void *final_state, float lower_bound, \
+        const kda_desc_t *desc, void *workspace, size_t workspace_bytes, void *stream
+#define KDA_PASS                                                                                          \
+    q, k, v, g_raw, beta_raw, cu_seqlens, initial_state, out, final_state, lower_bound, desc, workspace,    \
+        workspace_bytes, stream
+
+extern "C" kda_status_t kda_fwd(KDA_ARGS) { return run(KDA_PASS, kPrepare | kRecur); }
+extern "C" kda_status_t kda_fwd_prepare(KDA_ARGS) { return run(KDA_PASS, kPrepare); }
+extern "C" kda_status_t kda_fwd_recur(KDA_ARGS) { return run(KDA_PASS, kRecur); }
 
 extern "C" const char *kda_status_str(kda_status_t status)
 {

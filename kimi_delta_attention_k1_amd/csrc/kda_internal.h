@@ -77,9 +77,11 @@ struct Problem {
     WsLayout lay;
 };
 
-hipError_t launch_chunk_map(const Problem &p, hipStream_t s);
-hipError_t launch_ref(const Problem &p, hipStream_t s);
-hipError_t launch_mfma(const Problem &p, hipStream_t s);
+hipError_t launch_chunk_map(const Problem &p, hipStream_t s);   // K0
+hipError_t launch_prep_ref(const Problem &p, hipStream_t s);    // fp32 K1
+hipError_t launch_recur_ref(const Problem &p, hipStream_t s);   // fp32 K2
+hipError_t launch_prep_mfma(const Problem &p, hipStream_t s);   // bf16 K1
+hipError_t launch_recur_mfma(const Problem &p, hipStream_t s);  // bf16 K2
 
 // ---------------------------------------------------------------------------
 // Device helpers

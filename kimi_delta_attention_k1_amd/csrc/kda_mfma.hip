@@ -283,35 +283,34 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
 }
 
 // ---------------------------------------------------------------------------
-// K2: one workgroup of 8 waves per (sequence, head); wave w owns value channels
-// [16w, 16w+16). Lane l holds S^T[16t + 4g + r][16w + l%16] in accumulator
-// tile t (t = 0..7, r = 0..3). The value channels evolve independently, so the
-// waves never communicate.
+// K2: one workgroup per (sequence, head): 8 consumer waves, wave w owning value
+// channels [16w, 16w+16), and 2 producer waves. Lane l of a consumer holds
+// S^T[16t + 4g + r][16w + l%16] in accumulator tile t (t = 0..7, r = 0..3). The
+// value channels evolve independently, so consumers never exchange state; they
+// share each chunk's operands through LDS.
+//
+// The producers copy every chunk's 14848-byte workspace unit and its 16 x 256-byte
+// v tile straight from global memory into a ring of kK2Slots LDS slots with
+// 16-byte-per-lane global-to-LDS loads, kK2Slots - 1 chunks ahead, and wait
+// with explicit counts of their own loads. One workgroup barrier per chunk
+// publishes a slot and recycles the previous one. The barrier is a bare
+// s_barrier: a fenced barrier would drain the prefetch queue every chunk.
 // ---------------------------------------------------------------------------
-struct ChunkOps {
-    u32x4 kb[4], qb[4], ke[4];
-    f32x4 ab, aq, gm[8];
-    float vin[4];
-};
+constexpr int kK2Consumers = 8;
+constexpr int kK2Producers = 2;
+constexpr int kK2Threads = 64 * (kK2Consumers + kK2Producers);
+constexpr int kK2Slots = 6;
+constexpr int kSlotKB = 20;                        // 1 KB copy instructions per chunk
+constexpr int kSlotBytes = kSlotKB * 1024;         // unit 14848 | pad 512 | v 4096 | pad 1024
+constexpr int kVOff = 15 * 1024;                   // v tile offset inside a slot
+constexpr int kKBPerProducer = kSlotKB / kK2Producers;                 // 10
+constexpr int kProdPending = (kK2Slots - 2) * kKBPerProducer;          // loads allowed in flight
+static_assert(kProdPending <= 63, "vmcnt holds at most 63 outstanding loads");
+static_assert(kUnitBf16.bytes <= (size_t)kVOff, "unit must fit below the v tile");
 
-__device__ __forceinline__ void load_ops(ChunkOps &o, const char *__restrict__ u, const uint16_t *__restrict__ v,
-                                         int64_t vbase, int64_t vstride, int nvalid, int lane, int g)
-{
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        o.kb[p] = reinterpret_cast<const u32x4 *>(u + kUnitBf16.kb + p * 1024)[lane];
-        o.qb[p] = reinterpret_cast<const u32x4 *>(u + kUnitBf16.qb + p * 1024)[lane];
-        o.ke[p] = reinterpret_cast<const u32x4 *>(u + kUnitBf16.ke + p * 1024)[lane];
-    }
-    o.ab = reinterpret_cast<const f32x4 *>(u + kUnitBf16.ab)[lane];
-    o.aq = reinterpret_cast<const f32x4 *>(u + kUnitBf16.aq)[lane];
-    const f32x4 *gm = reinterpret_cast<const f32x4 *>(u + kUnitBf16.gm);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) o.gm[t] = gm[4 * t + g];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        o.vin[r] = (4 * g + r < nvalid) ? bf16_bits_to_f32(v[vbase + (int64_t)(4 * g + r) * vstride]) : 0.f;
-}
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void bar_sync() { asm volatile("s_barrier" ::: "memory"); }
 
 template <typename TSt>
 __device__ __forceinline__ f32x4 ld_state4(const TSt *p);
@@ -339,41 +338,75 @@ template <> __device__ __forceinline__ void st_state4<uint16_t>(uint16_t *p, f32
     *reinterpret_cast<u32x2 *>(p) = y;
 }
 
-constexpr int kK2Waves = 8;
-
 template <typename TSt>
-__global__ __launch_bounds__(64 * kK2Waves) void k2_mfma(const uint16_t *__restrict__ v, const TSt *s0, TSt *s1,
-                                                          uint16_t *__restrict__ out,
-                                                          const int32_t *__restrict__ tok_off,
-                                                          const int32_t *__restrict__ chunk_off, int H,
-                                                          int64_t n_c_max, const char *__restrict__ units)
+__global__ __launch_bounds__(kK2Threads) void k2_mfma(const uint16_t *__restrict__ v, const TSt *s0, TSt *s1,
+                                                       uint16_t *__restrict__ out,
+                                                       const int32_t *__restrict__ tok_off,
+                                                       const int32_t *__restrict__ chunk_off, int H,
+                                                       int64_t n_c_max, const char *__restrict__ units)
 {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(1024))) char lds[kK2Slots][kSlotBytes];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n = blockIdx.x / H, h = blockIdx.x % H;
-    const int g = lane >> 4, vcol = 16 * w + (lane & 15);
-    const int64_t sbase = (((int64_t)n * H + h) * kD + vcol) * kD + 4 * g;
-
-    f32x4 st[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        if (s0) st[t] = ld_state4(s0 + sbase + 16 * t);
-        else st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
     const int c0 = chunk_off[n], nch = chunk_off[n + 1] - c0;
     const int tb = tok_off[n], te = tok_off[n + 1];
-    const int64_t vstride = (int64_t)H * kD;
-    const char *ubase = units + ((int64_t)h * n_c_max + c0) * kUnitBf16.bytes;
 
-    ChunkOps cur;
-    if (nch > 0) load_ops(cur, ubase, v, ((int64_t)tb * H + h) * kD + vcol, vstride, te - tb, lane, g);
+    if (w >= kK2Consumers) {
+        // ------------------------------------------------------------ producers
+        if (nch == 0) return;  // uniform over the workgroup: nobody enters the barriers
+        const int pw = w - kK2Consumers;
+        const char *ubase = units + ((int64_t)h * n_c_max + c0) * kUnitBf16.bytes;
+        const char *vb = reinterpret_cast<const char *>(v);
+        auto copy_chunk = [&](int j, int slot) {
+            j = min(j, nch - 1);  // past the end: re-read the last chunk into a free slot
+            const char *u = ubase + (int64_t)j * kUnitBf16.bytes;
+#pragma unroll
+            for (int i = 0; i < kKBPerProducer; ++i) {
+                const int b = pw * kKBPerProducer + i;  // which KB of the slot
+                const char *src;
+                if (b < kVOff / 1024) {
+                    const int off = b * 1024 + lane * 16;
+                    src = u + (off < (int)kUnitBf16.bytes ? off : 0);
+                } else if (b < kVOff / 1024 + 4) {
+                    const int r = 4 * (b - kVOff / 1024) + (lane >> 4);
+                    const int row = min(tb + j * kC + r, te - 1);
+                    src = vb + (((int64_t)row * H + h) * kD) * 2 + (lane & 15) * 16;
+                } else {
+                    src = u;  // filler: keeps every producer at the same load count
+                }
+                __builtin_amdgcn_global_load_lds(src, (lds_void *)(&lds[slot][b * 1024]), 16, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int s = 0; s < kK2Slots - 1; ++s) copy_chunk(s, s);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kProdPending) : "memory");  // chunk 0 landed
+        bar_sync();
+#pragma unroll 1
+        for (int j = 0; j < nch; ++j) {
+            copy_chunk(j + kK2Slots - 1, (j + kK2Slots - 1) % kK2Slots);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kProdPending) : "memory");  // chunk j+1 landed
+            bar_sync();
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // nothing in flight into LDS at exit
+        return;
+    }
+
+    // ---------------------------------------------------------------- consumers
+    const int g = lane >> 4, vcol = 16 * w + (lane & 15);
+    const int64_t sbase = (((int64_t)n * H + h) * kD + vcol) * kD + 4 * g;
+    f32x4 st[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s0 != nullptr) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) st[t] = ld_state4(s0 + sbase + 16 * t);
+    }
+    if (nch > 0) bar_sync();
+#pragma unroll 1
     for (int j = 0; j < nch; ++j) {
+        const char *L = lds[j % kK2Slots];
         const int t0 = tb + j * kC;
         const int len = min(kC, te - t0);
-        ChunkOps nxt;
-        if (j + 1 < nch)
-            load_ops(nxt, ubase + (int64_t)(j + 1) * kUnitBf16.bytes, v,
-                     ((int64_t)(t0 + kC) * H + h) * kD + vcol, vstride, te - t0 - kC, lane, g);
 
         // state -> bf16 B operands (tiles 2p, 2p+1 form k step p)
         bf16x8 sb[4];
@@ -388,23 +421,29 @@ __global__ __launch_bounds__(64 * kK2Waves) void k2_mfma(const uint16_t *__restr
         f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = xk;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            xk = mma32(__builtin_bit_cast(bf16x8, cur.kb[p]), sb[p], xk);
-            xq = mma32(__builtin_bit_cast(bf16x8, cur.qb[p]), sb[p], xq);
+            const bf16x8 kb = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.kb + p * 1024 + lane * 16);
+            const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.qb + p * 1024 + lane * 16);
+            xk = mma32(kb, sb[p], xk);
+            xq = mma32(qb, sb[p], xq);
         }
         // Ebar = V - K_b S^T ; E = (A^kk Diag(beta)) Ebar with split operands
         f32x4 eb;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) eb[r] = cur.vin[r] - xk[r];
+        for (int r = 0; r < 4; ++r) {
+            const int tr = 4 * g + r;
+            const uint16_t vr = *reinterpret_cast<const uint16_t *>(L + kVOff + tr * 256 + vcol * 2);
+            eb[r] = (tr < len ? bf16_bits_to_f32(vr) : 0.f) - xk[r];
+        }
         bf16x4 eb_h, eb_l, ab_h, ab_l, aq_h, aq_l, e_h, e_l;
         split4(eb, eb_h, eb_l);
-        split4(cur.ab, ab_h, ab_l);
+        split4(*reinterpret_cast<const f32x4 *>(L + kUnitBf16.ab + lane * 16), ab_h, ab_l);
         f32x4 E = {0.f, 0.f, 0.f, 0.f};
         E = mma16(ab_h, eb_h, E);
         E = mma16(ab_l, eb_h, E);
         E = mma16(ab_h, eb_l, E);
         split4(E, e_h, e_l);
         // O = Q_b S^T + A^qk E
-        split4(cur.aq, aq_h, aq_l);
+        split4(*reinterpret_cast<const f32x4 *>(L + kUnitBf16.aq + lane * 16), aq_h, aq_l);
         f32x4 O = mma16(aq_h, e_h, xq);
         O = mma16(aq_l, e_h, O);
         O = mma16(aq_h, e_l, O);
@@ -413,15 +452,19 @@ __global__ __launch_bounds__(64 * kK2Waves) void k2_mfma(const uint16_t *__restr
             if (4 * g + r < len) out[((int64_t)(t0 + 4 * g + r) * H + h) * kD + vcol] = f32_to_bf16_bits(O[r]);
         // S^T <- Diag(gamma) S^T + K_end^T E
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const u32x4 kq = cur.ke[t >> 1];
-            const u32x2 kh = (t & 1) ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]};
-            const bf16x4 kt = __builtin_bit_cast(bf16x4, kh);
-            f32x4 s = st[t] * cur.gm[t];
-            s = mma16(kt, e_h, s);
-            st[t] = mma16(kt, e_l, s);
+        for (int p = 0; p < 4; ++p) {
+            const u32x4 kq = *reinterpret_cast<const u32x4 *>(L + kUnitBf16.ke + p * 1024 + lane * 16);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int t = 2 * p + hh;
+                const bf16x4 kt = __builtin_bit_cast(bf16x4, hh ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]});
+                const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kUnitBf16.gm + (16 * t + 4 * g) * 4);
+                f32x4 s = st[t] * gm;
+                s = mma16(kt, e_h, s);
+                st[t] = mma16(kt, e_l, s);
+            }
         }
-        if (j + 1 < nch) cur = nxt;
+        bar_sync();  // this chunk's slot may be refilled; chunk j+1 is published
     }
     if (s1) {
 #pragma unroll
@@ -429,29 +472,32 @@ __global__ __launch_bounds__(64 * kK2Waves) void k2_mfma(const uint16_t *__restr
     }
 }
 
-template <typename TSt>
-static hipError_t launch_mfma_t(const Problem &p, hipStream_t s)
+hipError_t launch_prep_mfma(const Problem &p, hipStream_t s)
 {
+    if (p.n_c_max == 0) return hipSuccess;
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
-    char *units = p.ws + p.lay.units;
-    if (p.n_c_max > 0) {
-        const int wpb = (p.H % 4 == 0) ? 4 : (p.H % 2 == 0 ? 2 : 1);
-        hipLaunchKernelGGL(k1_mfma, dim3((unsigned)p.n_c_max, p.H / wpb), dim3(64 * wpb), 0, s,
-                           (const uint16_t *)p.q, (const uint16_t *)p.k, (const uint16_t *)p.g,
-                           (const uint16_t *)p.beta, tok, chk, (int)p.N, p.H, p.n_c_max, p.lb, p.scale, units);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((k2_mfma<TSt>), dim3((unsigned)(p.N * p.H)), dim3(64 * kK2Waves), 0, s,
-                       (const uint16_t *)p.v, (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H,
-                       p.n_c_max, (const char *)units);
+    const int wpb = (p.H % 4 == 0) ? 4 : (p.H % 2 == 0 ? 2 : 1);  // waves per block divide H
+    hipLaunchKernelGGL(k1_mfma, dim3((unsigned)p.n_c_max, p.H / wpb), dim3(64 * wpb), 0, s, (const uint16_t *)p.q,
+                       (const uint16_t *)p.k, (const uint16_t *)p.g, (const uint16_t *)p.beta, tok, chk, (int)p.N,
+                       p.H, p.n_c_max, p.lb, p.scale, p.ws + p.lay.units);
     return hipGetLastError();
 }
 
-hipError_t launch_mfma(const Problem &p, hipStream_t s)
+template <typename TSt>
+static hipError_t launch_recur_mfma_t(const Problem &p, hipStream_t s)
 {
-    return p.st_bf16 ? launch_mfma_t<uint16_t>(p, s) : launch_mfma_t<float>(p, s);
+    const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
+    const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
+    hipLaunchKernelGGL((k2_mfma<TSt>), dim3((unsigned)(p.N * p.H)), dim3(kK2Threads), 0, s, (const uint16_t *)p.v,
+                       (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H, p.n_c_max,
+                       (const char *)(p.ws + p.lay.units));
+    return hipGetLastError();
+}
+
+hipError_t launch_recur_mfma(const Problem &p, hipStream_t s)
+{
+    return p.st_bf16 ? launch_recur_mfma_t<uint16_t>(p, s) : launch_recur_mfma_t<float>(p, s);
 }
 
 }  // namespace kda

@@ -281,30 +281,39 @@ __global__ __launch_bounds__(128) void k2_ref(const TIn *__restrict__ v, const T
     }
 }
 
-template <typename TIn, typename TSt>
-static hipError_t launch_ref_t(const Problem &p, hipStream_t s)
+template <typename TIn>
+static hipError_t launch_prep_ref_t(const Problem &p, hipStream_t s)
 {
+    if (p.n_c_max == 0) return hipSuccess;
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
-    char *units = p.ws + p.lay.units;
-    if (p.n_c_max > 0) {
-        hipLaunchKernelGGL((k1_ref<TIn>), dim3((unsigned)p.n_c_max, p.H), dim3(256), 0, s,
-                           (const TIn *)p.q, (const TIn *)p.k, (const TIn *)p.g, (const TIn *)p.beta, tok, chk,
-                           (int)p.N, p.H, p.n_c_max, p.lb, p.scale, units);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((k2_ref<TIn, TSt>), dim3((unsigned)p.N, p.H), dim3(128), 0, s, (const TIn *)p.v,
-                       (const TSt *)p.s0, (TSt *)p.s1, (TIn *)p.out, tok, chk, p.H, p.n_c_max,
-                       (const char *)units);
+    hipLaunchKernelGGL((k1_ref<TIn>), dim3((unsigned)p.n_c_max, p.H), dim3(256), 0, s, (const TIn *)p.q,
+                       (const TIn *)p.k, (const TIn *)p.g, (const TIn *)p.beta, tok, chk, (int)p.N, p.H,
+                       p.n_c_max, p.lb, p.scale, p.ws + p.lay.units);
     return hipGetLastError();
 }
 
-hipError_t launch_ref(const Problem &p, hipStream_t s)
+template <typename TIn, typename TSt>
+static hipError_t launch_recur_ref_t(const Problem &p, hipStream_t s)
+{
+    const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
+    const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
+    hipLaunchKernelGGL((k2_ref<TIn, TSt>), dim3((unsigned)p.N, p.H), dim3(128), 0, s, (const TIn *)p.v,
+                       (const TSt *)p.s0, (TSt *)p.s1, (TIn *)p.out, tok, chk, p.H, p.n_c_max,
+                       (const char *)(p.ws + p.lay.units));
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_ref(const Problem &p, hipStream_t s)
+{
+    return p.io_bf16 ? launch_prep_ref_t<uint16_t>(p, s) : launch_prep_ref_t<float>(p, s);
+}
+
+hipError_t launch_recur_ref(const Problem &p, hipStream_t s)
 {
     if (p.io_bf16)
-        return p.st_bf16 ? launch_ref_t<uint16_t, uint16_t>(p, s) : launch_ref_t<uint16_t, float>(p, s);
-    return p.st_bf16 ? launch_ref_t<float, uint16_t>(p, s) : launch_ref_t<float, float>(p, s);
+        return p.st_bf16 ? launch_recur_ref_t<uint16_t, uint16_t>(p, s) : launch_recur_ref_t<uint16_t, float>(p, s);
+    return p.st_bf16 ? launch_recur_ref_t<float, uint16_t>(p, s) : launch_recur_ref_t<float, float>(p, s);
 }
 
 }  // namespace kda
