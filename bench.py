@@ -101,7 +101,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        print("bench.py: the KDA forward runs on a single GPU; multi-GPU runs are not supported (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,0 +1,83 @@
+"""Summaries of rocprofv3 output for the KDA kernels.
+
+    python -m kimi_delta_attention_k1_amd.profsum stats  <kernel_stats.csv> <command...>
+    python -m kimi_delta_attention_k1_amd.profsum traffic <fetch_counter_collection.csv>
+           <write_counter_collection.csv> <workload> <copy_probe_mib>
+
+`stats` prints a Markdown table of per-kernel call counts and durations.
+`traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into HBM bytes per
+launch. Both counters are scaled by what they read for the plain device copy
+of known size that bench.py --copy-probe-mib runs in the same process
+(the runtime's copy kernel; its last dispatches are the probe). The result is
+merged into profiles/traffic_counters.json, keyed by workload and kernel, with
+the SHA-256 of the kernel source so bench.py reports null once the kernels
+change.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic_counters.json")
+SRC = os.path.join(ROOT, "kimi_delta_attention_k1_amd", "csrc", "kda_mfma.hip")
+SHORT = {"k1_mfma": "kda::k1_mfma", "k2_mfma": "kda::k2_mfma", "k0_chunk_map": "kda::k0_chunk_map",
+         "copy": "__amd_rocclr_copyBuffer"}
+
+
+def short_name(kernel_name: str) -> str:
+    for short, key in SHORT.items():
+        if key in kernel_name:
+            return short
+    return kernel_name.split("(")[0][:40]
+
+
+def stats(path: str, command: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = [f"Command: `{command}`", "", "| kernel | calls | avg us | min us | max us | % time |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    return "\n".join(out)
+
+
+def _per_kernel(path):
+    per = {}
+    for r in csv.DictReader(open(path)):
+        per.setdefault(short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return per
+
+
+def traffic(fetch_csv, write_csv, workload, probe_mib):
+    f, w = _per_kernel(fetch_csv), _per_kernel(write_csv)
+    probe_kib = probe_mib * 1024.0
+    # the probe copies are the last copy dispatches (three of them)
+    ff = probe_kib / (sum(f["copy"][-3:]) / 3)
+    fw = probe_kib / (sum(w["copy"][-3:]) / 3)
+    src = hashlib.sha256(open(SRC, "rb").read()).hexdigest()
+    rec = {}
+    if os.path.exists(TRAFFIC):
+        rec = json.load(open(TRAFFIC))
+    ent = rec.setdefault(workload, {})
+    for k in ("k1_mfma", "k2_mfma"):
+        fk = sum(f[k]) / len(f[k])
+        wk = sum(w[k]) / len(w[k])
+        ent[k] = {"fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+                  "fetch_scale": round(ff, 4), "write_scale": round(fw, 4),
+                  "bytes_per_launch": int(round((fk * ff + wk * fw) * 1024)),
+                  "dispatches": len(f[k]), "src_sha256": src}
+    os.makedirs(os.path.dirname(TRAFFIC), exist_ok=True)
+    with open(TRAFFIC, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+    return ent
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        print(stats(sys.argv[2], " ".join(sys.argv[3:])))
+    elif sys.argv[1] == "traffic":
+        print(json.dumps(traffic(sys.argv[2], sys.argv[3], sys.argv[4], float(sys.argv[5])), indent=1))
