@@ -29,8 +29,8 @@ constexpr float kL2Eps = 1e-6f;  // L2-norm epsilon: x / sqrt(sum x^2 + eps)
 //   KB   4096  K_b  = khat * exp(G_i)           bf16, 16x16x32 A-operand order
 //   QB   4096  Q_b  = s qhat * exp(G_i)         bf16, same order
 //   KE   4096  K_end= khat * exp(G_last - G_i)  bf16, 16x16x16 A-operand order
-//   AB   1024  (A^kk Diag(beta))^T              fp32, lane-major float4
-//   AQ   1024  (A^qk)^T                         fp32, lane-major float4
+//   AB   1024  (A^kk Diag(beta))^T  split into bf16 hi/lo: lane-major {hi x4, lo x4}
+//   AQ   1024  (A^qk)^T             split into bf16 hi/lo: lane-major {hi x4, lo x4}
 //   GM    512  gamma = exp(G_last)              fp32 [128]
 // fp32 path unit (27136 B), plain row-major:
 //   KB 8192 [16][128], QB 8192, KE 8192, AB 1024 [16][16] (A^kk Diag(beta)),

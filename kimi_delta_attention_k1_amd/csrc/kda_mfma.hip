@@ -65,6 +65,20 @@ __device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo)
     }
 }
 
+// {hi[0..3], lo[0..3]} with x = hi + lo: one 16x16x32 A operand that carries
+// both halves of a split 16x16 tile (its first half alone is the hi tile)
+__device__ __forceinline__ bf16x8 split8(f32x4 x)
+{
+    bf16x4 h, l;
+    split4(x, h, l);
+    return bf16x8{h[0], h[1], h[2], h[3], l[0], l[1], l[2], l[3]};
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b)
+{
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 // logistic sigmoid from 2^x and a reciprocal
 __device__ __forceinline__ float sigmoid_fast(float x)
 {
@@ -178,32 +192,32 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
 
     // ---- R = strict_tril(Diag(beta) K' K''^T), R^T, (A^qk)^T with K' = khat e^{G-Gref},
     //      K'' = khat e^{Gref-G}, Gref = G at token 7 (keeps both factors within e^{+-8|lb|}).
-    //      bf16 hi/lo split products: fp32-level accuracy from the bf16 matrix cores.
+    //      A^qk adds straight into the outputs, so its products use bf16 hi/lo splits
+    //      (fp32-level accuracy); R enters only through (I+R)^-1 and plain bf16 suffices.
+    //      dn = e^{Gref-G} is kept for K_end below.
     f32x4 dR = {0.f, 0.f, 0.f, 0.f}, dRT = dR, dAQT = dR;
-    const int src7 = (lane & 48) | 7;
+    const int src7 = (lane & 48) | 7, src15 = (lane & 48) | 15;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        bf16x8 kr_h, kr_l, ki_h, ki_l, qr_h, qr_l;
+        bf16x8 kr_h, ki_h, ki_l, qr_h, qr_l;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int i = 8 * s + e;
             const float gref = __shfl(gf[i], src7);
             const float up = __builtin_amdgcn_exp2f(gf[i] - gref);
             const float dn = __builtin_amdgcn_exp2f(gref - gf[i]);
+            const float cl = __shfl(up, src15);  // e^{G_last - Gref} for this channel
+            // K_end = khat e^{G_last - G} = khat e^{Gref - G} e^{G_last - Gref}, to LDS as [channel][token]
+            sKE[wv][32 * g + i][tok] = __builtin_bit_cast(uint16_t, (__bf16)(kf[i] * dn * cl));
             const float kr = kf[i] * up, ki = kf[i] * dn, qr = qf[i] * up;
             kr_h[e] = (__bf16)kr;
-            kr_l[e] = (__bf16)(kr - (float)kr_h[e]);
             ki_h[e] = (__bf16)ki;
             ki_l[e] = (__bf16)(ki - (float)ki_h[e]);
             qr_h[e] = (__bf16)qr;
             qr_l[e] = (__bf16)(qr - (float)qr_h[e]);
         }
         dR = mma32(kr_h, ki_h, dR);
-        dR = mma32(kr_l, ki_h, dR);
-        dR = mma32(kr_h, ki_l, dR);
         dRT = mma32(ki_h, kr_h, dRT);
-        dRT = mma32(ki_l, kr_h, dRT);
-        dRT = mma32(ki_h, kr_l, dRT);
         dAQT = mma32(ki_h, qr_h, dAQT);
         dAQT = mma32(ki_l, qr_h, dAQT);
         dAQT = mma32(ki_h, qr_l, dAQT);
@@ -235,40 +249,28 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
     for (int r = 0; r < 4; ++r) ABT[r] = beta_row[r] * AT[r];
 
     char *u = units + ((int64_t)h * n_c_max + c) * kUnitBf16.bytes;
-    reinterpret_cast<f32x4 *>(u + kUnitBf16.ab)[lane] = ABT;
-    reinterpret_cast<f32x4 *>(u + kUnitBf16.aq)[lane] = AQT;
+    reinterpret_cast<bf16x8 *>(u + kUnitBf16.ab)[lane] = split8(ABT);
+    reinterpret_cast<bf16x8 *>(u + kUnitBf16.aq)[lane] = split8(AQT);
 
-    // ---- K_b, Q_b (16x16x32 A-operand order), K_end (via LDS transpose), gamma
-    const int src15 = (lane & 48) | 15;
-    float gl[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) gl[i] = __shfl(gf[i], src15);
+    // ---- K_b, Q_b (16x16x32 A-operand order); gamma = e^{G_last} from token 15's e^{G}
+    float *gm = reinterpret_cast<float *>(u + kUnitBf16.gm) + 32 * g;
 #pragma unroll
     for (int gp = 0; gp < 4; ++gp) {  // destination lane tok + 16 gp, k step = g
         bf16x8 kb, qb;
+        float dec[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int i = (e < 4) ? (4 * gp + e) : (16 + 4 * gp + e - 4);
-            const float dec = __builtin_amdgcn_exp2f(gf[i]);
-            kb[e] = (__bf16)(kf[i] * dec);
-            qb[e] = (__bf16)(qf[i] * dec);
+            dec[e] = __builtin_amdgcn_exp2f(gf[i]);
+            kb[e] = (__bf16)(kf[i] * dec[e]);
+            qb[e] = (__bf16)(qf[i] * dec[e]);
         }
         const int64_t slot = (int64_t)g * 1024 + (tok + 16 * gp) * 16;
         *reinterpret_cast<bf16x8 *>(u + kUnitBf16.kb + slot) = kb;
         *reinterpret_cast<bf16x8 *>(u + kUnitBf16.qb + slot) = qb;
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const float ke = kf[i] * __builtin_amdgcn_exp2f(gl[i] - gf[i]);
-        sKE[wv][32 * g + i][tok] = __builtin_bit_cast(uint16_t, (__bf16)ke);
-    }
-    if (tok == 15) {
-        float *gm = reinterpret_cast<float *>(u + kUnitBf16.gm) + 32 * g;
-#pragma unroll
-        for (int i = 0; i < 32; i += 4) {
-            f32x4 x = {__builtin_amdgcn_exp2f(gf[i]), __builtin_amdgcn_exp2f(gf[i + 1]),
-                       __builtin_amdgcn_exp2f(gf[i + 2]), __builtin_amdgcn_exp2f(gf[i + 3])};
-            *reinterpret_cast<f32x4 *>(gm + i) = x;
+        if (tok == 15) {
+            *reinterpret_cast<f32x4 *>(gm + 4 * gp) = f32x4{dec[0], dec[1], dec[2], dec[3]};
+            *reinterpret_cast<f32x4 *>(gm + 16 + 4 * gp) = f32x4{dec[4], dec[5], dec[6], dec[7]};
         }
     }
     __syncthreads();
@@ -296,17 +298,22 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
 // publishes a slot and recycles the previous one. The barrier is a bare
 // s_barrier: a fenced barrier would drain the prefetch queue every chunk.
 // ---------------------------------------------------------------------------
-constexpr int kK2Consumers = 8;
-constexpr int kK2Producers = 2;
-constexpr int kK2Threads = 64 * (kK2Consumers + kK2Producers);
 constexpr int kK2Slots = 6;
 constexpr int kSlotKB = 20;                        // 1 KB copy instructions per chunk
 constexpr int kSlotBytes = kSlotKB * 1024;         // unit 14848 | pad 512 | v 4096 | pad 1024
 constexpr int kVOff = 15 * 1024;                   // v tile offset inside a slot
-constexpr int kKBPerProducer = kSlotKB / kK2Producers;                 // 10
-constexpr int kProdPending = (kK2Slots - 2) * kKBPerProducer;          // loads allowed in flight
-static_assert(kProdPending <= 63, "vmcnt holds at most 63 outstanding loads");
 static_assert(kUnitBf16.bytes <= (size_t)kVOff, "unit must fit below the v tile");
+
+// Workgroup shape for CONS consumer waves (8 / CONS workgroups per (sequence, head)).
+template <int CONS> struct K2Shape {
+    static constexpr int producers = CONS >= 4 ? 2 : 1;
+    static constexpr int slots = producers == 2 ? kK2Slots : 5;
+    static constexpr int threads = 64 * (CONS + producers);
+    static constexpr int kb_per_producer = kSlotKB / producers;
+    static constexpr int pending = (slots - 2) * kb_per_producer;  // loads allowed in flight
+    static_assert(pending <= 63, "vmcnt holds at most 63 outstanding loads");
+    static_assert(kSlotKB % producers == 0, "producers split a slot evenly");
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -338,23 +345,35 @@ template <> __device__ __forceinline__ void st_state4<uint16_t>(uint16_t *p, f32
     *reinterpret_cast<u32x2 *>(p) = y;
 }
 
-template <typename TSt>
-__global__ __launch_bounds__(kK2Threads) void k2_mfma(const uint16_t *__restrict__ v, const TSt *s0, TSt *s1,
-                                                       uint16_t *__restrict__ out,
-                                                       const int32_t *__restrict__ tok_off,
-                                                       const int32_t *__restrict__ chunk_off, int H,
-                                                       int64_t n_c_max, const char *__restrict__ units)
+template <typename TSt, int CONS>
+__global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
+    const uint16_t *__restrict__ v, const TSt *s0, TSt *s1, uint16_t *__restrict__ out,
+    const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off, int H, int pairs, int64_t n_c_max,
+    const char *__restrict__ units)
 {
-    __shared__ __attribute__((aligned(1024))) char lds[kK2Slots][kSlotBytes];
+    using Sh = K2Shape<CONS>;
+    constexpr int kGroups = 8 / CONS;  // workgroups per (sequence, head)
+    __shared__ __attribute__((aligned(1024))) char lds[Sh::slots][kSlotBytes];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int n = blockIdx.x / H, h = blockIdx.x % H;
+    // Workgroup b runs on XCD b % 8; the kGroups workgroups of one pair share an
+    // XCD (and its L2), which serves the repeated unit reads.
+    int pair = blockIdx.x, wbase = 0;
+    if (kGroups > 1) {
+        const int b = blockIdx.x;
+        pair = (b & 7) + 8 * (b / (8 * kGroups));
+        wbase = ((b >> 3) % kGroups) * CONS;
+        if (pair >= pairs) return;  // whole workgroup: no barrier is entered
+    }
+    const int n = pair / H, h = pair % H;
     const int c0 = chunk_off[n], nch = chunk_off[n + 1] - c0;
     const int tb = tok_off[n], te = tok_off[n + 1];
 
-    if (w >= kK2Consumers) {
+    if (w >= CONS) {
         // ------------------------------------------------------------ producers
         if (nch == 0) return;  // uniform over the workgroup: nobody enters the barriers
-        const int pw = w - kK2Consumers;
+        const int pw = w - CONS;
+        constexpr int kKBPerProducer = Sh::kb_per_producer;
+        constexpr int kProdPending = Sh::pending;
         const char *ubase = units + ((int64_t)h * n_c_max + c0) * kUnitBf16.bytes;
         const char *vb = reinterpret_cast<const char *>(v);
         auto copy_chunk = [&](int j, int slot) {
@@ -378,12 +397,12 @@ __global__ __launch_bounds__(kK2Threads) void k2_mfma(const uint16_t *__restrict
             }
         };
 #pragma unroll
-        for (int s = 0; s < kK2Slots - 1; ++s) copy_chunk(s, s);
+        for (int s = 0; s < Sh::slots - 1; ++s) copy_chunk(s, s);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kProdPending) : "memory");  // chunk 0 landed
         bar_sync();
 #pragma unroll 1
         for (int j = 0; j < nch; ++j) {
-            copy_chunk(j + kK2Slots - 1, (j + kK2Slots - 1) % kK2Slots);
+            copy_chunk(j + Sh::slots - 1, (j + Sh::slots - 1) % Sh::slots);
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kProdPending) : "memory");  // chunk j+1 landed
             bar_sync();
         }
@@ -392,7 +411,7 @@ __global__ __launch_bounds__(kK2Threads) void k2_mfma(const uint16_t *__restrict
     }
 
     // ---------------------------------------------------------------- consumers
-    const int g = lane >> 4, vcol = 16 * w + (lane & 15);
+    const int g = lane >> 4, vcol = 16 * (wbase + w) + (lane & 15);
     const int64_t sbase = (((int64_t)n * H + h) * kD + vcol) * kD + 4 * g;
     f32x4 st[8];
 #pragma unroll
@@ -404,7 +423,7 @@ __global__ __launch_bounds__(kK2Threads) void k2_mfma(const uint16_t *__restrict
     if (nch > 0) bar_sync();
 #pragma unroll 1
     for (int j = 0; j < nch; ++j) {
-        const char *L = lds[j % kK2Slots];
+        const char *L = lds[j % Sh::slots];
         const int t0 = tb + j * kC;
         const int len = min(kC, te - t0);
 
@@ -434,23 +453,33 @@ __global__ __launch_bounds__(kK2Threads) void k2_mfma(const uint16_t *__restrict
             const uint16_t vr = *reinterpret_cast<const uint16_t *>(L + kVOff + tr * 256 + vcol * 2);
             eb[r] = (tr < len ? bf16_bits_to_f32(vr) : 0.f) - xk[r];
         }
-        bf16x4 eb_h, eb_l, ab_h, ab_l, aq_h, aq_l, e_h, e_l;
+        // A operands arrive as {hi, lo}: [hi | lo] x [x_hi ; x_hi] + hi x x_lo is the
+        // split product hi*x_hi + lo*x_hi + hi*x_lo in two instructions.
+        bf16x4 eb_h, eb_l, e_h, e_l;
         split4(eb, eb_h, eb_l);
-        split4(*reinterpret_cast<const f32x4 *>(L + kUnitBf16.ab + lane * 16), ab_h, ab_l);
+        const bf16x8 ab = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.ab + lane * 16);
+        const bf16x4 ab_h = {ab[0], ab[1], ab[2], ab[3]};
         f32x4 E = {0.f, 0.f, 0.f, 0.f};
-        E = mma16(ab_h, eb_h, E);
-        E = mma16(ab_l, eb_h, E);
+        E = mma32(ab, cat8(eb_h, eb_h), E);
         E = mma16(ab_h, eb_l, E);
         split4(E, e_h, e_l);
         // O = Q_b S^T + A^qk E
-        split4(*reinterpret_cast<const f32x4 *>(L + kUnitBf16.aq + lane * 16), aq_h, aq_l);
-        f32x4 O = mma16(aq_h, e_h, xq);
-        O = mma16(aq_l, e_h, O);
+        const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.aq + lane * 16);
+        const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]};
+        f32x4 O = mma32(aq, cat8(e_h, e_h), xq);
         O = mma16(aq_h, e_l, O);
+        uint16_t *orow = out + ((int64_t)(t0 + 4 * g) * H + h) * kD + vcol;
+        const int64_t rstride = (int64_t)H * kD;
+        if (len == kC) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (4 * g + r < len) out[((int64_t)(t0 + 4 * g + r) * H + h) * kD + vcol] = f32_to_bf16_bits(O[r]);
-        // S^T <- Diag(gamma) S^T + K_end^T E
+            for (int r = 0; r < 4; ++r) orow[r * rstride] = __builtin_bit_cast(uint16_t, (__bf16)O[r]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r < len) orow[r * rstride] = __builtin_bit_cast(uint16_t, (__bf16)O[r]);
+        }
+        // S^T <- Diag(gamma) S^T + K_end^T (E_hi + E_lo): [K_end | K_end] x [E_hi ; E_lo]
+        const bf16x8 e_hl = cat8(e_h, e_l);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const u32x4 kq = *reinterpret_cast<const u32x4 *>(L + kUnitBf16.ke + p * 1024 + lane * 16);
@@ -459,9 +488,7 @@ __global__ __launch_bounds__(kK2Threads) void k2_mfma(const uint16_t *__restrict
                 const int t = 2 * p + hh;
                 const bf16x4 kt = __builtin_bit_cast(bf16x4, hh ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]});
                 const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kUnitBf16.gm + (16 * t + 4 * g) * 4);
-                f32x4 s = st[t] * gm;
-                s = mma16(kt, e_h, s);
-                st[t] = mma16(kt, e_l, s);
+                st[t] = mma32(cat8(kt, kt), e_hl, st[t] * gm);
             }
         }
         bar_sync();  // this chunk's slot may be refilled; chunk j+1 is published
@@ -484,15 +511,30 @@ hipError_t launch_prep_mfma(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename TSt>
-static hipError_t launch_recur_mfma_t(const Problem &p, hipStream_t s)
+template <typename TSt, int CONS>
+static hipError_t launch_k2(const Problem &p, hipStream_t s)
 {
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
-    hipLaunchKernelGGL((k2_mfma<TSt>), dim3((unsigned)(p.N * p.H)), dim3(kK2Threads), 0, s, (const uint16_t *)p.v,
-                       (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H, p.n_c_max,
+    const int pairs = (int)(p.N * p.H);
+    constexpr int groups = 8 / CONS;
+    const unsigned grid = groups == 1 ? (unsigned)pairs : (unsigned)((pairs + 7) / 8 * 8 * groups);
+    hipLaunchKernelGGL((k2_mfma<TSt, CONS>), dim3(grid), dim3(K2Shape<CONS>::threads), 0, s, (const uint16_t *)p.v,
+                       (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H, pairs, p.n_c_max,
                        (const char *)(p.ws + p.lay.units));
     return hipGetLastError();
+}
+
+// Consumer waves per workgroup: the largest that still puts about one
+// workgroup on every one of the 256 compute units.
+template <typename TSt>
+static hipError_t launch_recur_mfma_t(const Problem &p, hipStream_t s)
+{
+    const int64_t pairs = p.N * p.H;
+    if (pairs >= 192) return launch_k2<TSt, 8>(p, s);
+    if (pairs >= 96) return launch_k2<TSt, 4>(p, s);
+    if (pairs >= 48) return launch_k2<TSt, 2>(p, s);
+    return launch_k2<TSt, 1>(p, s);
 }
 
 hipError_t launch_recur_mfma(const Problem &p, hipStream_t s)

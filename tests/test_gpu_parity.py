@@ -237,8 +237,9 @@ def _decode_unit(raw: torch.Tensor):
                 tok = 4 * g + (e % 4)
                 kch = 32 * p + t + (16 if e >= 4 else 0)
                 ke[tok, kch] = KE[p, lane, e]
-    ab = u[12288:13312].view(torch.float32).view(64, 4)
-    aq = u[13312:14336].view(torch.float32).view(64, 4)
+    hl = lambda a, b: u[a:b].view(torch.bfloat16).float().view(64, 2, 4).sum(1)  # noqa: E731  hi + lo
+    ab = hl(12288, 13312)
+    aq = hl(13312, 14336)
     AB = torch.zeros(16, 16)
     AQ = torch.zeros(16, 16)
     for lane in range(64):
@@ -279,3 +280,12 @@ def test_k1_intermediates_against_chunked_oracle(gpu):
                 assert np.max(np.abs(d["Aqk"][:L, :L].numpy() - it["Aqk"])) <= 1e-4 * np.max(np.abs(it["Aqk"]))
                 assert np.allclose(d["gamma"].numpy(), it["gamma"], rtol=5e-5, atol=0)
             chunk += 1
+
+
+@pytest.mark.parametrize("nseq,H", [(12, 6), (30, 4), (50, 4)])
+def test_pair_counts_select_each_recurrence_shape(gpu, nseq, H):
+    """(sequence, head) pair counts 72, 120 and 200 run the recurrence with 2, 4 and
+    8 consumer waves per workgroup (4, 2 and 1 workgroups per pair)."""
+    _banner(f"{nseq} sequences x {H} heads = {nseq * H} pairs")
+    w = workloads.make(None, H, seed=41 + nseq, init_std=0.02, lens_drawn=(1, 70, nseq))
+    compare(w, *run_gpu(w, gpu), run_oracle(w), bf16_tol, f"{nseq * H} pairs")
