@@ -85,6 +85,12 @@ __device__ __forceinline__ float sigmoid_fast(float x)
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
 
+// value of lane n of the caller's 16-lane row (DPP row_newbcast: no LDS round trip)
+template <int N> __device__ __forceinline__ float row_bcast(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, false));
+}
+
 // value of lane (l - n) of the same 16-lane row, 0 for lanes below n
 template <int N> __device__ __forceinline__ float row_shr(float x)
 {
@@ -196,17 +202,16 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
     //      (fp32-level accuracy); R enters only through (I+R)^-1 and plain bf16 suffices.
     //      dn = e^{Gref-G} is kept for K_end below.
     f32x4 dR = {0.f, 0.f, 0.f, 0.f}, dRT = dR, dAQT = dR;
-    const int src7 = (lane & 48) | 7, src15 = (lane & 48) | 15;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         bf16x8 kr_h, ki_h, ki_l, qr_h, qr_l;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int i = 8 * s + e;
-            const float gref = __shfl(gf[i], src7);
+            const float gref = row_bcast<7>(gf[i]);  // G of token 7, same channel
             const float up = __builtin_amdgcn_exp2f(gf[i] - gref);
             const float dn = __builtin_amdgcn_exp2f(gref - gf[i]);
-            const float cl = __shfl(up, src15);  // e^{G_last - Gref} for this channel
+            const float cl = row_bcast<15>(up);  // e^{G_last - Gref} for this channel
             // K_end = khat e^{G_last - G} = khat e^{Gref - G} e^{G_last - Gref}, to LDS as [channel][token]
             sKE[wv][32 * g + i][tok] = __builtin_bit_cast(uint16_t, (__bf16)(kf[i] * dn * cl));
             const float kr = kf[i] * up, ki = kf[i] * dn, qr = qf[i] * up;
