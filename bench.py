@@ -1,19 +1,21 @@
 """Benchmark of the KDA forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 30] [--workload c3]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 30] [--workload c3] [--path auto]
 
-One step = one full forward (chunk map, chunk-parallel kernel, recurrence
-kernel) over the whole seeded synthetic batch, with inputs already resident
-in HBM. W untimed warmup steps, then K timed steps between two device
-synchronisations; HIP events on the launch stream between the two stages give
-each kernel's average duration inside the same timed region. Prints ONE JSON
-line. Default workload c3 (8 packed sequences x 8192 tokens, H=32, D=128,
-bf16), the headline metric's head count.
+One step = one full forward over the whole seeded synthetic batch, with inputs
+already resident in HBM: the chunk map plus either the single-pass kernel
+(path "fused") or the chunk-parallel and recurrence kernels (path "split");
+"auto" is the library's own rule. W untimed warmup steps, then K timed steps
+between two device synchronisations; HIP events recorded on the launch stream
+around each kernel call give each kernel's average duration inside the same
+timed region (the fused call's interval also holds the few-microsecond chunk
+map). The other path is then timed the same way for comparison. Prints ONE
+JSON line. Default workload c3 (8 packed sequences x 8192 tokens, H=32,
+D=128, bf16), the headline metric's head count.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -27,7 +29,6 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E peak
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
 UNIT_BYTES = 14848           # workspace bytes per (chunk, head) unit, bf16 path
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SRC = os.path.join(ROOT, "kimi_delta_attention_k1_amd", "csrc", "kda_mfma.hip")
 
 
 def algorithmic_work(w):
@@ -38,35 +39,34 @@ def algorithmic_work(w):
         beta_raw (2 B per token-head), writes one 14848 B workspace unit;
       recurrence kernel: reads the unit and v (256 B per token-head), writes o
         (256 B per token-head); per (sequence, head) it reads the 64 KiB fp32
-        initial state (when given) and writes the 64 KiB final state.
-    Recurrence flops per unit: K_b S^T and Q_b S^T (2 x 2*16*128*128), the
-    state update K_end^T E (2*128*16*128), A^kk E and A^qk E (2 x 2*16*16*128)
-    and the decay (128*128).
+        initial state (when given) and writes the 64 KiB final state;
+      single-pass kernel: reads q, k, g_raw, v and beta_raw (4 x 256 + 2 B per
+        token-head), writes o (256 B per token-head), and the states as above.
+    Recurrence flops per unit (both paths): K_b S^T and Q_b S^T
+    (2 x 2*16*128*128), the state update K_end^T E (2*128*16*128), A^kk E and
+    A^qk E (2 x 2*16*16*128) and the decay (128*128).
     """
     H = w.H
     units = sum((L + 15) // 16 for L in w.seq_lens) * H
     th = w.T_tot * H
-    st = w.N * H * 128 * 128 * 4
+    st = w.N * H * 128 * 128 * 4 * (2 if w.initial_state is not None else 1)
     k1 = th * (3 * 256 + 2) + units * UNIT_BYTES
-    k2 = units * UNIT_BYTES + th * 512 + st * (2 if w.initial_state is not None else 1)
+    k2 = units * UNIT_BYTES + th * 512 + st
+    kf = th * (4 * 256 + 2 + 256) + st
     flops = units * (3 * 2 * 16 * 128 * 128 + 2 * 2 * 16 * 16 * 128 + 128 * 128)
-    return dict(units=units, k1_bytes=k1, k2_bytes=k2, k2_flops=flops)
-
-
-def src_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    return dict(units=units, k1_bytes=k1, k2_bytes=k2, kf_bytes=kf, flops=flops)
 
 
 def traffic_for(kernel, workload):
-    """Counter-measured HBM bytes per launch, if taken on the current kernel source."""
+    """Counter-measured HBM bytes per launch, if taken on the kernel's current sources."""
+    from kimi_delta_attention_k1_amd.profsum import src_hash
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     ent = rec.get(workload, {}).get(kernel)
-    if not ent or ent.get("src_sha256") != src_hash():
+    if not ent or ent.get("src_sha256") != src_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -89,19 +89,50 @@ def cpu_baseline(w, nseq):
                       f"recurrence, {dt:.2f} s wall"}
 
 
+def time_path(call, path, steps, warmup):
+    """Run `steps` timed forwards on `path`; returns wall ms per step and the
+    event-measured average ms of each kernel call."""
+    import torch
+    if path == "fused":
+        stages = [("kf_fused", call.run)]
+    else:
+        stages = [("k1_mfma", call.prepare), ("k2_mfma", call.recur)]
+    for _ in range(warmup):
+        for _, fn in stages:
+            fn()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for j, (_, fn) in enumerate(stages):
+            fn()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = {name: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j, (name, _) in enumerate(stages)}
+    return wall * 1e3 / steps, kern
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "split"],
+                    help="kernels of the timed step (auto: the library's rule)")
+    ap.add_argument("--compare-steps", type=int, default=100,
+                    help="steps of the other path, timed afterwards for comparison (0: skip)")
     ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU-baseline sample (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: the KDA forward runs on a single GPU; multi-GPU runs are not supported (--gpus must be 1)", file=sys.stderr)
+        print("bench.py: the KDA forward runs on a single GPU; multi-GPU runs are not supported (--gpus must be 1)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -117,28 +148,21 @@ def main():
         shp = (w.N, w.seq_lens[0], w.H, 128)
         q, k, v, g = (t.view(shp) for t in (q, k, v, g))
         b = b.view(shp[:3])
-    call = kda.prepare_call(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu)
+    path = args.path
+    if path == "auto":
+        path = "fused" if w.N * w.H >= kda.FUSED_MIN_PAIRS else "split"
+    other = "split" if path == "fused" else "fused"
+    calls = {p: kda.prepare_call(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu,
+                                 path=p) for p in ("fused", "split")}
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
-        call.prepare()
-        call.recur()
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        call.prepare()
-        ev[i][1].record(stream)
-        call.recur()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    k1_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    k2_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    step_ms = sum(e[0].elapsed_time(e[2]) for e in ev) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step, kern_ms = time_path(calls[path], path, args.steps, args.warmup)
+    compare = None
+    if args.compare_steps > 0:
+        o_ms, o_kern = time_path(calls[other], other, args.compare_steps, min(args.warmup, 10))
+        compare = {"path": other, "steps": args.compare_steps, "ms_per_step": round(o_ms, 4),
+                   "tokens_per_s": round(w.T_tot / (o_ms * 1e-3), 1),
+                   "kernels_avg_ms": {n: round(x, 4) for n, x in o_kern.items()}}
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
@@ -148,21 +172,18 @@ def main():
         torch.cuda.synchronize()
 
     work = algorithmic_work(w)
-    kern = {
-        "k1_mfma": dict(ms=k1_ms, bytes=work["k1_bytes"]),
-        "k2_mfma": dict(ms=k2_ms, bytes=work["k2_bytes"], flops=work["k2_flops"]),
-    }
-    dom = max(kern, key=lambda n: kern[n]["ms"])
+    bytes_of = {"k1_mfma": work["k1_bytes"], "k2_mfma": work["k2_bytes"], "kf_fused": work["kf_bytes"]}
     per_kernel = {}
-    for name, kk in kern.items():
-        gbs = kk["bytes"] / (kk["ms"] * 1e-3) / 1e9
-        ent = {"avg_ms": round(kk["ms"], 4), "algorithmic_bytes": kk["bytes"], "achieved_GBps": round(gbs, 1),
+    for name, ms in kern_ms.items():
+        gbs = bytes_of[name] / (ms * 1e-3) / 1e9
+        ent = {"avg_ms": round(ms, 4), "algorithmic_bytes": bytes_of[name], "achieved_GBps": round(gbs, 1),
                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-        if "flops" in kk:
-            tf = kk["flops"] / (kk["ms"] * 1e-3) / 1e12
-            ent.update({"algorithmic_flops": kk["flops"], "achieved_TFLOPs": round(tf, 2),
+        if name != "k1_mfma":
+            tf = work["flops"] / (ms * 1e-3) / 1e12
+            ent.update({"algorithmic_flops": work["flops"], "achieved_TFLOPs": round(tf, 2),
                         "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)})
         per_kernel[name] = ent
+    dom = max(kern_ms, key=kern_ms.get)
     d = per_kernel[dom]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": d["achieved_GBps"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": d["hbm_frac"], "traffic": traffic_for(dom, args.workload)}
@@ -175,11 +196,13 @@ def main():
         "data": "synthetic (seeded CPU torch.Generator, N(0,1) family; see workloads.py)",
         "config": {"workload": f"{args.workload}: {workloads.DESCRIPTIONS[args.workload]}",
                    "tokens": w.T_tot, "heads": w.H, "head_dim": 128, "sequences": w.N, "chunk": 16,
-                   "lower_bound": w.lower_bound},
-        "event_ms_per_step": round(step_ms, 4),
+                   "lower_bound": w.lower_bound, "path": path},
+        "event_ms_per_step": round(sum(kern_ms.values()), 4),
         "kernels": per_kernel,
         "roofline": roofline,
     }
+    if compare is not None:
+        line["path_compare"] = compare
     if args.cpu_seqs > 0:
         line["cpu_baseline"] = cpu_baseline(w, min(args.cpu_seqs, w.N))
     print(json.dumps(line), flush=True)

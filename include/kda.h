@@ -14,8 +14,9 @@
  * fla_chunk_kda"): alpha_t = exp(lower_bound * sigmoid(g_raw_t)) per key
  * channel, beta_t = sigmoid(beta_raw_t), and q_t, k_t L2-normalised per token
  * as x / sqrt(sum x^2 + 1e-6). It is evaluated with the chunkwise method of the
- * same Doubleword page, section 6, split into a chunk-parallel kernel and a
- * per-(sequence, head) recurrence kernel.
+ * same Doubleword page, section 6, either split into a chunk-parallel kernel
+ * and a per-(sequence, head) recurrence kernel, or in one single-pass kernel
+ * per (sequence, head) (see KDA_FLAG_SPLIT / KDA_FLAG_FUSED).
  *
  * Conventions for every entry point:
  *  - Pointers named "device" point to GPU memory; all others to host memory.
@@ -54,11 +55,13 @@ extern "C" {
 typedef enum kda_status {
     KDA_OK = 0,
     KDA_ERR_NULL_ARG = 1,    /* a required pointer is NULL                          */
-    KDA_ERR_BAD_SHAPE = 2,   /* head_dim != 128, H < 1, B/T/N out of range           */
+    KDA_ERR_BAD_SHAPE = 2,   /* head_dim != 128, H outside [1, 65535], B/T/N out of
+                                range                                              */
     KDA_ERR_BAD_DTYPE = 3,   /* unknown dtype code                                  */
     KDA_ERR_BAD_SEQLENS = 4, /* cu_seqlens given with batch != 1, or N < 1           */
     KDA_ERR_BAD_ARG = 5,     /* lower_bound / scale out of range or non-finite,
-                                unknown flag bits, or out aliasing an input        */
+                                unknown or conflicting flag bits, or out aliasing
+                                an input                                           */
     KDA_ERR_WORKSPACE = 6,   /* workspace NULL, too small, or not 128-B aligned     */
     KDA_ERR_MISALIGNED = 7,  /* a tensor base address is not 16-B aligned           */
     KDA_ERR_HIP = 8          /* a kernel launch failed (HIP runtime error)          */
@@ -74,8 +77,26 @@ typedef enum kda_dtype {
 enum {
     /* Use the fp32 reference kernels (no bf16 matrix-core operands) even for
      * bf16 I/O. fp32 I/O always uses them. */
-    KDA_FLAG_FP32_COMPUTE = 1u
+    KDA_FLAG_FP32_COMPUTE = 1u,
+    /* bf16-compute kda_fwd: run the two-kernel path (chunk-parallel kernel
+     * writing the workspace, then the recurrence kernel), which is what
+     * kda_fwd_prepare + kda_fwd_recur run. */
+    KDA_FLAG_SPLIT = 2u,
+    /* bf16-compute kda_fwd: run the single-pass kernel (one workgroup per
+     * (sequence, head) prepares each chunk in on-chip memory and runs the
+     * recurrence on it; the workspace holds only the chunk map). Not valid
+     * with fp32 compute, with KDA_FLAG_SPLIT, or for kda_fwd_prepare /
+     * kda_fwd_recur. */
+    KDA_FLAG_FUSED = 4u
 };
+/* Without either path flag, bf16-compute kda_fwd runs the single-pass kernel
+ * when num_seqs * num_heads >= KDA_FUSED_MIN_PAIRS (enough (sequence, head)
+ * pairs to occupy the GPU's compute units one pair each) and the two-kernel
+ * path otherwise. The two paths evaluate the same chunkwise equations and
+ * agree to bf16 rounding; they are not bitwise identical (the single pass
+ * applies the L2 normalisation after its in-chunk products instead of
+ * before). */
+#define KDA_FUSED_MIN_PAIRS 256
 
 /*
  * Problem description (host memory).
@@ -95,7 +116,7 @@ typedef struct kda_desc {
     int64_t batch;       /* B >= 1                                           */
     int64_t seqlen;      /* T >= 0 per batch row, or T_tot with cu_seqlens    */
     int64_t num_seqs;    /* N >= 1 (== batch without cu_seqlens)              */
-    int32_t num_heads;   /* H >= 1                                            */
+    int32_t num_heads;   /* H in [1, 65535]                                   */
     int32_t head_dim;    /* must be KDA_HEAD_DIM                              */
     int32_t io_dtype;    /* kda_dtype_t of q, k, v, g_raw, beta_raw and out   */
     int32_t state_dtype; /* kda_dtype_t of initial_state and final_state      */
@@ -107,8 +128,11 @@ typedef struct kda_desc {
  * Bytes of device workspace kda_fwd needs for this description (a pure host
  * function; no GPU call). The size is an upper bound computed from B, T, N
  * and H only, because the chunk count of a packed batch depends on device-side
- * cu_seqlens: at most (T_tot + 15 N) / 16 chunks. Returns 0 if the description
- * itself is invalid (NULL, bad shape or dtype).
+ * cu_seqlens: at most (T_tot + 15 N) / 16 chunks. Unless flags hold
+ * KDA_FLAG_FUSED, it covers the two-kernel path, so the same workspace also
+ * serves kda_fwd_prepare / kda_fwd_recur; with KDA_FLAG_FUSED it is only the
+ * chunk map (a few hundred bytes plus 8 (N + 1)). Returns 0 if the
+ * description itself is invalid (NULL, bad shape, dtype or flags).
  */
 size_t kda_fwd_workspace_size(const kda_desc_t *desc);
 
@@ -154,11 +178,12 @@ kda_status_t kda_fwd(const void *q, const void *k, const void *v,
  * the decayed key/query operands; Doubleword KDA page, sections 6.1-6.3 and
  * 6.6) writes the workspace; the recurrence stage (the chunk-state scan with
  * outputs, sections 6.4-6.5) reads it and writes out and final_state.
- * kda_fwd(args) is exactly kda_fwd_prepare(args) followed by
- * kda_fwd_recur(args). Both take kda_fwd's arguments with the same meaning
- * and checks; recur must see the workspace written by a prepare call with the
- * same arguments, ordered before it (same stream, or an event). Each returns
- * after enqueueing its kernels.
+ * kda_fwd(args) on the two-kernel path (see KDA_FLAG_SPLIT) is exactly
+ * kda_fwd_prepare(args) followed by kda_fwd_recur(args). Both take kda_fwd's
+ * arguments with the same meaning and checks (KDA_FLAG_FUSED is rejected with
+ * KDA_ERR_BAD_ARG); recur must see the workspace written by a prepare call
+ * with the same arguments, ordered before it (same stream, or an event). Each
+ * returns after enqueueing its kernels.
  */
 kda_status_t kda_fwd_prepare(const void *q, const void *k, const void *v,
                              const void *g_raw, const void *beta_raw,

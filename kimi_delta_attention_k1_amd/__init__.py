@@ -7,7 +7,11 @@ CPU or PyTorch fallback: if the library is missing the calls raise.
 
     out, final_state = fwd(q, k, v, g_raw, beta_raw, lower_bound=-5.0,
                            initial_state=None, output_final_state=True,
-                           cu_seqlens=None)
+                           cu_seqlens=None, path="auto")
+
+`path` picks the kernels of a bf16-compute call: "split" (chunk-parallel
+kernel, then recurrence kernel), "fused" (one single-pass kernel) or "auto"
+(the library's rule: fused from KDA_FUSED_MIN_PAIRS (sequence, head) pairs on).
 
 Layouts follow the FlashKDA API (DocSearch FlashKDA digest, "flash_kda.fwd API
 reference"): q, k, v, g_raw are [B, T, H, 128] (or packed [T_tot, H, 128]),
@@ -20,11 +24,15 @@ import ctypes
 import os
 
 __all__ = ["fwd", "prepare_call", "Call", "workspace_size", "KdaError", "load_library", "library_path", "seqlens_flag",
-           "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE"]
+           "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE", "FLAG_SPLIT", "FLAG_FUSED", "FUSED_MIN_PAIRS"]
 
 HEAD_DIM = 128
 CHUNK = 16
 FLAG_FP32_COMPUTE = 1
+FLAG_SPLIT = 2
+FLAG_FUSED = 4
+FUSED_MIN_PAIRS = 256
+_PATH_FLAGS = {"auto": 0, "split": FLAG_SPLIT, "fused": FLAG_FUSED}
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 
@@ -85,10 +93,16 @@ def status_str(status: int) -> str:
     return load_library().kda_status_str(int(status)).decode()
 
 
+def _flags(fp32_compute, path):
+    if path not in _PATH_FLAGS:
+        raise ValueError(f"path must be one of {sorted(_PATH_FLAGS)}, not {path!r}")
+    return (FLAG_FP32_COMPUTE if fp32_compute else 0) | _PATH_FLAGS[path]
+
+
 def workspace_size(batch, seqlen, num_seqs, num_heads, io_dtype=DTYPE_BF16, state_dtype=DTYPE_FP32,
-                   fp32_compute=False) -> int:
+                   fp32_compute=False, path="auto") -> int:
     d = make_desc(batch, seqlen, num_seqs, num_heads, io_dtype, state_dtype, HEAD_DIM ** -0.5,
-                  FLAG_FP32_COMPUTE if fp32_compute else 0)
+                  _flags(fp32_compute, path))
     return int(load_library().kda_fwd_workspace_size(ctypes.byref(d)))
 
 
@@ -133,7 +147,7 @@ class Call:
 
 def fwd(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | None = None,
         initial_state=None, output_final_state: bool = True, cu_seqlens=None, out=None, final_state=None,
-        workspace=None, fp32_compute: bool = False, stream=None):
+        workspace=None, fp32_compute: bool = False, path: str = "auto", stream=None):
     """KDA forward through kda_fwd. Returns (out, final_state or None).
 
     All tensors must be contiguous and on the same GPU. `stream` is a
@@ -142,14 +156,16 @@ def fwd(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | N
     """
     c = prepare_call(q, k, v, g_raw, beta_raw, lower_bound=lower_bound, scale=scale, initial_state=initial_state,
                      output_final_state=output_final_state, cu_seqlens=cu_seqlens, out=out,
-                     final_state=final_state, workspace=workspace, fp32_compute=fp32_compute, stream=stream)
+                     final_state=final_state, workspace=workspace, fp32_compute=fp32_compute, path=path,
+                     stream=stream)
     c.run()
     return c.out, c.final_state
 
 
 def prepare_call(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | None = None,
                  initial_state=None, output_final_state: bool = True, cu_seqlens=None, out=None,
-                 final_state=None, workspace=None, fp32_compute: bool = False, stream=None) -> Call:
+                 final_state=None, workspace=None, fp32_compute: bool = False, path: str = "auto",
+                 stream=None) -> Call:
     """Check and marshal fwd's arguments once (allocating out, final_state and
     the workspace when not given) without launching anything."""
     import torch
@@ -194,7 +210,7 @@ def prepare_call(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: 
                                   device=q.device)
     if scale is None:
         scale = D ** -0.5
-    flags = FLAG_FP32_COMPUTE if fp32_compute else 0
+    flags = _flags(fp32_compute, path)
     desc = make_desc(B, seqlen, N, H, io, st_code, scale, flags, head_dim=D)
     need = int(lib.kda_fwd_workspace_size(ctypes.byref(desc)))
     if workspace is None:

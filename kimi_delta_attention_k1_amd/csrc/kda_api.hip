@@ -12,7 +12,7 @@ namespace {
 using kda::Problem;
 using kda::WsLayout;
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
@@ -27,19 +27,31 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 struct Shape {
     int64_t T_tot, n_c_max;
-    bool f32_path;
+    bool f32_path, fused;
 };
+
+// Which kernels kda_fwd runs (the rule is stated with KDA_FUSED_MIN_PAIRS).
+bool pick_fused(const kda_desc_t *d, bool f32_path)
+{
+    if (f32_path || (d->flags & KDA_FLAG_SPLIT)) return false;
+    if (d->flags & KDA_FLAG_FUSED) return true;
+    return d->num_seqs * (int64_t)d->num_heads >= KDA_FUSED_MIN_PAIRS;
+}
 
 // Shape-level checks shared by the size query and the forward call.
 kda_status_t check_desc(const kda_desc_t *d, bool varlen, Shape *out)
 {
     if (!d) return KDA_ERR_NULL_ARG;
-    if (d->head_dim != KDA_HEAD_DIM || d->num_heads < 1 || d->batch < 1 || d->seqlen < 0 || d->num_seqs < 1)
+    if (d->head_dim != KDA_HEAD_DIM || d->num_heads < 1 || d->num_heads > 65535 || d->batch < 1 ||
+        d->seqlen < 0 || d->num_seqs < 1)
         return KDA_ERR_BAD_SHAPE;
     if ((d->io_dtype != KDA_DTYPE_BF16 && d->io_dtype != KDA_DTYPE_FP32) ||
         (d->state_dtype != KDA_DTYPE_BF16 && d->state_dtype != KDA_DTYPE_FP32))
         return KDA_ERR_BAD_DTYPE;
-    if (d->flags & ~(uint32_t)KDA_FLAG_FP32_COMPUTE) return KDA_ERR_BAD_ARG;
+    const uint32_t known = KDA_FLAG_FP32_COMPUTE | KDA_FLAG_SPLIT | KDA_FLAG_FUSED;
+    if (d->flags & ~known) return KDA_ERR_BAD_ARG;
+    const bool f32_path = d->io_dtype == KDA_DTYPE_FP32 || (d->flags & KDA_FLAG_FP32_COMPUTE);
+    if ((d->flags & KDA_FLAG_FUSED) && (f32_path || (d->flags & KDA_FLAG_SPLIT))) return KDA_ERR_BAD_ARG;
     int64_t T_tot, n_c_max;
     const int64_t lim = (int64_t)1 << 30;  // tokens and sequences addressed with int32 on the device
     if (varlen) {
@@ -54,9 +66,11 @@ kda_status_t check_desc(const kda_desc_t *d, bool varlen, Shape *out)
         n_c_max = d->batch * ((d->seqlen + KDA_CHUNK - 1) / KDA_CHUNK);
     }
     if (n_c_max * (int64_t)d->num_heads >= ((int64_t)1 << 31)) return KDA_ERR_BAD_SHAPE;
+    if (d->num_seqs * (int64_t)d->num_heads >= ((int64_t)1 << 31)) return KDA_ERR_BAD_SHAPE;
     out->T_tot = T_tot;
     out->n_c_max = n_c_max;
-    out->f32_path = d->io_dtype == KDA_DTYPE_FP32 || (d->flags & KDA_FLAG_FP32_COMPUTE);
+    out->f32_path = f32_path;
+    out->fused = pick_fused(d, f32_path);
     return KDA_OK;
 }
 
@@ -70,7 +84,10 @@ extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc)
     for (int varlen = 0; varlen < 2; ++varlen) {
         Shape s;
         if (check_desc(desc, varlen != 0, &s) != KDA_OK) continue;
-        size_t b = kda::ws_layout(desc->num_seqs, desc->num_heads, s.n_c_max, s.f32_path).total;
+        // the single pass needs no units, but without KDA_FLAG_FUSED the same
+        // description is also valid for the two-stage entry points
+        const bool units = !(desc->flags & KDA_FLAG_FUSED);
+        size_t b = kda::ws_layout(desc->num_seqs, desc->num_heads, units ? s.n_c_max : 0, s.f32_path).total;
         if (b > best) best = b;
     }
     return best;
@@ -89,6 +106,8 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     const bool varlen = cu_seqlens != nullptr;
     kda_status_t st = check_desc(desc, varlen, &s);
     if (st != KDA_OK) return st;
+    if (stages != (kPrepare | kRecur) && (desc->flags & KDA_FLAG_FUSED)) return KDA_ERR_BAD_ARG;
+    const bool fused = stages == (kPrepare | kRecur) && s.fused;
     if (!isfinite(lower_bound) || lower_bound < KDA_LOWER_BOUND_MIN || lower_bound > KDA_LOWER_BOUND_MAX)
         return KDA_ERR_BAD_ARG;
     if (!isfinite(desc->scale) || !(desc->scale > 0.f)) return KDA_ERR_BAD_ARG;
@@ -102,7 +121,7 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
 
     if (s.T_tot > 0 && (!q || !k || !v || !g_raw || !beta_raw || !out)) return KDA_ERR_NULL_ARG;
     if (!workspace) return KDA_ERR_WORKSPACE;
-    const WsLayout lay = kda::ws_layout(N, H, s.n_c_max, s.f32_path);
+    const WsLayout lay = kda::ws_layout(N, H, fused ? 0 : s.n_c_max, s.f32_path);
     if (workspace_bytes < lay.total || !aligned(workspace, KDA_WORKSPACE_ALIGN)) return KDA_ERR_WORKSPACE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g_raw, 16) || !aligned(out, 16) ||
         !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(beta_raw, esz))
@@ -136,6 +155,11 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     p.lay = lay;
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (fused) {
+        if (kda::launch_chunk_map(p, hs) != hipSuccess || kda::launch_fused(p, hs) != hipSuccess)
+            return KDA_ERR_HIP;
+        return KDA_OK;
+    }
     if (stages & kPrepare) {
         if (kda::launch_chunk_map(p, hs) != hipSuccess) return KDA_ERR_HIP;
         if ((p.f32_path ? kda::launch_prep_ref(p, hs) : kda::launch_prep_mfma(p, hs)) != hipSuccess)
@@ -167,10 +191,10 @@ extern "C" const char *kda_status_str(kda_status_t status)
     switch (status) {
     case KDA_OK: return "ok";
     case KDA_ERR_NULL_ARG: return "a required pointer is NULL";
-    case KDA_ERR_BAD_SHAPE: return "bad shape (head_dim must be 128; H, B, N >= 1; T >= 0; sizes in range)";
+    case KDA_ERR_BAD_SHAPE: return "bad shape (head_dim must be 128; 1 <= H <= 65535; B, N >= 1; T >= 0; sizes in range)";
     case KDA_ERR_BAD_DTYPE: return "unknown dtype code";
     case KDA_ERR_BAD_SEQLENS: return "cu_seqlens requires batch == 1";
-    case KDA_ERR_BAD_ARG: return "bad argument (lower_bound, scale, flags, or overlapping buffers)";
+    case KDA_ERR_BAD_ARG: return "bad argument (lower_bound, scale, unknown or conflicting flags, or overlapping buffers)";
     case KDA_ERR_WORKSPACE: return "workspace missing, too small or not 128-byte aligned";
     case KDA_ERR_MISALIGNED: return "a tensor base address is not 16-byte aligned";
     case KDA_ERR_HIP: return "HIP kernel launch failed";

@@ -1,0 +1,441 @@
+// kda_fused.hip -- single-pass bf16 KDA forward for gfx950: one workgroup per
+// (sequence, head) builds each chunk's operands in LDS and runs the recurrence
+// on them, so the only HBM traffic is the inputs, the outputs and the states.
+//
+// Same mathematics as the two-kernel path (Doubleword page "You Could Have
+// Come Up with Kimi Delta Attention", section 6; see kda_mfma.hip): per chunk
+// G (in-chunk prefix sums of the log-decay, 6.6), rho and chi (6.3, 6.5),
+// A^kk = (I + R)^-1, then E = A^kk Diag(beta)(V - K_b S^T), O = Q_b S^T + A^qk E
+// and S^T <- Diag(gamma) S^T + K_end^T E (6.4).
+//
+// Workgroup: 4 consumer waves (the recurrence; wave w owns value channels
+// [32w, 32w+32) as two 16-wide column tiles, so every operand read from LDS
+// serves two tiles), 4 stage-A waves (wave m owns key channels [32m, 32m+32))
+// and 2 stage-B waves; waves w, w+4 (and w+8) share a SIMD. Time advances in ticks separated by one workgroup barrier;
+// chunk c is handled at
+//   tick c    : stage A -- gate, prefix sums, decays, partial 16x16 products
+//               over the wave's 32 channels, K_b / Q_b / K_end / gamma / v into
+//               prepared slot c % 3
+//   tick c+1  : stage B -- sum the four partials; one wave forms R, the
+//               inverse and (A^kk Diag(beta))^T, the other (A^qk)^T and the
+//               per-token scales, into slot c % 3
+//   tick c+2  : consumers run the recurrence step on slot c % 3.
+// Each stage-A wave streams its 32-channel slices of q, k, g_raw, v and
+// beta_raw with global-to-LDS loads kFIn chunks ahead and waits on exact counts
+// of its own loads.
+//
+// L2 normalisation is deferred: stage A works on raw q, k; stage B forms the
+// per-token scales rk = 1/|k|, rq = s/|q| (the read scale s folded in) from the
+// summed partial norms and folds them into R, (A^kk Diag(beta))^T and
+// (A^qk)^T; the consumers scale K_b S^T by rk and Q_b S^T by rq per row. The recurrence then runs on
+// E' = Diag(rk) E, which is exactly what the state update needs with the raw
+// K_end (K_end^T E = K_end_raw^T E'), and A^qk / Diag(rk) applied to E' gives
+// the same outputs.
+#include "kda_mfma_common.h"
+
+namespace kda {
+
+constexpr int kFCons = 4;                             // consumer waves (32 value channels each)
+constexpr int kFPrep = 4;                             // stage-A waves
+constexpr int kFSolve = 2;                            // stage-B waves
+constexpr int kFThreads = 64 * (kFCons + kFPrep + kFSolve);  // 640
+constexpr int kFIn = 4;                               // input chunks in flight per prep wave
+constexpr int kFSlots = 3;                            // prepared-chunk slots
+constexpr int kFDma = 5;                              // global-to-LDS loads per chunk per prep wave
+constexpr int kFPending = (kFIn - 1) * kFDma;         // loads allowed in flight at a stage-A start
+static_assert(kFPending <= 63, "vmcnt holds at most 63 outstanding loads");
+
+// prepared slot
+constexpr int kPKB = 0, kPQB = 4096, kPKE = 8192, kPAB = 12288, kPAQ = 13312, kPGM = 14336;
+constexpr int kPSC = 14848;  // rk[16], s*rq[16]
+constexpr int kPV = 14976;   // v tile [16][128] bf16, rows kVRow bytes apart
+constexpr int kVRow = 272;   // 256 + 16: row r starts 4 r banks further, so row-wise
+                             // 16-byte writes and column-wise reads spread over the banks
+constexpr int kPBytes = kPV + kC * kVRow;
+// per-prep-wave input slot: q, k, g_raw, v as [16 rows][32 channels] bf16, then
+// beta_raw as one aligned dword per lane (the token's element in its low or high half)
+constexpr int kIQ = 0, kIK = 1024, kIG = 2048, kIV = 3072, kIB = 4096, kIBytes = 4352;
+// partial-product buffer (two, alternating by chunk parity)
+constexpr int kXR = 0, kXRT = 1024, kXAQ = 2048, kXNQ = 3072, kXNK = 3136, kXWave = 3200;
+constexpr int kXBeta = kFPrep * kXWave;
+constexpr int kXBytes = kXBeta + 64;
+constexpr int kFLds = kFSlots * kPBytes + kFPrep * kFIn * kIBytes + 2 * kXBytes;
+static_assert(kFLds <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+static_assert(kPBytes % 128 == 0 && kIBytes % 64 == 0 && kXBytes % 64 == 0, "16-byte aligned LDS blocks");
+
+// 16-byte slot of lane L in a 1 KB operand block: L with its low three bits XORed with
+// bits 3-5. The consumers' 16-byte reads still cover all banks in every group of eight
+// lanes, and stage A's scattered 2- and 8-byte writes spread over the banks.
+__device__ __forceinline__ int swz(int L) { return L ^ ((L >> 3) & 7); }
+
+// barrier that first completes this wave's own LDS traffic (not its global loads)
+__device__ __forceinline__ void tick_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <typename TSt>
+__global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                      const uint16_t *__restrict__ v,
+                                                      const uint16_t *__restrict__ graw,
+                                                      const uint16_t *__restrict__ braw, const TSt *s0, TSt *s1,
+                                                      uint16_t *__restrict__ out,
+                                                      const int32_t *__restrict__ tok_off,
+                                                      const int32_t *__restrict__ chunk_off, int H, float lb,
+                                                      float scale)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[kFLds];
+    char *const slots = lds;
+    char *const inring = lds + kFSlots * kPBytes;
+    char *const parts = inring + kFPrep * kFIn * kIBytes;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n = blockIdx.x / H, h = blockIdx.x % H;
+    const int c0 = chunk_off[n], nch = chunk_off[n + 1] - c0;
+    const int tb = tok_off[n], te = tok_off[n + 1];
+    const int ticks = nch > 0 ? nch + 2 : 0;
+
+    if (w >= kFCons + kFPrep) {
+        // ================================================================ stage-B waves
+        if (nch == 0) return;  // uniform over the workgroup: no barrier is entered
+        const int role = w - kFCons - kFPrep;
+#pragma unroll 1
+        for (int tau = 0; tau < ticks; ++tau) {
+            if (tau >= 1 && tau - 1 < nch) {
+                const int c = tau - 1;
+                const char *X = parts + (c & 1) * kXBytes;
+                char *P = slots + (c % kFSlots) * kPBytes;
+                const int tok = lane & 15, g = lane >> 4;  // D layout: rows 4g+r, column tok
+                // sum of the four waves' partials of one lane-ordered block / one token vector
+                auto sum4 = [&](int off) {
+                    f32x4 a = reinterpret_cast<const f32x4 *>(X + off)[lane];
+#pragma unroll
+                    for (int mm = 1; mm < kFPrep; ++mm) a += reinterpret_cast<const f32x4 *>(X + mm * kXWave + off)[lane];
+                    return a;
+                };
+                auto tok_sum = [&](int off, int i) {
+                    float a = reinterpret_cast<const float *>(X + off)[i];
+#pragma unroll
+                    for (int mm = 1; mm < kFPrep; ++mm) a += reinterpret_cast<const float *>(X + mm * kXWave + off)[i];
+                    return a;
+                };
+                if (role == 0) {
+                    const f32x4 Rs = sum4(kXR), RTs = sum4(kXRT);
+                    const f32x4 beta_a = *reinterpret_cast<const f32x4 *>(X + kXBeta + 16 * g);
+                    const float beta_b = reinterpret_cast<const float *>(X + kXBeta)[tok];
+                    const float rkb = __builtin_amdgcn_rsqf(tok_sum(kXNK, tok) + kL2Eps);
+                    f32x4 R, RT;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int a = 4 * g + r;
+                        const float rka = __builtin_amdgcn_rsqf(tok_sum(kXNK, a) + kL2Eps);
+                        R[r] = (tok < a) ? beta_a[r] * rka * rkb * Rs[r] : 0.f;
+                        RT[r] = (a < tok) ? beta_b * rkb * rka * RTs[r] : 0.f;
+                    }
+                    // (A^kk)^T = (I + R^T)^-1 = (I-M)(I+M^2)(I+M^4)(I+M^8), M = R^T
+                    const f32x4 M2 = mm16_f32(R, RT);
+                    const f32x4 M2T = mm16_f32(RT, R);
+                    const f32x4 M4 = mm16_f32(M2T, M2);
+                    const f32x4 M4T = mm16_f32(M2, M2T);
+                    const f32x4 M8T = mm16_f32(M4, M4T);
+                    const f32x4 P1 = mm16_f32(eye_plus(R, -1.f, g, tok), eye_plus(M2, 1.f, g, tok));
+                    const f32x4 P2 = mm16_f32(eye_plus(M4T, 1.f, g, tok), P1);
+                    const f32x4 AT = mm16_f32(eye_plus(M8T, 1.f, g, tok), P2);
+                    f32x4 ABT;  // rk_b beta_a A^kk[b][a]: E' = Diag(rk) A^kk Diag(beta) Ebar
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ABT[r] = rkb * beta_a[r] * AT[r];
+                    reinterpret_cast<bf16x8 *>(P + kPAB)[lane] = split8(ABT);
+                } else {
+                    const f32x4 AQs = sum4(kXAQ);
+                    const float rqb = scale * __builtin_amdgcn_rsqf(tok_sum(kXNQ, tok) + kL2Eps);
+                    f32x4 AQT;  // chi_{b,a} / rk_a = s rq_b (q_b . k_a decayed), a <= b
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) AQT[r] = (4 * g + r <= tok) ? rqb * AQs[r] : 0.f;
+                    reinterpret_cast<bf16x8 *>(P + kPAQ)[lane] = split8(AQT);
+                    if (lane < 32) {  // rk (lanes 0-15) and s rq (lanes 16-31)
+                        const float nn = tok_sum(lane < 16 ? kXNK : kXNQ, tok);
+                        reinterpret_cast<float *>(P + kPSC)[lane] =
+                            (lane < 16 ? 1.f : scale) * __builtin_amdgcn_rsqf(nn + kL2Eps);
+                    }
+                }
+            }
+            tick_sync();
+        }
+        return;
+    }
+    if (w >= kFCons) {
+        // ================================================================ stage-A waves
+        if (nch == 0) return;  // uniform over the workgroup: no barrier is entered
+        const int m = w - kFCons;
+        const int t = lane & 15, sg = lane >> 4;  // token; channel subgroup of 8
+        char *const myin = inring + m * kFIn * kIBytes;
+        const char *const qb8 = reinterpret_cast<const char *>(q);
+        const char *const kb8 = reinterpret_cast<const char *>(k);
+        const char *const gb8 = reinterpret_cast<const char *>(graw);
+        const char *const vb8 = reinterpret_cast<const char *>(v);
+        const char *const bb8 = reinterpret_cast<const char *>(braw);
+
+        // this wave's 32-channel slices of chunk c into input slot `slot`
+        auto dma_chunk = [&](int c, int slot) {
+            c = min(c, nch - 1);  // past the end: re-read the last chunk (never consumed)
+            const int row = min(tb + c * kC + (lane >> 2), te - 1);
+            const int64_t off = (((int64_t)row * H + h) * kD + 32 * m) * 2 + (lane & 3) * 16;
+            char *dst = myin + slot * kIBytes;
+            __builtin_amdgcn_global_load_lds(qb8 + off, (lds_void *)(dst + kIQ), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(kb8 + off, (lds_void *)(dst + kIK), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gb8 + off, (lds_void *)(dst + kIG), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vb8 + off, (lds_void *)(dst + kIV), 16, 0, 0);
+            // the dword holding beta_raw[brow][h]: rounding the address down to 4 bytes
+            // stays inside the 4-byte word, hence inside the page, that holds the element
+            const int brow = min(tb + c * kC + (lane & 15), te - 1);
+            const uintptr_t ba = reinterpret_cast<uintptr_t>(bb8 + ((int64_t)brow * H + h) * 2);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(ba & ~(uintptr_t)3),
+                                             (lds_void *)(dst + kIB), 4, 0, 0);
+        };
+#pragma unroll
+        for (int i = 0; i < kFIn; ++i) dma_chunk(i, i);
+
+        const float lb2 = lb * kLog2e;
+#pragma unroll 1
+        for (int tau = 0; tau < ticks; ++tau) {
+            if (tau < nch) {
+                // ------------------------------------------------ stage A, chunk c = tau
+                const int c = tau;
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kFPending) : "memory");  // chunk c landed
+                const char *I = myin + (c % kFIn) * kIBytes;
+                const int t0 = tb + c * kC, len = min(kC, te - t0);
+                // rows past the end of the sequence hold copies of its last row; zero
+                // gate and beta make them absent: they reach only the masked triangles
+                // of R and A^qk, rows of E' that come out exactly zero, and output rows
+                // that are never stored
+                const bool valid = t < len;
+                const u32x4 qa = *reinterpret_cast<const u32x4 *>(I + kIQ + t * 64 + sg * 16);
+                const u32x4 ka = *reinterpret_cast<const u32x4 *>(I + kIK + t * 64 + sg * 16);
+                const u32x4 ga = *reinterpret_cast<const u32x4 *>(I + kIG + t * 64 + sg * 16);
+                const u32x4 va = *reinterpret_cast<const u32x4 *>(I + kIV + t * 64 + sg * 16);
+                const uint32_t bw = *reinterpret_cast<const uint32_t *>(I + kIB + t * 4);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // input slot read: refill it
+                dma_chunk(c + kFIn, c % kFIn);
+
+                const int brow = min(t0 + t, te - 1);
+                const bool bhi = (reinterpret_cast<uintptr_t>(bb8 + ((int64_t)brow * H + h) * 2) & 2) != 0;
+                const float vmask = valid ? 1.f : 0.f;
+                float qf[8], kf[8], gf[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    qf[2 * e] = bf_lo(qa[e]);
+                    qf[2 * e + 1] = bf_hi(qa[e]);
+                    kf[2 * e] = bf_lo(ka[e]);
+                    kf[2 * e + 1] = bf_hi(ka[e]);
+                    gf[2 * e] = bf_lo(ga[e]);
+                    gf[2 * e + 1] = bf_hi(ga[e]);
+                }
+                const float beta = vmask * sigmoid_fast(bhi ? bf_hi(bw) : bf_lo(bw));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {  // gate (log2 units) and prefix sum over tokens
+                    float x = vmask * lb2 * sigmoid_fast(gf[i]);
+                    x += row_shr<1>(x);
+                    x += row_shr<2>(x);
+                    x += row_shr<4>(x);
+                    x += row_shr<8>(x);
+                    gf[i] = x;
+                }
+                float nq = 0.f, nk = 0.f;  // partial squared norms over this wave's 32 channels
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    nq += qf[i] * qf[i];
+                    nk += kf[i] * kf[i];
+                }
+                nq += __shfl_xor(nq, 16);
+                nq += __shfl_xor(nq, 32);
+                nk += __shfl_xor(nk, 16);
+                nk += __shfl_xor(nk, 32);
+
+                char *X = parts + (c & 1) * kXBytes;
+                char *P = slots + (c % kFSlots) * kPBytes;
+                if (sg == 0) {
+                    reinterpret_cast<float *>(X + m * kXWave + kXNQ)[t] = nq;
+                    reinterpret_cast<float *>(X + m * kXWave + kXNK)[t] = nk;
+                    if (m == 0) reinterpret_cast<float *>(X + kXBeta)[t] = beta;
+                }
+                // decays relative to token 7 (each factor within e^{8|lb|}); K_end via token 15
+                bf16x8 kr_h, ki_h, ki_l, qr_h, qr_l;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float gref = row_bcast<7>(gf[i]);
+                    const float up = __builtin_amdgcn_exp2f(gf[i] - gref);
+                    const float dn = __builtin_amdgcn_exp2f(gref - gf[i]);
+                    const float cl = row_bcast<15>(up);  // e^{G_last - Gref}
+                    const float kr = kf[i] * up, ki = kf[i] * dn, qr = qf[i] * up;
+                    kr_h[i] = (__bf16)kr;
+                    ki_h[i] = (__bf16)ki;
+                    ki_l[i] = (__bf16)(ki - (float)ki_h[i]);
+                    qr_h[i] = (__bf16)qr;
+                    qr_l[i] = (__bf16)(qr - (float)qr_h[i]);
+                    // raw K_end = k e^{G_last - G}: consumer fragment (tile pair m), lane
+                    // (kc + 16 (t/4)), element (t%4) + 4 hi, channel 32m + 16 hi + kc
+                    const int cr = 8 * sg + i, kc = cr & 15, hi = cr >> 4;
+                    *reinterpret_cast<__bf16 *>(P + kPKE + m * 1024 + swz(kc + 16 * (t >> 2)) * 16 +
+                                                ((t & 3) + 4 * hi) * 2) = (__bf16)(ki * cl);
+                }
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 dR = mma32(kr_h, ki_h, z);
+                const f32x4 dRT = mma32(ki_h, kr_h, z);
+                f32x4 dAQT = mma32(ki_h, qr_h, z);
+                dAQT = mma32(ki_l, qr_h, dAQT);
+                dAQT = mma32(ki_h, qr_l, dAQT);
+                reinterpret_cast<f32x4 *>(X + m * kXWave + kXR)[lane] = dR;
+                reinterpret_cast<f32x4 *>(X + m * kXWave + kXRT)[lane] = dRT;
+                reinterpret_cast<f32x4 *>(X + m * kXWave + kXAQ)[lane] = dAQT;
+
+                // raw K_b = k e^{G}, Q_b = q e^{G} in the consumer's 16x16x32 A order
+                // (k step m); gamma = e^{G_last} from token 15; the v tile
+                bf16x4 kb4[2], qb4[2];
+                float dec[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    dec[i] = __builtin_amdgcn_exp2f(gf[i]);
+                    kb4[i >> 2][i & 3] = (__bf16)(kf[i] * dec[i]);
+                    qb4[i >> 2][i & 3] = (__bf16)(qf[i] * dec[i]);
+                }
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int q4 = 2 * sg + hf;                 // which 4 channels of the 32
+                    const int gd = q4 & 3, e0 = (q4 >> 2) * 4;  // consumer lane group, element
+                    const int o = m * 1024 + swz(t + 16 * gd) * 16 + e0 * 2;
+                    *reinterpret_cast<bf16x4 *>(P + kPKB + o) = kb4[hf];
+                    *reinterpret_cast<bf16x4 *>(P + kPQB + o) = qb4[hf];
+                }
+                if (t == 15) {
+                    float *gm = reinterpret_cast<float *>(P + kPGM) + 32 * m + 8 * sg;
+                    *reinterpret_cast<f32x4 *>(gm) = f32x4{dec[0], dec[1], dec[2], dec[3]};
+                    *reinterpret_cast<f32x4 *>(gm + 4) = f32x4{dec[4], dec[5], dec[6], dec[7]};
+                }
+                *reinterpret_cast<u32x4 *>(P + kPV + t * kVRow + (32 * m + 8 * sg) * 2) =
+                    valid ? va : u32x4{0u, 0u, 0u, 0u};
+            }
+            tick_sync();
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // nothing still landing in LDS at exit
+        return;
+    }
+
+    // ==================================================================== consumers
+    // Lane (col, g) of consumer wave w holds, for column tile u, rows 4g..4g+3 of
+    // the 16x16 state tiles st[u][t] = S^T[16t .., 32w + 16u + col] (D layout).
+    const int g = lane >> 4, col = lane & 15, sl = swz(lane);
+    const int64_t sbase = (((int64_t)n * H + h) * kD + 32 * w + col) * kD + 4 * g;
+    f32x4 st[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) st[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s0 != nullptr) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) st[u][t] = ld_state4(s0 + sbase + (int64_t)16 * kD * u + 16 * t);
+    }
+#pragma unroll 1
+    for (int tau = 0; tau < ticks; ++tau) {
+        if (tau >= 2) {
+            const int c = tau - 2;
+            const char *L = slots + (c % kFSlots) * kPBytes;
+            const int t0 = tb + c * kC, len = min(kC, te - t0);
+            // K_b S^T and Q_b S^T for both column tiles (bf16 state operand)
+            f32x4 xk[2], xq[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) xk[u] = xq[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const bf16x8 kb = *reinterpret_cast<const bf16x8 *>(L + kPKB + p * 1024 + sl * 16);
+                const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(L + kPQB + p * 1024 + sl * 16);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    bf16x8 sb;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        sb[r] = (__bf16)st[u][2 * p][r];
+                        sb[4 + r] = (__bf16)st[u][2 * p + 1][r];
+                    }
+                    xk[u] = mma32(kb, sb, xk[u]);
+                    xq[u] = mma32(qb, sb, xq[u]);
+                }
+            }
+            const f32x4 rk4 = *reinterpret_cast<const f32x4 *>(L + kPSC + 16 * g);
+            const f32x4 rq4 = *reinterpret_cast<const f32x4 *>(L + kPSC + 64 + 16 * g);
+            const bf16x8 ab = *reinterpret_cast<const bf16x8 *>(L + kPAB + lane * 16);
+            const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(L + kPAQ + lane * 16);
+            const bf16x4 ab_h = {ab[0], ab[1], ab[2], ab[3]};
+            const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]};
+            bf16x8 e_hl[2];
+            const int64_t rstride = (int64_t)H * kD;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int vcol = 32 * w + 16 * u + col;
+                f32x4 eb;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint16_t vr =
+                        *reinterpret_cast<const uint16_t *>(L + kPV + (4 * g + r) * kVRow + vcol * 2);
+                    eb[r] = bf16_bits_to_f32(vr) - rk4[r] * xk[u][r];  // rows past the end hold zeros
+                    xq[u][r] *= rq4[r];
+                }
+                bf16x4 eb_h, eb_l, e_h, e_l;
+                split4(eb, eb_h, eb_l);
+                f32x4 E = {0.f, 0.f, 0.f, 0.f};  // E' = Diag(rk) E
+                E = mma32(ab, cat8(eb_h, eb_h), E);
+                E = mma16(ab_h, eb_l, E);
+                split4(E, e_h, e_l);
+                e_hl[u] = cat8(e_h, e_l);
+                f32x4 O = mma32(aq, cat8(e_h, e_h), xq[u]);
+                O = mma16(aq_h, e_l, O);
+                uint16_t *orow = out + ((int64_t)(t0 + 4 * g) * H + h) * kD + vcol;
+                if (len == kC) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) orow[r * rstride] = __builtin_bit_cast(uint16_t, (__bf16)O[r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * g + r < len) orow[r * rstride] = __builtin_bit_cast(uint16_t, (__bf16)O[r]);
+                }
+            }
+            // S^T <- Diag(gamma) S^T + K_end^T E'
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const u32x4 kq = *reinterpret_cast<const u32x4 *>(L + kPKE + p * 1024 + sl * 16);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int t = 2 * p + hh;
+                    const bf16x4 kt = __builtin_bit_cast(bf16x4, hh ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]});
+                    const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kPGM + (16 * t + 4 * g) * 4);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) st[u][t] = mma32(cat8(kt, kt), e_hl[u], st[u][t] * gm);
+                }
+            }
+        }
+        tick_sync();
+    }
+    if (s1) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) st_state4(s1 + sbase + (int64_t)16 * kD * u + 16 * t, st[u][t]);
+    }
+}
+
+template <typename TSt>
+static hipError_t launch_fused_t(const Problem &p, hipStream_t s)
+{
+    const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
+    const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
+    hipLaunchKernelGGL((kf_fused<TSt>), dim3((unsigned)(p.N * p.H)), dim3(kFThreads), 0, s, (const uint16_t *)p.q,
+                       (const uint16_t *)p.k, (const uint16_t *)p.v, (const uint16_t *)p.g,
+                       (const uint16_t *)p.beta, (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H,
+                       p.lb, p.scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused(const Problem &p, hipStream_t s)
+{
+    return p.st_bf16 ? launch_fused_t<uint16_t>(p, s) : launch_fused_t<float>(p, s);
+}
+
+}  // namespace kda

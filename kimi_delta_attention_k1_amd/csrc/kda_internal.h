@@ -82,6 +82,7 @@ hipError_t launch_prep_ref(const Problem &p, hipStream_t s);    // fp32 K1
 hipError_t launch_recur_ref(const Problem &p, hipStream_t s);   // fp32 K2
 hipError_t launch_prep_mfma(const Problem &p, hipStream_t s);   // bf16 K1
 hipError_t launch_recur_mfma(const Problem &p, hipStream_t s);  // bf16 K2
+hipError_t launch_fused(const Problem &p, hipStream_t s);       // bf16 single pass
 
 // ---------------------------------------------------------------------------
 // Device helpers

@@ -26,94 +26,9 @@
 // contraction order inside a 32-wide k step is a free permutation, which K1
 // uses to write K_b and Q_b so that the state accumulators of two 16-row tiles
 // form one 16x16x32 B operand without data movement.
-#include "kda_internal.h"
+#include "kda_mfma_common.h"
 
 namespace kda {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
-                                                      0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-
-// x = hi + lo with hi, lo bf16: about 16 significant bits between them.
-__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo)
-{
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        __bf16 h = (__bf16)x[r];
-        hi[r] = h;
-        lo[r] = (__bf16)(x[r] - (float)h);
-    }
-}
-
-// {hi[0..3], lo[0..3]} with x = hi + lo: one 16x16x32 A operand that carries
-// both halves of a split 16x16 tile (its first half alone is the hi tile)
-__device__ __forceinline__ bf16x8 split8(f32x4 x)
-{
-    bf16x4 h, l;
-    split4(x, h, l);
-    return bf16x8{h[0], h[1], h[2], h[3], l[0], l[1], l[2], l[3]};
-}
-
-__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b)
-{
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// logistic sigmoid from 2^x and a reciprocal
-__device__ __forceinline__ float sigmoid_fast(float x)
-{
-    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
-}
-
-// value of lane n of the caller's 16-lane row (DPP row_newbcast: no LDS round trip)
-template <int N> __device__ __forceinline__ float row_bcast(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, false));
-}
-
-// value of lane (l - n) of the same 16-lane row, 0 for lanes below n
-template <int N> __device__ __forceinline__ float row_shr(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
-}
-
-// C = X Y for 16x16 fp32 tiles; xt holds X^T and y holds Y, both in D layout.
-__device__ __forceinline__ f32x4 mm16_f32(f32x4 xt, f32x4 y)
-{
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mma4(xt[s], y[s], acc);
-    return acc;
-}
-
-// I + a*X in D layout (row 4g+r, column tok)
-__device__ __forceinline__ f32x4 eye_plus(f32x4 x, float a, int g, int tok)
-{
-    f32x4 y;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) y[r] = a * x[r] + ((4 * g + r == tok) ? 1.f : 0.f);
-    return y;
-}
 
 // ---------------------------------------------------------------------------
 // K1: one wave per (chunk, head). Lane l holds token l%16 and key channels
@@ -319,36 +234,6 @@ template <int CONS> struct K2Shape {
     static_assert(pending <= 63, "vmcnt holds at most 63 outstanding loads");
     static_assert(kSlotKB % producers == 0, "producers split a slot evenly");
 };
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void bar_sync() { asm volatile("s_barrier" ::: "memory"); }
-
-template <typename TSt>
-__device__ __forceinline__ f32x4 ld_state4(const TSt *p);
-template <> __device__ __forceinline__ f32x4 ld_state4<float>(const float *p)
-{
-    return *reinterpret_cast<const f32x4 *>(p);
-}
-template <> __device__ __forceinline__ f32x4 ld_state4<uint16_t>(const uint16_t *p)
-{
-    const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
-    f32x4 y = {bf_lo(x[0]), bf_hi(x[0]), bf_lo(x[1]), bf_hi(x[1])};
-    return y;
-}
-template <typename TSt>
-__device__ __forceinline__ void st_state4(TSt *p, f32x4 x);
-template <> __device__ __forceinline__ void st_state4<float>(float *p, f32x4 x)
-{
-    *reinterpret_cast<f32x4 *>(p) = x;
-}
-template <> __device__ __forceinline__ void st_state4<uint16_t>(uint16_t *p, f32x4 x)
-{
-    u32x2 y;
-    y[0] = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
-    y[1] = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
-    *reinterpret_cast<u32x2 *>(p) = y;
-}
 
 template <typename TSt, int CONS>
 __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(

@@ -10,8 +10,7 @@ launch. Both counters are scaled by what they read for the plain device copy
 of known size that bench.py --copy-probe-mib runs in the same process
 (the runtime's copy kernel; its last dispatches are the probe). The result is
 merged into profiles/traffic_counters.json, keyed by workload and kernel, with
-the SHA-256 of the kernel source so bench.py reports null once the kernels
-change.
+the SHA-256 of the kernel's sources so bench.py reports null once they change.
 """
 from __future__ import annotations
 
@@ -23,9 +22,24 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic_counters.json")
-SRC = os.path.join(ROOT, "kimi_delta_attention_k1_amd", "csrc", "kda_mfma.hip")
-SHORT = {"k1_mfma": "kda::k1_mfma", "k2_mfma": "kda::k2_mfma", "k0_chunk_map": "kda::k0_chunk_map",
-         "copy": "__amd_rocclr_copyBuffer"}
+CSRC = os.path.join(ROOT, "kimi_delta_attention_k1_amd", "csrc")
+# the sources each kernel is compiled from (a change to any of them voids its counters)
+KERNEL_SOURCES = {
+    "k1_mfma": ("kda_mfma.hip", "kda_mfma_common.h", "kda_internal.h"),
+    "k2_mfma": ("kda_mfma.hip", "kda_mfma_common.h", "kda_internal.h"),
+    "kf_fused": ("kda_fused.hip", "kda_mfma_common.h", "kda_internal.h"),
+}
+SHORT = {"k1_mfma": "kda::k1_mfma", "k2_mfma": "kda::k2_mfma", "kf_fused": "kda::kf_fused",
+         "k0_chunk_map": "kda::k0_chunk_map", "copy": "__amd_rocclr_copyBuffer"}
+
+
+def src_hash(kernel: str) -> str:
+    """SHA-256 over the kernel's source files, in a fixed order."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def short_name(kernel_name: str) -> str:
@@ -58,18 +72,19 @@ def traffic(fetch_csv, write_csv, workload, probe_mib):
     # the probe copies are the last copy dispatches (three of them)
     ff = probe_kib / (sum(f["copy"][-3:]) / 3)
     fw = probe_kib / (sum(w["copy"][-3:]) / 3)
-    src = hashlib.sha256(open(SRC, "rb").read()).hexdigest()
     rec = {}
     if os.path.exists(TRAFFIC):
         rec = json.load(open(TRAFFIC))
     ent = rec.setdefault(workload, {})
-    for k in ("k1_mfma", "k2_mfma"):
+    for k in KERNEL_SOURCES:
+        if k not in f or k not in w:
+            continue
         fk = sum(f[k]) / len(f[k])
         wk = sum(w[k]) / len(w[k])
         ent[k] = {"fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
                   "fetch_scale": round(ff, 4), "write_scale": round(fw, 4),
                   "bytes_per_launch": int(round((fk * ff + wk * fw) * 1024)),
-                  "dispatches": len(f[k]), "src_sha256": src}
+                  "dispatches": len(f[k]), "src_sha256": src_hash(k)}
     os.makedirs(os.path.dirname(TRAFFIC), exist_ok=True)
     with open(TRAFFIC, "w") as fh:
         json.dump(rec, fh, indent=1, sort_keys=True)

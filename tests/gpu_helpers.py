@@ -26,9 +26,13 @@ def np64(t: torch.Tensor) -> np.ndarray:
 
 
 def run_gpu(w, dev, *, state_dtype=torch.float32, fp32_compute=False, workspace=None, final=True,
-            initial_state="from_workload", out=None, final_state=None):
-    """Run workload w on the GPU; returns (out [T_tot,H,128] tensor, final_state tensor or None)."""
+            initial_state="from_workload", out=None, final_state=None, path="auto", beta=None):
+    """Run workload w on the GPU; returns (out [T_tot,H,128] tensor, final_state tensor or None).
+    `path` selects the kernels ("auto", "split", "fused"); `beta` replaces the
+    device copy of beta_raw (same shape and values, e.g. at an odd address)."""
     q, k, v, g, b = (t.to(dev) for t in (w.q, w.k, w.v, w.g_raw, w.beta_raw))
+    if beta is not None:
+        b = beta
     s0 = w.initial_state if initial_state == "from_workload" else initial_state
     if s0 is not None:
         s0 = s0.to(dev, state_dtype)
@@ -36,14 +40,14 @@ def run_gpu(w, dev, *, state_dtype=torch.float32, fp32_compute=False, workspace=
         cu = w.cu_seqlens().to(dev)
         o, s = kda.fwd(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, output_final_state=final,
                        cu_seqlens=cu, fp32_compute=fp32_compute, workspace=workspace, out=out,
-                       final_state=final_state)
+                       final_state=final_state, path=path)
     else:
         B, T = w.N, w.seq_lens[0]
         shp = (B, T, w.H, 128)
         o, s = kda.fwd(q.view(shp), k.view(shp), v.view(shp), g.view(shp), b.view(B, T, w.H),
                        lower_bound=w.lower_bound, initial_state=s0, output_final_state=final,
                        fp32_compute=fp32_compute, workspace=workspace,
-                       out=None if out is None else out.view(shp), final_state=final_state)
+                       out=None if out is None else out.view(shp), final_state=final_state, path=path)
         o = o.view(B * T, w.H, 128)
     torch.cuda.synchronize(dev)
     return o, s

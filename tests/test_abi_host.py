@@ -39,7 +39,7 @@ def test_header_symbols_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() >= 100
+    assert lib.kda_version() >= 200
     for code in range(9):
         assert kda.status_str(code) and kda.status_str(code) != "unknown status"
     assert kda.status_str(99) == "unknown status"
@@ -133,7 +133,12 @@ def _desc(**kw):
     (dict(lb=float("nan")), BAD_ARG),
     (dict(desc=dict(scale=0.0)), BAD_ARG),
     (dict(desc=dict(scale=float("inf"))), BAD_ARG),
-    (dict(desc=dict(flags=2)), BAD_ARG),
+    (dict(desc=dict(flags=8)), BAD_ARG),                     # unknown flag bit
+    (dict(desc=dict(flags=kda.FLAG_SPLIT | kda.FLAG_FUSED)), BAD_ARG),
+    (dict(desc=dict(flags=kda.FLAG_FP32_COMPUTE | kda.FLAG_FUSED)), BAD_ARG),
+    (dict(desc=dict(io_dtype=1, flags=kda.FLAG_FUSED)), BAD_ARG),  # fp32 I/O has no single pass
+    (dict(desc=dict(num_heads=65536)), BAD_SHAPE),
+    (dict(desc=dict(flags=kda.FLAG_SPLIT), ws_bytes=1024), WORKSPACE),
     (dict(drop=("q",)), NULL_ARG),
     (dict(drop=("out",)), NULL_ARG),
     (dict(drop=("ws",)), WORKSPACE),
@@ -154,3 +159,23 @@ def test_validation_rejects_before_launch(lib, case, expect):
 
 def test_null_desc(lib):
     assert _call(lib, None) == NULL_ARG
+
+
+def test_path_flags_and_workspace(lib):
+    # the single pass needs only the chunk map; without its flag the size covers the split path
+    assert kda.workspace_size(1, 65536, 8, 32, path="fused") == _layout(8, 32, 0, 14848)
+    assert kda.workspace_size(1, 65536, 8, 32, path="split") == kda.workspace_size(1, 65536, 8, 32)
+    assert kda.workspace_size(1, 65536, 8, 32, path="auto") == _layout(8, 32, (65536 + 15 * 8) // 16, 14848)
+    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32, path="fused") == 0  # invalid: fp32 I/O
+    with pytest.raises(ValueError):
+        kda.workspace_size(1, 64, 1, 1, path="both")
+
+
+def test_stage_entry_points_reject_fused_flag(lib):
+    desc = _desc(flags=kda.FLAG_FUSED)
+    f = Fake(dict(x=1 << 20))
+    a = ctypes.c_void_p(f.addr["x"])
+    for fn in (lib.kda_fwd_prepare, lib.kda_fwd_recur):
+        rc = fn(a, a, a, a, a, None, None, a, None, ctypes.c_float(-5.0), ctypes.byref(desc), a,
+                ctypes.c_size_t(1 << 30), None)
+        assert rc == BAD_ARG, kda.status_str(rc)
