@@ -96,7 +96,7 @@ enum {
  * agree to bf16 rounding; they are not bitwise identical (the single pass
  * applies the L2 normalisation after its in-chunk products instead of
  * before). */
-#define KDA_FUSED_MIN_PAIRS 256
+#define KDA_FUSED_MIN_PAIRS 192
 
 /*
  * Problem description (host memory).

@@ -31,7 +31,7 @@ CHUNK = 16
 FLAG_FP32_COMPUTE = 1
 FLAG_SPLIT = 2
 FLAG_FUSED = 4
-FUSED_MIN_PAIRS = 256
+FUSED_MIN_PAIRS = 192
 _PATH_FLAGS = {"auto": 0, "split": FLAG_SPLIT, "fused": FLAG_FUSED}
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1

@@ -86,7 +86,9 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
     char *const inring = lds + kFSlots * kPBytes;
     char *const parts = inring + kFPrep * kFIn * kIBytes;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index is uniform over the wave: keep it scalar so role branches and
+    // the address arithmetic built on it stay in scalar registers
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = blockIdx.x / H, h = blockIdx.x % H;
     const int c0 = chunk_off[n], nch = chunk_off[n + 1] - c0;
     const int tb = tok_off[n], te = tok_off[n + 1];
@@ -191,6 +193,20 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
         };
 #pragma unroll
         for (int i = 0; i < kFIn; ++i) dma_chunk(i, i);
+        // The inputs of chunk c are read from LDS into registers at the end of tick
+        // c - 1 (chunk 0: here), so their LDS latency overlaps the other waves' work.
+        u32x4 qa, ka, ga, va;
+        uint32_t bw;
+        auto read_inputs = [&](int c) {
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kFPending) : "memory");  // chunk c landed
+            const char *I = myin + (c % kFIn) * kIBytes;
+            qa = *reinterpret_cast<const u32x4 *>(I + kIQ + t * 64 + sg * 16);
+            ka = *reinterpret_cast<const u32x4 *>(I + kIK + t * 64 + sg * 16);
+            ga = *reinterpret_cast<const u32x4 *>(I + kIG + t * 64 + sg * 16);
+            va = *reinterpret_cast<const u32x4 *>(I + kIV + t * 64 + sg * 16);
+            bw = *reinterpret_cast<const uint32_t *>(I + kIB + t * 4);
+        };
+        read_inputs(0);
 
         const float lb2 = lb * kLog2e;
 #pragma unroll 1
@@ -198,21 +214,16 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
             if (tau < nch) {
                 // ------------------------------------------------ stage A, chunk c = tau
                 const int c = tau;
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kFPending) : "memory");  // chunk c landed
-                const char *I = myin + (c % kFIn) * kIBytes;
+                // the registers hold chunk c (reads completed before the last barrier):
+                // refill its input slot with chunk c + kFIn
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                dma_chunk(c + kFIn, c % kFIn);
                 const int t0 = tb + c * kC, len = min(kC, te - t0);
                 // rows past the end of the sequence hold copies of its last row; zero
                 // gate and beta make them absent: they reach only the masked triangles
                 // of R and A^qk, rows of E' that come out exactly zero, and output rows
                 // that are never stored
                 const bool valid = t < len;
-                const u32x4 qa = *reinterpret_cast<const u32x4 *>(I + kIQ + t * 64 + sg * 16);
-                const u32x4 ka = *reinterpret_cast<const u32x4 *>(I + kIK + t * 64 + sg * 16);
-                const u32x4 ga = *reinterpret_cast<const u32x4 *>(I + kIG + t * 64 + sg * 16);
-                const u32x4 va = *reinterpret_cast<const u32x4 *>(I + kIV + t * 64 + sg * 16);
-                const uint32_t bw = *reinterpret_cast<const uint32_t *>(I + kIB + t * 4);
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // input slot read: refill it
-                dma_chunk(c + kFIn, c % kFIn);
 
                 const int brow = min(t0 + t, te - 1);
                 const bool bhi = (reinterpret_cast<uintptr_t>(bb8 + ((int64_t)brow * H + h) * 2) & 2) != 0;
@@ -310,6 +321,7 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                 }
                 *reinterpret_cast<u32x4 *>(P + kPV + t * kVRow + (32 * m + 8 * sg) * 2) =
                     valid ? va : u32x4{0u, 0u, 0u, 0u};
+                if (c + 1 < nch) read_inputs(c + 1);
             }
             tick_sync();
         }
@@ -411,7 +423,8 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                 }
             }
         }
-        tick_sync();
+        // consumers write no LDS and use every value they read before this point
+        bar_sync();
     }
     if (s1) {
 #pragma unroll

@@ -244,7 +244,9 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
     using Sh = K2Shape<CONS>;
     constexpr int kGroups = 8 / CONS;  // workgroups per (sequence, head)
     __shared__ __attribute__((aligned(1024))) char lds[Sh::slots][kSlotBytes];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index is uniform over the wave: keep it scalar so role branches and
+    // the address arithmetic built on it stay in scalar registers
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // Workgroup b runs on XCD b % 8; the kGroups workgroups of one pair share an
     // XCD (and its L2), which serves the repeated unit reads.
     int pair = blockIdx.x, wbase = 0;
