@@ -40,8 +40,9 @@ def algorithmic_work(w):
       recurrence kernel: reads the unit and v (256 B per token-head), writes o
         (256 B per token-head); per (sequence, head) it reads the 64 KiB fp32
         initial state (when given) and writes the 64 KiB final state;
-      single-pass kernel: reads q, k, g_raw, v and beta_raw (4 x 256 + 2 B per
-        token-head), writes o (256 B per token-head), and the states as above.
+      single-pass and token-by-token kernels: read q, k, g_raw, v and beta_raw
+        (4 x 256 + 2 B per token-head), write o (256 B per token-head), and the
+        states as above.
     Recurrence flops per unit (both paths): K_b S^T and Q_b S^T
     (2 x 2*16*128*128), the state update K_end^T E (2*128*16*128), A^kk E and
     A^qk E (2 x 2*16*16*128) and the decay (128*128).
@@ -93,8 +94,8 @@ def time_path(call, path, steps, warmup):
     """Run `steps` timed forwards on `path`; returns wall ms per step and the
     event-measured average ms of each kernel call."""
     import torch
-    if path == "fused":
-        stages = [("kf_fused", call.run)]
+    if path in ("fused", "recurrent"):
+        stages = [("kf_fused" if path == "fused" else "kr_recurrent", call.run)]
     else:
         stages = [("k1_mfma", call.prepare), ("k2_mfma", call.recur)]
     for _ in range(warmup):
@@ -120,8 +121,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5"])
-    ap.add_argument("--path", default="auto", choices=["auto", "fused", "split"],
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5", "d1"])
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "split", "recurrent"],
                     help="kernels of the timed step (auto: the library's rule)")
     ap.add_argument("--compare-steps", type=int, default=100,
                     help="steps of the other path, timed afterwards for comparison (0: skip)")
@@ -149,11 +150,14 @@ def main():
         q, k, v, g = (t.view(shp) for t in (q, k, v, g))
         b = b.view(shp[:3])
     path = args.path
-    if path == "auto":
-        path = "fused" if w.N * w.H >= kda.FUSED_MIN_PAIRS else "split"
-    other = "split" if path == "fused" else "fused"
+    if path == "auto":  # the library's rule, include/kda.h
+        if w.T_tot <= kda.RECURRENT_MAX_AVG_TOKENS * w.N:
+            path = "recurrent"
+        else:
+            path = "fused" if w.N * w.H >= kda.FUSED_MIN_PAIRS else "split"
+    other = "split" if path != "split" else "fused"
     calls = {p: kda.prepare_call(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu,
-                                 path=p) for p in ("fused", "split")}
+                                 path=p) for p in (path, other)}
     torch.cuda.synchronize()
 
     ms_per_step, kern_ms = time_path(calls[path], path, args.steps, args.warmup)
@@ -172,13 +176,14 @@ def main():
         torch.cuda.synchronize()
 
     work = algorithmic_work(w)
-    bytes_of = {"k1_mfma": work["k1_bytes"], "k2_mfma": work["k2_bytes"], "kf_fused": work["kf_bytes"]}
+    bytes_of = {"k1_mfma": work["k1_bytes"], "k2_mfma": work["k2_bytes"], "kf_fused": work["kf_bytes"],
+                "kr_recurrent": work["kf_bytes"]}
     per_kernel = {}
     for name, ms in kern_ms.items():
         gbs = bytes_of[name] / (ms * 1e-3) / 1e9
         ent = {"avg_ms": round(ms, 4), "algorithmic_bytes": bytes_of[name], "achieved_GBps": round(gbs, 1),
                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-        if name != "k1_mfma":
+        if name in ("k2_mfma", "kf_fused"):
             tf = work["flops"] / (ms * 1e-3) / 1e12
             ent.update({"algorithmic_flops": work["flops"], "achieved_TFLOPs": round(tf, 2),
                         "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)})

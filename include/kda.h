@@ -16,7 +16,9 @@
  * as x / sqrt(sum x^2 + 1e-6). It is evaluated with the chunkwise method of the
  * same Doubleword page, section 6, either split into a chunk-parallel kernel
  * and a per-(sequence, head) recurrence kernel, or in one single-pass kernel
- * per (sequence, head) (see KDA_FLAG_SPLIT / KDA_FLAG_FUSED).
+ * per (sequence, head) (see KDA_FLAG_SPLIT / KDA_FLAG_FUSED); short sequences
+ * and decode steps run the section 4 recurrence token by token
+ * (KDA_FLAG_RECURRENT).
  *
  * Conventions for every entry point:
  *  - Pointers named "device" point to GPU memory; all others to host memory.
@@ -87,16 +89,25 @@ enum {
      * recurrence on it; the workspace holds only the chunk map). Not valid
      * with fp32 compute, with KDA_FLAG_SPLIT, or for kda_fwd_prepare /
      * kda_fwd_recur. */
-    KDA_FLAG_FUSED = 4u
+    KDA_FLAG_FUSED = 4u,
+    /* kda_fwd: run the token-by-token kernel (the boxed recurrence in fp32,
+     * one token after another, for decode and short sequences; any io and
+     * state dtype; the workspace holds only the chunk map). Not valid with
+     * KDA_FLAG_SPLIT or KDA_FLAG_FUSED, or for kda_fwd_prepare /
+     * kda_fwd_recur. */
+    KDA_FLAG_RECURRENT = 8u
 };
-/* Without either path flag, bf16-compute kda_fwd runs the single-pass kernel
- * when num_seqs * num_heads >= KDA_FUSED_MIN_PAIRS (enough (sequence, head)
- * pairs to occupy the GPU's compute units one pair each) and the two-kernel
- * path otherwise. The two paths evaluate the same chunkwise equations and
+/* Without a path flag, kda_fwd runs the token-by-token kernel when the
+ * sequences average at most KDA_RECURRENT_MAX_AVG_TOKENS tokens (batch mode:
+ * seqlen; packed: T_tot / num_seqs), else, for bf16 compute, the single-pass
+ * kernel when num_seqs * num_heads >= KDA_FUSED_MIN_PAIRS (enough (sequence,
+ * head) pairs to occupy the GPU's compute units one pair each) and the
+ * two-kernel path otherwise; fp32 compute uses the fp32 two-kernel path. The two paths evaluate the same chunkwise equations and
  * agree to bf16 rounding; they are not bitwise identical (the single pass
  * applies the L2 normalisation after its in-chunk products instead of
  * before). */
 #define KDA_FUSED_MIN_PAIRS 192
+#define KDA_RECURRENT_MAX_AVG_TOKENS 4
 
 /*
  * Problem description (host memory).
@@ -129,9 +140,9 @@ typedef struct kda_desc {
  * function; no GPU call). The size is an upper bound computed from B, T, N
  * and H only, because the chunk count of a packed batch depends on device-side
  * cu_seqlens: at most (T_tot + 15 N) / 16 chunks. Unless flags hold
- * KDA_FLAG_FUSED, it covers the two-kernel path, so the same workspace also
- * serves kda_fwd_prepare / kda_fwd_recur; with KDA_FLAG_FUSED it is only the
- * chunk map (a few hundred bytes plus 8 (N + 1)). Returns 0 if the
+ * KDA_FLAG_FUSED or KDA_FLAG_RECURRENT, it covers the two-kernel path, so the
+ * same workspace also serves kda_fwd_prepare / kda_fwd_recur; with either of
+ * those flags it is only the chunk map (a few hundred bytes plus 8 (N + 1)). Returns 0 if the
  * description itself is invalid (NULL, bad shape, dtype or flags).
  */
 size_t kda_fwd_workspace_size(const kda_desc_t *desc);
@@ -180,8 +191,8 @@ kda_status_t kda_fwd(const void *q, const void *k, const void *v,
  * outputs, sections 6.4-6.5) reads it and writes out and final_state.
  * kda_fwd(args) on the two-kernel path (see KDA_FLAG_SPLIT) is exactly
  * kda_fwd_prepare(args) followed by kda_fwd_recur(args). Both take kda_fwd's
- * arguments with the same meaning and checks (KDA_FLAG_FUSED is rejected with
- * KDA_ERR_BAD_ARG); recur must see the workspace written by a prepare call
+ * arguments with the same meaning and checks (KDA_FLAG_FUSED and
+ * KDA_FLAG_RECURRENT are rejected with KDA_ERR_BAD_ARG); recur must see the workspace written by a prepare call
  * with the same arguments, ordered before it (same stream, or an event). Each
  * returns after enqueueing its kernels.
  */

@@ -9,9 +9,11 @@ CPU or PyTorch fallback: if the library is missing the calls raise.
                            initial_state=None, output_final_state=True,
                            cu_seqlens=None, path="auto")
 
-`path` picks the kernels of a bf16-compute call: "split" (chunk-parallel
-kernel, then recurrence kernel), "fused" (one single-pass kernel) or "auto"
-(the library's rule: fused from KDA_FUSED_MIN_PAIRS (sequence, head) pairs on).
+`path` picks the kernels: "split" (chunk-parallel kernel, then recurrence
+kernel), "fused" (one single-pass kernel, bf16 compute only), "recurrent" (the
+recurrence token by token, for decode and short sequences) or "auto" (the
+library's rule: recurrent up to RECURRENT_MAX_AVG_TOKENS tokens per sequence on
+average, else fused from FUSED_MIN_PAIRS (sequence, head) pairs on, else split).
 
 Layouts follow the FlashKDA API (DocSearch FlashKDA digest, "flash_kda.fwd API
 reference"): q, k, v, g_raw are [B, T, H, 128] (or packed [T_tot, H, 128]),
@@ -24,15 +26,18 @@ import ctypes
 import os
 
 __all__ = ["fwd", "prepare_call", "Call", "workspace_size", "KdaError", "load_library", "library_path", "seqlens_flag",
-           "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE", "FLAG_SPLIT", "FLAG_FUSED", "FUSED_MIN_PAIRS"]
+           "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE", "FLAG_SPLIT", "FLAG_FUSED", "FLAG_RECURRENT", "FUSED_MIN_PAIRS",
+           "RECURRENT_MAX_AVG_TOKENS"]
 
 HEAD_DIM = 128
 CHUNK = 16
 FLAG_FP32_COMPUTE = 1
 FLAG_SPLIT = 2
 FLAG_FUSED = 4
+FLAG_RECURRENT = 8
 FUSED_MIN_PAIRS = 192
-_PATH_FLAGS = {"auto": 0, "split": FLAG_SPLIT, "fused": FLAG_FUSED}
+RECURRENT_MAX_AVG_TOKENS = 4
+_PATH_FLAGS = {"auto": 0, "split": FLAG_SPLIT, "fused": FLAG_FUSED, "recurrent": FLAG_RECURRENT}
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 

@@ -25,17 +25,23 @@ Range range_of(const void *p, size_t bytes)
 bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+enum Path { kSplit, kFused, kRecurrent };
+
 struct Shape {
     int64_t T_tot, n_c_max;
-    bool f32_path, fused;
+    bool f32_path;
+    Path path;  // what kda_fwd runs
 };
 
 // Which kernels kda_fwd runs (the rule is stated with KDA_FUSED_MIN_PAIRS).
-bool pick_fused(const kda_desc_t *d, bool f32_path)
+Path pick_path(const kda_desc_t *d, bool f32_path, int64_t T_tot)
 {
-    if (f32_path || (d->flags & KDA_FLAG_SPLIT)) return false;
-    if (d->flags & KDA_FLAG_FUSED) return true;
-    return d->num_seqs * (int64_t)d->num_heads >= KDA_FUSED_MIN_PAIRS;
+    if (d->flags & KDA_FLAG_RECURRENT) return kRecurrent;
+    if (d->flags & KDA_FLAG_FUSED) return kFused;
+    if (d->flags & KDA_FLAG_SPLIT) return kSplit;
+    if (T_tot <= (int64_t)KDA_RECURRENT_MAX_AVG_TOKENS * d->num_seqs) return kRecurrent;
+    if (!f32_path && d->num_seqs * (int64_t)d->num_heads >= KDA_FUSED_MIN_PAIRS) return kFused;
+    return kSplit;
 }
 
 // Shape-level checks shared by the size query and the forward call.
@@ -48,10 +54,12 @@ kda_status_t check_desc(const kda_desc_t *d, bool varlen, Shape *out)
     if ((d->io_dtype != KDA_DTYPE_BF16 && d->io_dtype != KDA_DTYPE_FP32) ||
         (d->state_dtype != KDA_DTYPE_BF16 && d->state_dtype != KDA_DTYPE_FP32))
         return KDA_ERR_BAD_DTYPE;
-    const uint32_t known = KDA_FLAG_FP32_COMPUTE | KDA_FLAG_SPLIT | KDA_FLAG_FUSED;
+    const uint32_t known = KDA_FLAG_FP32_COMPUTE | KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT;
     if (d->flags & ~known) return KDA_ERR_BAD_ARG;
     const bool f32_path = d->io_dtype == KDA_DTYPE_FP32 || (d->flags & KDA_FLAG_FP32_COMPUTE);
-    if ((d->flags & KDA_FLAG_FUSED) && (f32_path || (d->flags & KDA_FLAG_SPLIT))) return KDA_ERR_BAD_ARG;
+    const uint32_t paths = d->flags & (KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT);
+    if (paths & (paths - 1)) return KDA_ERR_BAD_ARG;  // more than one path flag
+    if ((d->flags & KDA_FLAG_FUSED) && f32_path) return KDA_ERR_BAD_ARG;
     int64_t T_tot, n_c_max;
     const int64_t lim = (int64_t)1 << 30;  // tokens and sequences addressed with int32 on the device
     if (varlen) {
@@ -70,7 +78,7 @@ kda_status_t check_desc(const kda_desc_t *d, bool varlen, Shape *out)
     out->T_tot = T_tot;
     out->n_c_max = n_c_max;
     out->f32_path = f32_path;
-    out->fused = pick_fused(d, f32_path);
+    out->path = pick_path(d, f32_path, T_tot);
     return KDA_OK;
 }
 
@@ -84,9 +92,10 @@ extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc)
     for (int varlen = 0; varlen < 2; ++varlen) {
         Shape s;
         if (check_desc(desc, varlen != 0, &s) != KDA_OK) continue;
-        // the single pass needs no units, but without KDA_FLAG_FUSED the same
-        // description is also valid for the two-stage entry points
-        const bool units = !(desc->flags & KDA_FLAG_FUSED);
+        // the single-pass and token-by-token paths need no units, but without
+        // their flags the same description is also valid for the two-stage
+        // entry points
+        const bool units = !(desc->flags & (KDA_FLAG_FUSED | KDA_FLAG_RECURRENT));
         size_t b = kda::ws_layout(desc->num_seqs, desc->num_heads, units ? s.n_c_max : 0, s.f32_path).total;
         if (b > best) best = b;
     }
@@ -106,8 +115,10 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     const bool varlen = cu_seqlens != nullptr;
     kda_status_t st = check_desc(desc, varlen, &s);
     if (st != KDA_OK) return st;
-    if (stages != (kPrepare | kRecur) && (desc->flags & KDA_FLAG_FUSED)) return KDA_ERR_BAD_ARG;
-    const bool fused = stages == (kPrepare | kRecur) && s.fused;
+    if (stages != (kPrepare | kRecur) && (desc->flags & (KDA_FLAG_FUSED | KDA_FLAG_RECURRENT)))
+        return KDA_ERR_BAD_ARG;
+    const Path path = stages == (kPrepare | kRecur) ? s.path : kSplit;
+    const bool no_units = path != kSplit;
     if (!isfinite(lower_bound) || lower_bound < KDA_LOWER_BOUND_MIN || lower_bound > KDA_LOWER_BOUND_MAX)
         return KDA_ERR_BAD_ARG;
     if (!isfinite(desc->scale) || !(desc->scale > 0.f)) return KDA_ERR_BAD_ARG;
@@ -121,7 +132,7 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
 
     if (s.T_tot > 0 && (!q || !k || !v || !g_raw || !beta_raw || !out)) return KDA_ERR_NULL_ARG;
     if (!workspace) return KDA_ERR_WORKSPACE;
-    const WsLayout lay = kda::ws_layout(N, H, fused ? 0 : s.n_c_max, s.f32_path);
+    const WsLayout lay = kda::ws_layout(N, H, no_units ? 0 : s.n_c_max, s.f32_path);
     if (workspace_bytes < lay.total || !aligned(workspace, KDA_WORKSPACE_ALIGN)) return KDA_ERR_WORKSPACE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g_raw, 16) || !aligned(out, 16) ||
         !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(beta_raw, esz))
@@ -155,8 +166,9 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     p.lay = lay;
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (fused) {
-        if (kda::launch_chunk_map(p, hs) != hipSuccess || kda::launch_fused(p, hs) != hipSuccess)
+    if (path == kFused || path == kRecurrent) {
+        if (kda::launch_chunk_map(p, hs) != hipSuccess) return KDA_ERR_HIP;
+        if ((path == kFused ? kda::launch_fused(p, hs) : kda::launch_recurrent(p, hs)) != hipSuccess)
             return KDA_ERR_HIP;
         return KDA_OK;
     }

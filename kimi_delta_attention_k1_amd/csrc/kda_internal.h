@@ -83,6 +83,7 @@ hipError_t launch_recur_ref(const Problem &p, hipStream_t s);   // fp32 K2
 hipError_t launch_prep_mfma(const Problem &p, hipStream_t s);   // bf16 K1
 hipError_t launch_recur_mfma(const Problem &p, hipStream_t s);  // bf16 K2
 hipError_t launch_fused(const Problem &p, hipStream_t s);       // bf16 single pass
+hipError_t launch_recurrent(const Problem &p, hipStream_t s);   // token-by-token (decode)
 
 // ---------------------------------------------------------------------------
 // Device helpers

@@ -28,8 +28,10 @@ KERNEL_SOURCES = {
     "k1_mfma": ("kda_mfma.hip", "kda_mfma_common.h", "kda_internal.h"),
     "k2_mfma": ("kda_mfma.hip", "kda_mfma_common.h", "kda_internal.h"),
     "kf_fused": ("kda_fused.hip", "kda_mfma_common.h", "kda_internal.h"),
+    "kr_recurrent": ("kda_recurrent.hip", "kda_internal.h"),
 }
 SHORT = {"k1_mfma": "kda::k1_mfma", "k2_mfma": "kda::k2_mfma", "kf_fused": "kda::kf_fused",
+         "kr_recurrent": "kda::kr_recurrent",
          "k0_chunk_map": "kda::k0_chunk_map", "copy": "__amd_rocclr_copyBuffer"}
 
 

@@ -17,6 +17,8 @@ Named workloads (T = tokens, H = heads, head dim 128, lower_bound = -5):
   c4  one sequence, T=131072, H=32, bf16, g_raw ~ N(-1,1), zero initial state, seed 3
   c5  64 packed sequences with lengths uniform in [256, 4096], H=32, bf16,
       g_raw ~ N(0,1), beta_raw ~ N(1,1), initial state N(0, 0.02^2), seed 4
+  d1  one decode step: 256 packed sequences x 1 token, H=32, bf16, all N(0,1),
+      initial state N(0, 0.02^2), seed 5
 """
 from __future__ import annotations
 
@@ -114,7 +116,11 @@ def c5() -> Workload:
                 lens_drawn=(256, 4096, 64))
 
 
-CONFIGS = {"c1": c1, "c2": c2, "c3": c3, "c4": c4, "c5": c5}
+def d1() -> Workload:
+    return make([1] * 256, 32, seed=5, packed=True, init_std=0.02, name="d1")
+
+
+CONFIGS = {"c1": c1, "c2": c2, "c3": c3, "c4": c4, "c5": c5, "d1": d1}
 
 DESCRIPTIONS = {
     "c1": "single sequence T=64 H=1 D=128 fp32 I/O, zero initial state",
@@ -123,4 +129,5 @@ DESCRIPTIONS = {
     "c4": "long context T=131072 H=32 D=128 bf16, g_raw ~ N(-1,1), zero initial state",
     "c5": "ragged varlen 64 sequences, lengths U[256,4096], H=32 D=128 bf16, beta_raw ~ N(1,1), "
           "initial state N(0,0.02^2)",
+    "d1": "decode step: 256 sequences x 1 token, H=32 D=128 bf16, initial state N(0,0.02^2)",
 }

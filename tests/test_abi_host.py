@@ -133,7 +133,9 @@ def _desc(**kw):
     (dict(lb=float("nan")), BAD_ARG),
     (dict(desc=dict(scale=0.0)), BAD_ARG),
     (dict(desc=dict(scale=float("inf"))), BAD_ARG),
-    (dict(desc=dict(flags=8)), BAD_ARG),                     # unknown flag bit
+    (dict(desc=dict(flags=16)), BAD_ARG),                    # unknown flag bit
+    (dict(desc=dict(flags=kda.FLAG_RECURRENT | kda.FLAG_FUSED)), BAD_ARG),
+    (dict(desc=dict(flags=kda.FLAG_RECURRENT | kda.FLAG_SPLIT)), BAD_ARG),
     (dict(desc=dict(flags=kda.FLAG_SPLIT | kda.FLAG_FUSED)), BAD_ARG),
     (dict(desc=dict(flags=kda.FLAG_FP32_COMPUTE | kda.FLAG_FUSED)), BAD_ARG),
     (dict(desc=dict(io_dtype=1, flags=kda.FLAG_FUSED)), BAD_ARG),  # fp32 I/O has no single pass
@@ -167,12 +169,16 @@ def test_path_flags_and_workspace(lib):
     assert kda.workspace_size(1, 65536, 8, 32, path="split") == kda.workspace_size(1, 65536, 8, 32)
     assert kda.workspace_size(1, 65536, 8, 32, path="auto") == _layout(8, 32, (65536 + 15 * 8) // 16, 14848)
     assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32, path="fused") == 0  # invalid: fp32 I/O
+    # the token-by-token path also needs only the chunk map, for any dtype
+    assert kda.workspace_size(1, 65536, 8, 32, path="recurrent") == _layout(8, 32, 0, 14848)
+    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32, path="recurrent") == _layout(1, 1, 0, 27136)
     with pytest.raises(ValueError):
         kda.workspace_size(1, 64, 1, 1, path="both")
 
 
-def test_stage_entry_points_reject_fused_flag(lib):
-    desc = _desc(flags=kda.FLAG_FUSED)
+@pytest.mark.parametrize("flag", [kda.FLAG_FUSED, kda.FLAG_RECURRENT])
+def test_stage_entry_points_reject_single_call_paths(lib, flag):
+    desc = _desc(flags=flag)
     f = Fake(dict(x=1 << 20))
     a = ctypes.c_void_p(f.addr["x"])
     for fn in (lib.kda_fwd_prepare, lib.kda_fwd_recur):
