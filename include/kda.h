@@ -95,7 +95,13 @@ enum {
      * state dtype; the workspace holds only the chunk map). Not valid with
      * KDA_FLAG_SPLIT or KDA_FLAG_FUSED, or for kda_fwd_prepare /
      * kda_fwd_recur. */
-    KDA_FLAG_RECURRENT = 8u
+    KDA_FLAG_RECURRENT = 8u,
+    /* g_raw holds one gate per token and head, [B*T][H] like beta_raw (only
+     * element-aligned), applied to every key channel: alpha_t is then
+     * exp(lower_bound * sigmoid(g_raw_t)) times the all-ones vector, the
+     * Gated DeltaNet special case of the recurrence (Doubleword page, section
+     * 3). Valid with every path. */
+    KDA_FLAG_SCALAR_GATE = 16u
 };
 /* Without a path flag, kda_fwd runs the token-by-token kernel when the
  * sequences average at most KDA_RECURRENT_MAX_AVG_TOKENS tokens (batch mode:
@@ -116,7 +122,7 @@ enum {
  * reference"; instagit FlashKDA summary "Chunked Token Processing"):
  *   q, k, g_raw, v, out : [B*T][H][128]  (batch rows flattened; with
  *                          cu_seqlens B = 1 and the T_tot tokens are packed)
- *   beta_raw            : [B*T][H]
+ *   beta_raw            : [B*T][H]  (g_raw too with KDA_FLAG_SCALAR_GATE)
  *   initial/final state : [N][H][128 (value channel V)][128 (key channel K)]
  *
  * Without cu_seqlens every batch row is an independent sequence of length
@@ -149,7 +155,8 @@ size_t kda_fwd_workspace_size(const kda_desc_t *desc);
 
 /*
  * Forward pass.
- *   q, k, v, g_raw : device, io_dtype, [B*T][H][128]
+ *   q, k, v, g_raw : device, io_dtype, [B*T][H][128] (g_raw: [B*T][H] with
+ *                    KDA_FLAG_SCALAR_GATE)
  *   beta_raw       : device, io_dtype, [B*T][H]
  *   cu_seqlens     : device int32 [N+1] token offsets, or NULL (batch mode).
  *                    Contents are the caller's contract (cu_seqlens[0] = 0,
@@ -168,7 +175,7 @@ size_t kda_fwd_workspace_size(const kda_desc_t *desc);
  *   workspace      : device, >= kda_fwd_workspace_size(desc) bytes, 128-B
  *                    aligned; contents on entry are ignored
  *   stream         : hipStream_t, or NULL for the null stream
- * Tensor bases must be 16-B aligned (beta_raw: element-aligned).
+ * Tensor bases must be 16-B aligned (beta_raw, and a scalar g_raw: element-aligned).
  * A sequence of length 0 gets final_state = initial_state (or zeros).
  * B*T = 0 with batch mode is a no-op apart from writing final_state.
  */

@@ -18,7 +18,9 @@ average, else fused from FUSED_MIN_PAIRS (sequence, head) pairs on, else split).
 Layouts follow the FlashKDA API (DocSearch FlashKDA digest, "flash_kda.fwd API
 reference"): q, k, v, g_raw are [B, T, H, 128] (or packed [T_tot, H, 128]),
 beta_raw is [B, T, H] (or [T_tot, H]); states are [N, H, 128 (V), 128 (K)];
-with cu_seqlens (int32, N+1 offsets) B must be 1.
+with cu_seqlens (int32, N+1 offsets) B must be 1. A g_raw shaped like beta_raw
+is a scalar per-head gate (Gated DeltaNet): one value per token and head for
+every key channel (KDA_FLAG_SCALAR_GATE).
 """
 from __future__ import annotations
 
@@ -26,8 +28,8 @@ import ctypes
 import os
 
 __all__ = ["fwd", "prepare_call", "Call", "workspace_size", "KdaError", "load_library", "library_path", "seqlens_flag",
-           "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE", "FLAG_SPLIT", "FLAG_FUSED", "FLAG_RECURRENT", "FUSED_MIN_PAIRS",
-           "RECURRENT_MAX_AVG_TOKENS"]
+           "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE", "FLAG_SPLIT", "FLAG_FUSED", "FLAG_RECURRENT", "FLAG_SCALAR_GATE",
+           "FUSED_MIN_PAIRS", "RECURRENT_MAX_AVG_TOKENS"]
 
 HEAD_DIM = 128
 CHUNK = 16
@@ -35,6 +37,7 @@ FLAG_FP32_COMPUTE = 1
 FLAG_SPLIT = 2
 FLAG_FUSED = 4
 FLAG_RECURRENT = 8
+FLAG_SCALAR_GATE = 16
 FUSED_MIN_PAIRS = 192
 RECURRENT_MAX_AVG_TOKENS = 4
 _PATH_FLAGS = {"auto": 0, "split": FLAG_SPLIT, "fused": FLAG_FUSED, "recurrent": FLAG_RECURRENT}
@@ -185,11 +188,17 @@ def prepare_call(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: 
         B, (T, H, D) = 1, q.shape
     else:
         raise ValueError("q must be [B,T,H,128] or [T_tot,H,128]")
-    for t in (k, v, g_raw):
+    for t in (k, v):
         if t.shape != q.shape:
-            raise ValueError("q, k, v and g_raw must have the same shape")
+            raise ValueError("q, k and v must have the same shape")
     if tuple(beta_raw.shape) != tuple(q.shape[:-1]):
         raise ValueError("beta_raw must have the shape of q without the last dimension")
+    if tuple(g_raw.shape) == tuple(q.shape):
+        scalar_gate = False
+    elif tuple(g_raw.shape) == tuple(q.shape[:-1]):
+        scalar_gate = True  # one gate per token and head
+    else:
+        raise ValueError("g_raw must have the shape of q, or of beta_raw for a scalar per-head gate")
     io = _dtype_code(q)
     if any(_dtype_code(t) != io for t in tensors):
         raise TypeError("q, k, v, g_raw and beta_raw must share one dtype")
@@ -215,7 +224,7 @@ def prepare_call(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: 
                                   device=q.device)
     if scale is None:
         scale = D ** -0.5
-    flags = _flags(fp32_compute, path)
+    flags = _flags(fp32_compute, path) | (FLAG_SCALAR_GATE if scalar_gate else 0)
     desc = make_desc(B, seqlen, N, H, io, st_code, scale, flags, head_dim=D)
     need = int(lib.kda_fwd_workspace_size(ctypes.byref(desc)))
     if workspace is None:

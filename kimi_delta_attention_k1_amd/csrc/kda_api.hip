@@ -54,7 +54,8 @@ kda_status_t check_desc(const kda_desc_t *d, bool varlen, Shape *out)
     if ((d->io_dtype != KDA_DTYPE_BF16 && d->io_dtype != KDA_DTYPE_FP32) ||
         (d->state_dtype != KDA_DTYPE_BF16 && d->state_dtype != KDA_DTYPE_FP32))
         return KDA_ERR_BAD_DTYPE;
-    const uint32_t known = KDA_FLAG_FP32_COMPUTE | KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT;
+    const uint32_t known =
+        KDA_FLAG_FP32_COMPUTE | KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT | KDA_FLAG_SCALAR_GATE;
     if (d->flags & ~known) return KDA_ERR_BAD_ARG;
     const bool f32_path = d->io_dtype == KDA_DTYPE_FP32 || (d->flags & KDA_FLAG_FP32_COMPUTE);
     const uint32_t paths = d->flags & (KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT);
@@ -128,20 +129,22 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     const size_t ssz = desc->state_dtype == KDA_DTYPE_BF16 ? 2 : 4;
     const size_t tens = (size_t)s.T_tot * H * KDA_HEAD_DIM * esz;
     const size_t bet = (size_t)s.T_tot * H * esz;
+    const bool sgate = (desc->flags & KDA_FLAG_SCALAR_GATE) != 0;
+    const size_t gsz = sgate ? bet : tens;
     const size_t sts = (size_t)N * H * KDA_HEAD_DIM * KDA_HEAD_DIM * ssz;
 
     if (s.T_tot > 0 && (!q || !k || !v || !g_raw || !beta_raw || !out)) return KDA_ERR_NULL_ARG;
     if (!workspace) return KDA_ERR_WORKSPACE;
     const WsLayout lay = kda::ws_layout(N, H, no_units ? 0 : s.n_c_max, s.f32_path);
     if (workspace_bytes < lay.total || !aligned(workspace, KDA_WORKSPACE_ALIGN)) return KDA_ERR_WORKSPACE;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g_raw, 16) || !aligned(out, 16) ||
-        !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(beta_raw, esz))
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g_raw, sgate ? esz : 16) ||
+        !aligned(out, 16) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(beta_raw, esz))
         return KDA_ERR_MISALIGNED;
     if (varlen && !aligned(cu_seqlens, 4)) return KDA_ERR_MISALIGNED;
 
     // Overlap rules: out and the workspace touch nothing else; final_state may
     // only coincide exactly with initial_state.
-    const Range rq = range_of(q, tens), rk = range_of(k, tens), rv = range_of(v, tens), rg = range_of(g_raw, tens);
+    const Range rq = range_of(q, tens), rk = range_of(k, tens), rv = range_of(v, tens), rg = range_of(g_raw, gsz);
     const Range rb = range_of(beta_raw, bet), ro = range_of(out, tens);
     const Range r0 = range_of(initial_state, sts), r1 = range_of(final_state, sts);
     const Range rw = range_of(workspace, lay.total);
@@ -162,6 +165,7 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     p.io_bf16 = desc->io_dtype == KDA_DTYPE_BF16;
     p.st_bf16 = desc->state_dtype == KDA_DTYPE_BF16;
     p.f32_path = s.f32_path;
+    p.scalar_gate = sgate;
     p.ws = static_cast<char *>(workspace);
     p.lay = lay;
 

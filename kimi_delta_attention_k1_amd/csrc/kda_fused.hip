@@ -53,7 +53,8 @@ constexpr int kVRow = 272;   // 256 + 16: row r starts 4 r banks further, so row
                              // 16-byte writes and column-wise reads spread over the banks
 constexpr int kPBytes = kPV + kC * kVRow;
 // per-prep-wave input slot: q, k, g_raw, v as [16 rows][32 channels] bf16, then
-// beta_raw as one aligned dword per lane (the token's element in its low or high half)
+// beta_raw as one aligned dword per lane (the token's element in its low or high half);
+// a scalar g_raw takes the same dword form at the start of its block
 constexpr int kIQ = 0, kIK = 1024, kIG = 2048, kIV = 3072, kIB = 4096, kIBytes = 4352;
 // partial-product buffer (two, alternating by chunk parity)
 constexpr int kXR = 0, kXRT = 1024, kXAQ = 2048, kXNQ = 3072, kXNK = 3136, kXWave = 3200;
@@ -71,7 +72,9 @@ __device__ __forceinline__ int swz(int L) { return L ^ ((L >> 3) & 7); }
 // barrier that first completes this wave's own LDS traffic (not its global loads)
 __device__ __forceinline__ void tick_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <typename TSt>
+// SG: scalar gate, g_raw is [T][H] and its one value per token and head applies to
+// every key channel (Gated DeltaNet, Doubleword section 3)
+template <typename TSt, bool SG>
 __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                       const uint16_t *__restrict__ v,
                                                       const uint16_t *__restrict__ graw,
@@ -182,12 +185,20 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
             char *dst = myin + slot * kIBytes;
             __builtin_amdgcn_global_load_lds(qb8 + off, (lds_void *)(dst + kIQ), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(kb8 + off, (lds_void *)(dst + kIK), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(gb8 + off, (lds_void *)(dst + kIG), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(vb8 + off, (lds_void *)(dst + kIV), 16, 0, 0);
-            // the dword holding beta_raw[brow][h]: rounding the address down to 4 bytes
-            // stays inside the 4-byte word, hence inside the page, that holds the element
+            // the dword holding beta_raw[brow][h] (and a scalar g_raw[brow][h]): rounding
+            // the address down to 4 bytes stays inside the 4-byte word, hence inside the
+            // page, that holds the element
             const int brow = min(tb + c * kC + (lane & 15), te - 1);
-            const uintptr_t ba = reinterpret_cast<uintptr_t>(bb8 + ((int64_t)brow * H + h) * 2);
+            const int64_t eo = ((int64_t)brow * H + h) * 2;
+            if constexpr (SG) {
+                const uintptr_t ga = reinterpret_cast<uintptr_t>(gb8 + eo);
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(ga & ~(uintptr_t)3),
+                                                 (lds_void *)(dst + kIG), 4, 0, 0);
+            } else {
+                __builtin_amdgcn_global_load_lds(gb8 + off, (lds_void *)(dst + kIG), 16, 0, 0);
+            }
+            const uintptr_t ba = reinterpret_cast<uintptr_t>(bb8 + eo);
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(ba & ~(uintptr_t)3),
                                              (lds_void *)(dst + kIB), 4, 0, 0);
         };
@@ -202,7 +213,11 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
             const char *I = myin + (c % kFIn) * kIBytes;
             qa = *reinterpret_cast<const u32x4 *>(I + kIQ + t * 64 + sg * 16);
             ka = *reinterpret_cast<const u32x4 *>(I + kIK + t * 64 + sg * 16);
-            ga = *reinterpret_cast<const u32x4 *>(I + kIG + t * 64 + sg * 16);
+            if constexpr (SG) {
+                ga[0] = *reinterpret_cast<const uint32_t *>(I + kIG + t * 4);
+            } else {
+                ga = *reinterpret_cast<const u32x4 *>(I + kIG + t * 64 + sg * 16);
+            }
             va = *reinterpret_cast<const u32x4 *>(I + kIV + t * 64 + sg * 16);
             bw = *reinterpret_cast<const uint32_t *>(I + kIB + t * 4);
         };
@@ -226,7 +241,8 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                 const bool valid = t < len;
 
                 const int brow = min(t0 + t, te - 1);
-                const bool bhi = (reinterpret_cast<uintptr_t>(bb8 + ((int64_t)brow * H + h) * 2) & 2) != 0;
+                const int64_t eo = ((int64_t)brow * H + h) * 2;  // byte offset of [brow][h]
+                const bool bhi = (reinterpret_cast<uintptr_t>(bb8 + eo) & 2) != 0;
                 const float vmask = valid ? 1.f : 0.f;
                 float qf[8], kf[8], gf[8];
 #pragma unroll
@@ -235,18 +251,32 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                     qf[2 * e + 1] = bf_hi(qa[e]);
                     kf[2 * e] = bf_lo(ka[e]);
                     kf[2 * e + 1] = bf_hi(ka[e]);
-                    gf[2 * e] = bf_lo(ga[e]);
-                    gf[2 * e + 1] = bf_hi(ga[e]);
                 }
                 const float beta = vmask * sigmoid_fast(bhi ? bf_hi(bw) : bf_lo(bw));
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {  // gate (log2 units) and prefix sum over tokens
-                    float x = vmask * lb2 * sigmoid_fast(gf[i]);
+                if constexpr (SG) {  // one gate and one prefix sum serve every channel
+                    const bool ghi = (reinterpret_cast<uintptr_t>(gb8 + eo) & 2) != 0;
+                    float x = vmask * lb2 * sigmoid_fast(ghi ? bf_hi(ga[0]) : bf_lo(ga[0]));
                     x += row_shr<1>(x);
                     x += row_shr<2>(x);
                     x += row_shr<4>(x);
                     x += row_shr<8>(x);
-                    gf[i] = x;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) gf[i] = x;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        gf[2 * e] = bf_lo(ga[e]);
+                        gf[2 * e + 1] = bf_hi(ga[e]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {  // gate (log2 units) and prefix sum over tokens
+                        float x = vmask * lb2 * sigmoid_fast(gf[i]);
+                        x += row_shr<1>(x);
+                        x += row_shr<2>(x);
+                        x += row_shr<4>(x);
+                        x += row_shr<8>(x);
+                        gf[i] = x;
+                    }
                 }
                 float nq = 0.f, nk = 0.f;  // partial squared norms over this wave's 32 channels
 #pragma unroll
@@ -434,12 +464,12 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
     }
 }
 
-template <typename TSt>
+template <typename TSt, bool SG>
 static hipError_t launch_fused_t(const Problem &p, hipStream_t s)
 {
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
-    hipLaunchKernelGGL((kf_fused<TSt>), dim3((unsigned)(p.N * p.H)), dim3(kFThreads), 0, s, (const uint16_t *)p.q,
+    hipLaunchKernelGGL((kf_fused<TSt, SG>), dim3((unsigned)(p.N * p.H)), dim3(kFThreads), 0, s, (const uint16_t *)p.q,
                        (const uint16_t *)p.k, (const uint16_t *)p.v, (const uint16_t *)p.g,
                        (const uint16_t *)p.beta, (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H,
                        p.lb, p.scale);
@@ -448,7 +478,8 @@ static hipError_t launch_fused_t(const Problem &p, hipStream_t s)
 
 hipError_t launch_fused(const Problem &p, hipStream_t s)
 {
-    return p.st_bf16 ? launch_fused_t<uint16_t>(p, s) : launch_fused_t<float>(p, s);
+    if (p.scalar_gate) return p.st_bf16 ? launch_fused_t<uint16_t, true>(p, s) : launch_fused_t<float, true>(p, s);
+    return p.st_bf16 ? launch_fused_t<uint16_t, false>(p, s) : launch_fused_t<float, false>(p, s);
 }
 
 }  // namespace kda

@@ -73,6 +73,7 @@ struct Problem {
     int64_t B, T, N, T_tot, n_c_max;
     int H;
     bool io_bf16, st_bf16, f32_path;
+    bool scalar_gate;       // g_raw is [T][H] (one gate per token and head), not [T][H][128]
     char *ws;
     WsLayout lay;
 };

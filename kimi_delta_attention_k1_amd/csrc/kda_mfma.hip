@@ -37,6 +37,9 @@ namespace kda {
 // ---------------------------------------------------------------------------
 constexpr int kK1MaxWaves = 4;
 
+// SG: scalar gate, g_raw is [T][H] and its one value per token and head applies
+// to every key channel (Gated DeltaNet, Doubleword section 3)
+template <bool SG>
 __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ graw,
     const uint16_t *__restrict__ braw, const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off,
@@ -59,18 +62,31 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
         const int64_t off = ((int64_t)(t0 + tok) * H + h) * kD + 32 * g;
         const u32x4 *pq = reinterpret_cast<const u32x4 *>(q + off);
         const u32x4 *pk = reinterpret_cast<const u32x4 *>(k + off);
-        const u32x4 *pg = reinterpret_cast<const u32x4 *>(graw + off);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            u32x4 a = pq[i], b = pk[i], d = pg[i];
+            u32x4 a = pq[i], b = pk[i];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 qf[8 * i + 2 * e] = bf_lo(a[e]);
                 qf[8 * i + 2 * e + 1] = bf_hi(a[e]);
                 kf[8 * i + 2 * e] = bf_lo(b[e]);
                 kf[8 * i + 2 * e + 1] = bf_hi(b[e]);
-                gf[8 * i + 2 * e] = bf_lo(d[e]);
-                gf[8 * i + 2 * e + 1] = bf_hi(d[e]);
+            }
+        }
+        if constexpr (SG) {
+            const float gs = bf16_bits_to_f32(graw[(int64_t)(t0 + tok) * H + h]);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) gf[i] = gs;
+        } else {
+            const u32x4 *pg = reinterpret_cast<const u32x4 *>(graw + off);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 d = pg[i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    gf[8 * i + 2 * e] = bf_lo(d[e]);
+                    gf[8 * i + 2 * e + 1] = bf_hi(d[e]);
+                }
             }
         }
     } else {
@@ -82,14 +98,24 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
 
     // ---- gate (log2 units) and in-chunk inclusive prefix sum over tokens
     const float lb2 = lb * kLog2e;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        float x = valid ? lb2 * sigmoid_fast(gf[i]) : 0.f;
+    if constexpr (SG) {  // one prefix sum serves every channel
+        float x = valid ? lb2 * sigmoid_fast(gf[0]) : 0.f;
         x += row_shr<1>(x);
         x += row_shr<2>(x);
         x += row_shr<4>(x);
         x += row_shr<8>(x);
-        gf[i] = x;  // G_tok (log2)
+#pragma unroll
+        for (int i = 0; i < 32; ++i) gf[i] = x;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            float x = valid ? lb2 * sigmoid_fast(gf[i]) : 0.f;
+            x += row_shr<1>(x);
+            x += row_shr<2>(x);
+            x += row_shr<4>(x);
+            x += row_shr<8>(x);
+            gf[i] = x;  // G_tok (log2)
+        }
     }
 
     // ---- L2 norms over 128 channels: 32 per lane, 4 lanes per token
@@ -397,7 +423,8 @@ hipError_t launch_prep_mfma(const Problem &p, hipStream_t s)
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
     const int wpb = (p.H % 4 == 0) ? 4 : (p.H % 2 == 0 ? 2 : 1);  // waves per block divide H
-    hipLaunchKernelGGL(k1_mfma, dim3((unsigned)p.n_c_max, p.H / wpb), dim3(64 * wpb), 0, s, (const uint16_t *)p.q,
+    auto kern = p.scalar_gate ? k1_mfma<true> : k1_mfma<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.n_c_max, p.H / wpb), dim3(64 * wpb), 0, s, (const uint16_t *)p.q,
                        (const uint16_t *)p.k, (const uint16_t *)p.g, (const uint16_t *)p.beta, tok, chk, (int)p.N,
                        p.H, p.n_c_max, p.lb, p.scale, p.ws + p.lay.units);
     return hipGetLastError();

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kRThreads) void kr_recurrent(const TIn *__restrict_
                                                           const TIn *__restrict__ v, const TIn *__restrict__ graw,
                                                           const TIn *__restrict__ braw, const TSt *s0, TSt *s1,
                                                           TIn *__restrict__ out, const int32_t *__restrict__ tok_off,
-                                                          int H, float lb, float scale)
+                                                          int H, float lb, float scale, int scalar_gate)
 {
     __shared__ __attribute__((aligned(16))) float sQ[kRBlock][kD], sK[kRBlock][kD], sA[kRBlock][kD];
     __shared__ float sB[kRBlock], sV[kRBlock][kRRows];
@@ -161,7 +161,9 @@ __global__ __launch_bounds__(kRThreads) void kr_recurrent(const TIn *__restrict_
         // still spreads over all 128 threads
         for (int e = tid; e < nb * kD; e += kRThreads) {
             const int j = e / kD, c = e % kD;
-            const float g = ld_elem(graw, ((int64_t)(t0 + j) * H + h) * kD + c);
+            // a scalar gate ([T][H]) serves every channel
+            const int64_t th = (int64_t)(t0 + j) * H + h;
+            const float g = ld_elem(graw, scalar_gate ? th : th * kD + c);
             sA[j][c] = __builtin_amdgcn_exp2f(lb2 * sigmoid2(g));
         }
         __syncthreads();
@@ -206,7 +208,7 @@ static hipError_t launch_recurrent_t(const Problem &p, hipStream_t st)
     const unsigned grid = (unsigned)(p.N * p.H * (kD / kRRows));
     hipLaunchKernelGGL((kr_recurrent<TIn, TSt>), dim3(grid), dim3(kRThreads), 0, st, (const TIn *)p.q,
                        (const TIn *)p.k, (const TIn *)p.v, (const TIn *)p.g, (const TIn *)p.beta, (const TSt *)p.s0,
-                       (TSt *)p.s1, (TIn *)p.out, tok, p.H, p.lb, p.scale);
+                       (TSt *)p.s1, (TIn *)p.out, tok, p.H, p.lb, p.scale, (int)p.scalar_gate);
     return hipGetLastError();
 }
 

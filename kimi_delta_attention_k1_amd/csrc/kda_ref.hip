@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void k1_ref(const TIn *__restrict__ q, const T
                                                const TIn *__restrict__ g, const TIn *__restrict__ beta,
                                                const int32_t *__restrict__ tok_off,
                                                const int32_t *__restrict__ chunk_off, int N, int H,
-                                               int64_t n_c_max, float lb, float scale,
+                                               int64_t n_c_max, float lb, float scale, int scalar_gate,
                                                char *__restrict__ units)
 {
     const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
@@ -126,7 +126,9 @@ __global__ __launch_bounds__(256) void k1_ref(const TIn *__restrict__ q, const T
             const int64_t off = ((int64_t)(t0 + i) * H + h) * kD + d;
             qv = ld_elem(q, off);
             kv = ld_elem(k, off);
-            gv = lb * sigmoid_ref(ld_elem(g, off));  // log-decay g = lb * sigmoid(g_raw)
+            // log-decay g = lb * sigmoid(g_raw); a scalar gate ([T][H]) serves every channel
+            const int64_t goff = scalar_gate ? (int64_t)(t0 + i) * H + h : off;
+            gv = lb * sigmoid_ref(ld_elem(g, goff));
         }
         sq[i][d] = qv;
         sk[i][d] = kv;
@@ -289,7 +291,7 @@ static hipError_t launch_prep_ref_t(const Problem &p, hipStream_t s)
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
     hipLaunchKernelGGL((k1_ref<TIn>), dim3((unsigned)p.n_c_max, p.H), dim3(256), 0, s, (const TIn *)p.q,
                        (const TIn *)p.k, (const TIn *)p.g, (const TIn *)p.beta, tok, chk, (int)p.N, p.H,
-                       p.n_c_max, p.lb, p.scale, p.ws + p.lay.units);
+                       p.n_c_max, p.lb, p.scale, (int)p.scalar_gate, p.ws + p.lay.units);
     return hipGetLastError();
 }
 

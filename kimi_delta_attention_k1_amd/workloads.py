@@ -75,8 +75,9 @@ def _draw(gen, shape, mean=0.0, std=1.0, dtype=torch.bfloat16):
 
 
 def make(seq_lens, H, *, seed, dtype=torch.bfloat16, packed=True, g_mean=0.0, beta_mean=0.0,
-         init_std=0.0, lower_bound=-5.0, name="custom", lens_drawn=None) -> Workload:
-    """Generic seeded workload. seq_lens: list of sequence lengths."""
+         init_std=0.0, lower_bound=-5.0, name="custom", lens_drawn=None, scalar_gate=False) -> Workload:
+    """Generic seeded workload. seq_lens: list of sequence lengths. scalar_gate:
+    g_raw is drawn as [T, H] (one gate per token and head) instead of [T, H, 128]."""
     gen = torch.Generator().manual_seed(int(seed))
     if lens_drawn is not None:  # ragged lengths are the first draw
         lo, hi, count = lens_drawn
@@ -86,13 +87,14 @@ def make(seq_lens, H, *, seed, dtype=torch.bfloat16, packed=True, g_mean=0.0, be
     q = _draw(gen, shape, dtype=dtype)
     k = _draw(gen, shape, dtype=dtype)
     v = _draw(gen, shape, dtype=dtype)
-    g = _draw(gen, shape, mean=g_mean, dtype=dtype)
+    g = _draw(gen, (T, H) if scalar_gate else shape, mean=g_mean, dtype=dtype)
     b = _draw(gen, (T, H), mean=beta_mean, dtype=dtype)
     s0 = None
     if init_std > 0:
         s0 = _draw(gen, (len(seq_lens), H, HEAD_DIM, HEAD_DIM), std=init_std, dtype=torch.float32)
     return Workload(name, q, k, v, g, b, list(seq_lens), packed, s0, lower_bound,
-                    dict(seed=seed, dtype=str(dtype), g_mean=g_mean, beta_mean=beta_mean, init_std=init_std))
+                    dict(seed=seed, dtype=str(dtype), g_mean=g_mean, beta_mean=beta_mean, init_std=init_std,
+                         scalar_gate=scalar_gate))
 
 
 def c1() -> Workload:

@@ -44,13 +44,21 @@ def run_gpu(w, dev, *, state_dtype=torch.float32, fp32_compute=False, workspace=
     else:
         B, T = w.N, w.seq_lens[0]
         shp = (B, T, w.H, 128)
-        o, s = kda.fwd(q.view(shp), k.view(shp), v.view(shp), g.view(shp), b.view(B, T, w.H),
+        gshp = shp if g.dim() == 3 else shp[:3]
+        o, s = kda.fwd(q.view(shp), k.view(shp), v.view(shp), g.view(gshp), b.view(B, T, w.H),
                        lower_bound=w.lower_bound, initial_state=s0, output_final_state=final,
                        fp32_compute=fp32_compute, workspace=workspace,
                        out=None if out is None else out.view(shp), final_state=final_state, path=path)
         o = o.view(B * T, w.H, 128)
     torch.cuda.synchronize(dev)
     return o, s
+
+
+def _gate(w):
+    """g_raw as the oracle takes it, [T, H, 128]: a scalar per-head gate is the
+    same value on every key channel (the Gated DeltaNet case of the recurrence)."""
+    g = w.g_raw
+    return g[..., None].expand(*g.shape, 128) if g.dim() == 2 else g
 
 
 def run_oracle(w, pairs=None, threads=0):
@@ -60,7 +68,7 @@ def run_oracle(w, pairs=None, threads=0):
     f = lambda t: t.to(torch.float32).numpy()  # noqa: E731  exact widening of bf16/fp32
     res = {}
     if pairs is None:
-        o, S = oracle.token_forward(f(w.q), f(w.k), f(w.v), f(w.g_raw), f(w.beta_raw), offs,
+        o, S = oracle.token_forward(f(w.q), f(w.k), f(w.v), f(_gate(w)), f(w.beta_raw), offs,
                                     None if w.initial_state is None else w.initial_state.numpy(),
                                     lower_bound=w.lower_bound, threads=threads)
         for n in range(w.N):
@@ -75,7 +83,7 @@ def run_oracle(w, pairs=None, threads=0):
         a, e = offs[n], offs[n + 1]
         sl = lambda t: f(t[a:e][:, hs])  # noqa: E731
         s0 = None if w.initial_state is None else w.initial_state[n][hs].numpy()[None]
-        o, S = oracle.token_forward(sl(w.q), sl(w.k), sl(w.v), sl(w.g_raw), sl(w.beta_raw), [0, e - a], s0,
+        o, S = oracle.token_forward(sl(w.q), sl(w.k), sl(w.v), sl(_gate(w)), sl(w.beta_raw), [0, e - a], s0,
                                     lower_bound=w.lower_bound, threads=threads)
         for i, h in enumerate(hs):
             res[(n, h)] = (o[:, i], S[0, i])

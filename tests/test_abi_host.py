@@ -133,7 +133,7 @@ def _desc(**kw):
     (dict(lb=float("nan")), BAD_ARG),
     (dict(desc=dict(scale=0.0)), BAD_ARG),
     (dict(desc=dict(scale=float("inf"))), BAD_ARG),
-    (dict(desc=dict(flags=16)), BAD_ARG),                    # unknown flag bit
+    (dict(desc=dict(flags=32)), BAD_ARG),                    # unknown flag bit
     (dict(desc=dict(flags=kda.FLAG_RECURRENT | kda.FLAG_FUSED)), BAD_ARG),
     (dict(desc=dict(flags=kda.FLAG_RECURRENT | kda.FLAG_SPLIT)), BAD_ARG),
     (dict(desc=dict(flags=kda.FLAG_SPLIT | kda.FLAG_FUSED)), BAD_ARG),
@@ -147,6 +147,8 @@ def _desc(**kw):
     (dict(ws_bytes=1000), WORKSPACE),
     (dict(shift=dict(ws=64)), WORKSPACE),
     (dict(shift=dict(q=2)), MISALIGNED),
+    (dict(shift=dict(g=2)), MISALIGNED),                     # [T][H][128] g_raw needs 16 bytes
+    (dict(desc=dict(flags=kda.FLAG_SCALAR_GATE), shift=dict(g=1)), MISALIGNED),  # scalar g_raw: 2 bytes
     (dict(shift=dict(s1=8)), MISALIGNED),
     (dict(overrides=dict(out=("q", 0))), BAD_ARG),          # out aliases q
     (dict(overrides=dict(s1=("s0", 256))), BAD_ARG),        # partial state overlap
