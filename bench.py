@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5", "d1"])
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "split", "recurrent"],
                     help="kernels of the timed step (auto: the library's rule)")
+    ap.add_argument("--bf16-resident-state", action="store_true",
+                    help="two-kernel path with the recurrence's state rounded to bf16 between chunks")
     ap.add_argument("--compare-steps", type=int, default=100,
                     help="steps of the other path, timed afterwards for comparison (0: skip)")
     ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU-baseline sample (0: skip)")
@@ -150,14 +152,17 @@ def main():
         q, k, v, g = (t.view(shp) for t in (q, k, v, g))
         b = b.view(shp[:3])
     path = args.path
+    if args.bf16_resident_state:
+        path = "split"
     if path == "auto":  # the library's rule, include/kda.h
         if w.T_tot <= kda.RECURRENT_MAX_AVG_TOKENS * w.N:
             path = "recurrent"
         else:
             path = "fused" if w.N * w.H >= kda.FUSED_MIN_PAIRS else "split"
     other = "split" if path != "split" else "fused"
-    calls = {p: kda.prepare_call(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu,
-                                 path=p) for p in (path, other)}
+    calls = {p: kda.prepare_call(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu, path=p,
+                                 bf16_resident_state=args.bf16_resident_state and p == "split")
+             for p in (path, other)}
     torch.cuda.synchronize()
 
     ms_per_step, kern_ms = time_path(calls[path], path, args.steps, args.warmup)
@@ -201,7 +206,8 @@ def main():
         "data": "synthetic (seeded CPU torch.Generator, N(0,1) family; see workloads.py)",
         "config": {"workload": f"{args.workload}: {workloads.DESCRIPTIONS[args.workload]}",
                    "tokens": w.T_tot, "heads": w.H, "head_dim": 128, "sequences": w.N, "chunk": 16,
-                   "lower_bound": w.lower_bound, "path": path},
+                   "lower_bound": w.lower_bound,
+                   "path": path + (" (bf16-resident state)" if args.bf16_resident_state else "")},
         "event_ms_per_step": round(sum(kern_ms.values()), 4),
         "kernels": per_kernel,
         "roofline": roofline,

@@ -101,7 +101,14 @@ enum {
      * exp(lower_bound * sigmoid(g_raw_t)) times the all-ones vector, the
      * Gated DeltaNet special case of the recurrence (Doubleword page, section
      * 3). Valid with every path. */
-    KDA_FLAG_SCALAR_GATE = 16u
+    KDA_FLAG_SCALAR_GATE = 16u,
+    /* Two-kernel bf16 path with a bf16-resident recurrent state: the
+     * recurrence rounds its state to bf16 when loading it and after every
+     * chunk's fp32 update, as a kernel that keeps the on-chip state in bf16
+     * between updates does (FlashKDA deep-dive, section 3), instead of
+     * carrying it in fp32. For measuring that choice; implies the two-kernel
+     * path and is not valid with fp32 compute or another path flag. */
+    KDA_FLAG_BF16_RESIDENT_STATE = 32u
 };
 /* Without a path flag, kda_fwd runs the token-by-token kernel when the
  * sequences average at most KDA_RECURRENT_MAX_AVG_TOKENS tokens (batch mode:

@@ -29,6 +29,7 @@ import os
 
 __all__ = ["fwd", "prepare_call", "Call", "workspace_size", "KdaError", "load_library", "library_path", "seqlens_flag",
            "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE", "FLAG_SPLIT", "FLAG_FUSED", "FLAG_RECURRENT", "FLAG_SCALAR_GATE",
+           "FLAG_BF16_RESIDENT_STATE",
            "FUSED_MIN_PAIRS", "RECURRENT_MAX_AVG_TOKENS"]
 
 HEAD_DIM = 128
@@ -38,6 +39,7 @@ FLAG_SPLIT = 2
 FLAG_FUSED = 4
 FLAG_RECURRENT = 8
 FLAG_SCALAR_GATE = 16
+FLAG_BF16_RESIDENT_STATE = 32
 FUSED_MIN_PAIRS = 192
 RECURRENT_MAX_AVG_TOKENS = 4
 _PATH_FLAGS = {"auto": 0, "split": FLAG_SPLIT, "fused": FLAG_FUSED, "recurrent": FLAG_RECURRENT}
@@ -155,17 +157,20 @@ class Call:
 
 def fwd(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | None = None,
         initial_state=None, output_final_state: bool = True, cu_seqlens=None, out=None, final_state=None,
-        workspace=None, fp32_compute: bool = False, path: str = "auto", stream=None):
+        workspace=None, fp32_compute: bool = False, path: str = "auto", bf16_resident_state: bool = False,
+        stream=None):
     """KDA forward through kda_fwd. Returns (out, final_state or None).
 
     All tensors must be contiguous and on the same GPU. `stream` is a
     torch.cuda.Stream (default: the current stream). `workspace` may be a
     preallocated uint8 tensor of at least workspace_size(...) bytes.
+    bf16_resident_state runs the two-kernel path with the recurrence's state
+    rounded to bf16 between chunk updates (KDA_FLAG_BF16_RESIDENT_STATE).
     """
     c = prepare_call(q, k, v, g_raw, beta_raw, lower_bound=lower_bound, scale=scale, initial_state=initial_state,
                      output_final_state=output_final_state, cu_seqlens=cu_seqlens, out=out,
                      final_state=final_state, workspace=workspace, fp32_compute=fp32_compute, path=path,
-                     stream=stream)
+                     bf16_resident_state=bf16_resident_state, stream=stream)
     c.run()
     return c.out, c.final_state
 
@@ -173,7 +178,7 @@ def fwd(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | N
 def prepare_call(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | None = None,
                  initial_state=None, output_final_state: bool = True, cu_seqlens=None, out=None,
                  final_state=None, workspace=None, fp32_compute: bool = False, path: str = "auto",
-                 stream=None) -> Call:
+                 bf16_resident_state: bool = False, stream=None) -> Call:
     """Check and marshal fwd's arguments once (allocating out, final_state and
     the workspace when not given) without launching anything."""
     import torch
@@ -224,7 +229,8 @@ def prepare_call(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: 
                                   device=q.device)
     if scale is None:
         scale = D ** -0.5
-    flags = _flags(fp32_compute, path) | (FLAG_SCALAR_GATE if scalar_gate else 0)
+    flags = _flags(fp32_compute, path) | (FLAG_SCALAR_GATE if scalar_gate else 0) | \
+        (FLAG_BF16_RESIDENT_STATE if bf16_resident_state else 0)
     desc = make_desc(B, seqlen, N, H, io, st_code, scale, flags, head_dim=D)
     need = int(lib.kda_fwd_workspace_size(ctypes.byref(desc)))
     if workspace is None:

@@ -38,7 +38,7 @@ Path pick_path(const kda_desc_t *d, bool f32_path, int64_t T_tot)
 {
     if (d->flags & KDA_FLAG_RECURRENT) return kRecurrent;
     if (d->flags & KDA_FLAG_FUSED) return kFused;
-    if (d->flags & KDA_FLAG_SPLIT) return kSplit;
+    if (d->flags & (KDA_FLAG_SPLIT | KDA_FLAG_BF16_RESIDENT_STATE)) return kSplit;
     if (T_tot <= (int64_t)KDA_RECURRENT_MAX_AVG_TOKENS * d->num_seqs) return kRecurrent;
     if (!f32_path && d->num_seqs * (int64_t)d->num_heads >= KDA_FUSED_MIN_PAIRS) return kFused;
     return kSplit;
@@ -54,13 +54,15 @@ kda_status_t check_desc(const kda_desc_t *d, bool varlen, Shape *out)
     if ((d->io_dtype != KDA_DTYPE_BF16 && d->io_dtype != KDA_DTYPE_FP32) ||
         (d->state_dtype != KDA_DTYPE_BF16 && d->state_dtype != KDA_DTYPE_FP32))
         return KDA_ERR_BAD_DTYPE;
-    const uint32_t known =
-        KDA_FLAG_FP32_COMPUTE | KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT | KDA_FLAG_SCALAR_GATE;
+    const uint32_t known = KDA_FLAG_FP32_COMPUTE | KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT |
+                           KDA_FLAG_SCALAR_GATE | KDA_FLAG_BF16_RESIDENT_STATE;
     if (d->flags & ~known) return KDA_ERR_BAD_ARG;
     const bool f32_path = d->io_dtype == KDA_DTYPE_FP32 || (d->flags & KDA_FLAG_FP32_COMPUTE);
     const uint32_t paths = d->flags & (KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT);
     if (paths & (paths - 1)) return KDA_ERR_BAD_ARG;  // more than one path flag
     if ((d->flags & KDA_FLAG_FUSED) && f32_path) return KDA_ERR_BAD_ARG;
+    if ((d->flags & KDA_FLAG_BF16_RESIDENT_STATE) && (f32_path || (paths & ~(uint32_t)KDA_FLAG_SPLIT)))
+        return KDA_ERR_BAD_ARG;
     int64_t T_tot, n_c_max;
     const int64_t lim = (int64_t)1 << 30;  // tokens and sequences addressed with int32 on the device
     if (varlen) {
@@ -166,6 +168,7 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     p.st_bf16 = desc->state_dtype == KDA_DTYPE_BF16;
     p.f32_path = s.f32_path;
     p.scalar_gate = sgate;
+    p.bf16_resident = (desc->flags & KDA_FLAG_BF16_RESIDENT_STATE) != 0;
     p.ws = static_cast<char *>(workspace);
     p.lay = lay;
 

@@ -74,6 +74,7 @@ struct Problem {
     int H;
     bool io_bf16, st_bf16, f32_path;
     bool scalar_gate;       // g_raw is [T][H] (one gate per token and head), not [T][H][128]
+    bool bf16_resident;     // bf16 recurrence: state rounded to bf16 between chunk updates
     char *ws;
     WsLayout lay;
 };

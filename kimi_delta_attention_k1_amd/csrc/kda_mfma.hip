@@ -261,7 +261,11 @@ template <int CONS> struct K2Shape {
     static_assert(kSlotKB % producers == 0, "producers split a slot evenly");
 };
 
-template <typename TSt, int CONS>
+// RS: bf16-resident state -- the state is rounded to bf16 when it is loaded and
+// after every chunk's fp32 update, as a design that keeps the on-chip state in bf16
+// between updates would (FlashKDA deep-dive, section 3); it exists to measure that
+// choice against the fp32 state.
+template <typename TSt, int CONS, bool RS>
 __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
     const uint16_t *__restrict__ v, const TSt *s0, TSt *s1, uint16_t *__restrict__ out,
     const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off, int H, int pairs, int64_t n_c_max,
@@ -338,6 +342,10 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
 #pragma unroll
         for (int t = 0; t < 8; ++t) st[t] = ld_state4(s0 + sbase + 16 * t);
     }
+    if constexpr (RS) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) st[t] = round_bf16x4(st[t]);
+    }
     if (nch > 0) bar_sync();
 #pragma unroll 1
     for (int j = 0; j < nch; ++j) {
@@ -407,6 +415,7 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                 const bf16x4 kt = __builtin_bit_cast(bf16x4, hh ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]});
                 const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kUnitBf16.gm + (16 * t + 4 * g) * 4);
                 st[t] = mma32(cat8(kt, kt), e_hl, st[t] * gm);
+                if constexpr (RS) st[t] = round_bf16x4(st[t]);
             }
         }
         bar_sync();  // this chunk's slot may be refilled; chunk j+1 is published
@@ -430,7 +439,7 @@ hipError_t launch_prep_mfma(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename TSt, int CONS>
+template <typename TSt, int CONS, bool RS>
 static hipError_t launch_k2(const Problem &p, hipStream_t s)
 {
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
@@ -438,7 +447,7 @@ static hipError_t launch_k2(const Problem &p, hipStream_t s)
     const int pairs = (int)(p.N * p.H);
     constexpr int groups = 8 / CONS;
     const unsigned grid = groups == 1 ? (unsigned)pairs : (unsigned)((pairs + 7) / 8 * 8 * groups);
-    hipLaunchKernelGGL((k2_mfma<TSt, CONS>), dim3(grid), dim3(K2Shape<CONS>::threads), 0, s, (const uint16_t *)p.v,
+    hipLaunchKernelGGL((k2_mfma<TSt, CONS, RS>), dim3(grid), dim3(K2Shape<CONS>::threads), 0, s, (const uint16_t *)p.v,
                        (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H, pairs, p.n_c_max,
                        (const char *)(p.ws + p.lay.units));
     return hipGetLastError();
@@ -446,19 +455,21 @@ static hipError_t launch_k2(const Problem &p, hipStream_t s)
 
 // Consumer waves per workgroup: the largest that still puts about one
 // workgroup on every one of the 256 compute units.
-template <typename TSt>
+template <typename TSt, bool RS>
 static hipError_t launch_recur_mfma_t(const Problem &p, hipStream_t s)
 {
     const int64_t pairs = p.N * p.H;
-    if (pairs >= 192) return launch_k2<TSt, 8>(p, s);
-    if (pairs >= 96) return launch_k2<TSt, 4>(p, s);
-    if (pairs >= 48) return launch_k2<TSt, 2>(p, s);
-    return launch_k2<TSt, 1>(p, s);
+    if (pairs >= 192) return launch_k2<TSt, 8, RS>(p, s);
+    if (pairs >= 96) return launch_k2<TSt, 4, RS>(p, s);
+    if (pairs >= 48) return launch_k2<TSt, 2, RS>(p, s);
+    return launch_k2<TSt, 1, RS>(p, s);
 }
 
 hipError_t launch_recur_mfma(const Problem &p, hipStream_t s)
 {
-    return p.st_bf16 ? launch_recur_mfma_t<uint16_t>(p, s) : launch_recur_mfma_t<float>(p, s);
+    if (p.bf16_resident)
+        return p.st_bf16 ? launch_recur_mfma_t<uint16_t, true>(p, s) : launch_recur_mfma_t<float, true>(p, s);
+    return p.st_bf16 ? launch_recur_mfma_t<uint16_t, false>(p, s) : launch_recur_mfma_t<float, false>(p, s);
 }
 
 }  // namespace kda

@@ -57,6 +57,14 @@ __device__ __forceinline__ bf16x8 split8(f32x4 x)
     return bf16x8{h[0], h[1], h[2], h[3], l[0], l[1], l[2], l[3]};
 }
 
+// each element rounded to the nearest bf16 (ties to even), kept as fp32
+__device__ __forceinline__ f32x4 round_bf16x4(f32x4 x)
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (float)(__bf16)x[r];
+    return x;
+}
+
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b)
 {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};

@@ -26,7 +26,8 @@ def np64(t: torch.Tensor) -> np.ndarray:
 
 
 def run_gpu(w, dev, *, state_dtype=torch.float32, fp32_compute=False, workspace=None, final=True,
-            initial_state="from_workload", out=None, final_state=None, path="auto", beta=None):
+            initial_state="from_workload", out=None, final_state=None, path="auto", beta=None,
+            bf16_resident_state=False):
     """Run workload w on the GPU; returns (out [T_tot,H,128] tensor, final_state tensor or None).
     `path` selects the kernels ("auto", "split", "fused"); `beta` replaces the
     device copy of beta_raw (same shape and values, e.g. at an odd address)."""
@@ -40,7 +41,7 @@ def run_gpu(w, dev, *, state_dtype=torch.float32, fp32_compute=False, workspace=
         cu = w.cu_seqlens().to(dev)
         o, s = kda.fwd(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, output_final_state=final,
                        cu_seqlens=cu, fp32_compute=fp32_compute, workspace=workspace, out=out,
-                       final_state=final_state, path=path)
+                       final_state=final_state, path=path, bf16_resident_state=bf16_resident_state)
     else:
         B, T = w.N, w.seq_lens[0]
         shp = (B, T, w.H, 128)
@@ -48,7 +49,8 @@ def run_gpu(w, dev, *, state_dtype=torch.float32, fp32_compute=False, workspace=
         o, s = kda.fwd(q.view(shp), k.view(shp), v.view(shp), g.view(gshp), b.view(B, T, w.H),
                        lower_bound=w.lower_bound, initial_state=s0, output_final_state=final,
                        fp32_compute=fp32_compute, workspace=workspace,
-                       out=None if out is None else out.view(shp), final_state=final_state, path=path)
+                       out=None if out is None else out.view(shp), final_state=final_state, path=path,
+                       bf16_resident_state=bf16_resident_state)
         o = o.view(B * T, w.H, 128)
     torch.cuda.synchronize(dev)
     return o, s

@@ -133,7 +133,11 @@ def _desc(**kw):
     (dict(lb=float("nan")), BAD_ARG),
     (dict(desc=dict(scale=0.0)), BAD_ARG),
     (dict(desc=dict(scale=float("inf"))), BAD_ARG),
-    (dict(desc=dict(flags=32)), BAD_ARG),                    # unknown flag bit
+    (dict(desc=dict(flags=64)), BAD_ARG),                    # unknown flag bit
+    (dict(desc=dict(flags=kda.FLAG_BF16_RESIDENT_STATE | kda.FLAG_FUSED)), BAD_ARG),
+    (dict(desc=dict(flags=kda.FLAG_BF16_RESIDENT_STATE | kda.FLAG_RECURRENT)), BAD_ARG),
+    (dict(desc=dict(flags=kda.FLAG_BF16_RESIDENT_STATE | kda.FLAG_FP32_COMPUTE)), BAD_ARG),
+    (dict(desc=dict(io_dtype=1, flags=kda.FLAG_BF16_RESIDENT_STATE)), BAD_ARG),
     (dict(desc=dict(flags=kda.FLAG_RECURRENT | kda.FLAG_FUSED)), BAD_ARG),
     (dict(desc=dict(flags=kda.FLAG_RECURRENT | kda.FLAG_SPLIT)), BAD_ARG),
     (dict(desc=dict(flags=kda.FLAG_SPLIT | kda.FLAG_FUSED)), BAD_ARG),

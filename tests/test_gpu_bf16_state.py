@@ -1,0 +1,81 @@
+"""bf16 states (FlashKDA deep-dive, section 3; DocSearch "flash_kda.fwd API
+reference": states may be bf16): in-place streaming with bf16 state I/O on
+every path, and the bf16-resident recurrence (KDA_FLAG_BF16_RESIDENT_STATE),
+which rounds the state to bf16 after every chunk update, measured against the
+fp32-resident recurrence on the same inputs.
+
+Measured on MI355X (error / tolerance on the final state, T = 8192, H = 4):
+the bf16-resident state costs 1.5-2x more state error than the fp32 state but
+stays inside the bound while the gate decays (lower_bound <= -0.2); with no
+decay (lower_bound = 0) it leaves the bound while the fp32 state does not.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_k1_amd as kda
+from kimi_delta_attention_k1_amd import workloads
+from tests.gpu_helpers import bf16_tol, compare, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _banner(name):
+    print(f"\n[case] bf16 state: {name}", flush=True)
+
+
+def _state_ratio(w, s, ref):
+    tol = bf16_tol(np.concatenate([r[1].reshape(-1) for r in ref.values()]))
+    sg = s.float().cpu()
+    return max(float(np.abs(sg[n, h].numpy() - r[1]).max()) for (n, h), r in ref.items()) / tol
+
+
+@pytest.mark.parametrize("lb", [-5.0, -1.0])
+def test_bf16_resident_within_bound_when_the_gate_decays(gpu, lb):
+    _banner(f"bf16-resident recurrence, T=8192, H=4, lower_bound {lb}")
+    w = workloads.make([8192], 4, seed=71, init_std=0.02, lower_bound=lb)
+    ref = run_oracle(w, threads=4)
+    o, s = run_gpu(w, gpu, bf16_resident_state=True)
+    _, s32 = run_gpu(w, gpu, path="split")
+    print(f"lb={lb}: state err/tol fp32-resident {_state_ratio(w, s32, ref):.3f}, "
+          f"bf16-resident {_state_ratio(w, s, ref):.3f}", flush=True)
+    compare(w, o, s, ref, bf16_tol, f"bf16-resident lb={lb}")
+
+
+def test_bf16_resident_leaves_the_bound_without_decay(gpu):
+    """lower_bound = 0 (no forgetting, DeltaNet): 512 chunk roundings of the state
+    accumulate; the fp32-resident state keeps its error inside the bound."""
+    _banner("bf16-resident vs fp32-resident recurrence, T=8192, H=4, lower_bound 0")
+    w = workloads.make([8192], 4, seed=71, init_std=0.02, lower_bound=0.0)
+    ref = run_oracle(w, threads=4)
+    o32, s32 = run_gpu(w, gpu, path="split")
+    compare(w, o32, s32, ref, bf16_tol, "fp32-resident lb=0")
+    _, s16 = run_gpu(w, gpu, bf16_resident_state=True)
+    r32, r16 = _state_ratio(w, s32, ref), _state_ratio(w, s16, ref)
+    print(f"lb=0: state err/tol fp32-resident {r32:.3f}, bf16-resident {r16:.3f}", flush=True)
+    assert r16 > 2.0 * r32
+    assert r16 > 0.8
+
+
+@pytest.mark.parametrize("path", ["split", "fused", "recurrent"])
+def test_streaming_bf16_state_in_place(gpu, path):
+    """2048 tokens fed as 8 calls of 256, the bf16 state updated in place; the
+    result is compared with the oracle on the whole sequence (so the state is
+    rounded to bf16 seven extra times)."""
+    _banner(f"8 x 256-token calls, bf16 state in place, {path}")
+    T, H, n_calls = 2048, 2, 8
+    w = workloads.make([T], H, seed=72, init_std=0.05)
+    w.initial_state = w.initial_state.to(torch.bfloat16).to(torch.float32)  # exact in bf16
+    ref = run_oracle(w)
+    state = w.initial_state.to(gpu, torch.bfloat16).contiguous()
+    step = T // n_calls
+    cu = torch.tensor([0, step], dtype=torch.int32, device=gpu)
+    outs = []
+    for i in range(n_calls):
+        sl = lambda x: x[i * step:(i + 1) * step].to(gpu).contiguous()  # noqa: E731
+        o, s = kda.fwd(sl(w.q), sl(w.k), sl(w.v), sl(w.g_raw), sl(w.beta_raw), lower_bound=w.lower_bound,
+                       initial_state=state, final_state=state, cu_seqlens=cu, path=path)
+        assert s.data_ptr() == state.data_ptr() and s.dtype == torch.bfloat16
+        outs.append(o)
+    torch.cuda.synchronize()
+    compare(w, torch.cat(outs), state, ref, bf16_tol, f"bf16 state streamed {path}")
