@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                     if (m == 0) reinterpret_cast<float *>(X + kXBeta)[t] = beta;
                 }
                 // decays relative to token 7 (each factor within e^{8|lb|}); K_end via token 15
-                bf16x8 kr_h, ki_h, ki_l, qr_h, qr_l;
+                bf16x8 kr_h, ki_h, qr_h;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float gref = row_bcast<7>(gf[i]);
@@ -307,9 +307,7 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                     const float kr = kf[i] * up, ki = kf[i] * dn, qr = qf[i] * up;
                     kr_h[i] = (__bf16)kr;
                     ki_h[i] = (__bf16)ki;
-                    ki_l[i] = (__bf16)(ki - (float)ki_h[i]);
                     qr_h[i] = (__bf16)qr;
-                    qr_l[i] = (__bf16)(qr - (float)qr_h[i]);
                     // raw K_end = k e^{G_last - G}: consumer fragment (tile pair m), lane
                     // (kc + 16 (t/4)), element (t%4) + 4 hi, channel 32m + 16 hi + kc
                     const int cr = 8 * sg + i, kc = cr & 15, hi = cr >> 4;
@@ -319,9 +317,7 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 const f32x4 dR = mma32(kr_h, ki_h, z);
                 const f32x4 dRT = mma32(ki_h, kr_h, z);
-                f32x4 dAQT = mma32(ki_h, qr_h, z);
-                dAQT = mma32(ki_l, qr_h, dAQT);
-                dAQT = mma32(ki_h, qr_l, dAQT);
+                const f32x4 dAQT = mma32(ki_h, qr_h, z);
                 reinterpret_cast<f32x4 *>(X + m * kXWave + kXR)[lane] = dR;
                 reinterpret_cast<f32x4 *>(X + m * kXWave + kXRT)[lane] = dRT;
                 reinterpret_cast<f32x4 *>(X + m * kXWave + kXAQ)[lane] = dAQT;
@@ -421,11 +417,11 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                     xq[u][r] *= rq4[r];
                 }
                 bf16x4 eb_h, eb_l, e_h, e_l;
-                split4(eb, eb_h, eb_l);
+                split4t(eb, eb_h, eb_l);
                 f32x4 E = {0.f, 0.f, 0.f, 0.f};  // E' = Diag(rk) E
                 E = mma32(ab, cat8(eb_h, eb_h), E);
                 E = mma16(ab_h, eb_l, E);
-                split4(E, e_h, e_l);
+                split4t(E, e_h, e_l);
                 e_hl[u] = cat8(e_h, e_l);
                 f32x4 O = mma32(aq, cat8(e_h, e_h), xq[u]);
                 O = mma16(aq_h, e_l, O);

@@ -48,6 +48,18 @@ __device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo)
     }
 }
 
+// x = hi + lo with hi = x truncated to bf16 (its top 16 bits) and lo = x - hi (exact
+// in fp32) rounded to bf16: about 16 significant bits, one op per element cheaper
+__device__ __forceinline__ void split4t(f32x4 x, bf16x4 &hi, bf16x4 &lo)
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t u = __float_as_uint(x[r]);
+        hi[r] = __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));
+        lo[r] = (__bf16)(x[r] - __uint_as_float(u & 0xffff0000u));
+    }
+}
+
 // {hi[0..3], lo[0..3]} with x = hi + lo: one 16x16x32 A operand that carries
 // both halves of a split 16x16 tile (its first half alone is the hi tile)
 __device__ __forceinline__ bf16x8 split8(f32x4 x)
