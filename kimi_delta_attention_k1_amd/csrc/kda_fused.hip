@@ -134,15 +134,17 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                         R[r] = (tok < a) ? beta_a[r] * rka * rkb * Rs[r] : 0.f;
                         RT[r] = (a < tok) ? beta_b * rkb * rka * RTs[r] : 0.f;
                     }
-                    // (A^kk)^T = (I + R^T)^-1 = (I-M)(I+M^2)(I+M^4)(I+M^8), M = R^T
-                    const f32x4 M2 = mm16_f32(R, RT);
-                    const f32x4 M2T = mm16_f32(RT, R);
-                    const f32x4 M4 = mm16_f32(M2T, M2);
-                    const f32x4 M4T = mm16_f32(M2, M2T);
-                    const f32x4 M8T = mm16_f32(M4, M4T);
-                    const f32x4 P1 = mm16_f32(eye_plus(R, -1.f, g, tok), eye_plus(M2, 1.f, g, tok));
-                    const f32x4 P2 = mm16_f32(eye_plus(M4T, 1.f, g, tok), P1);
-                    const f32x4 AT = mm16_f32(eye_plus(M8T, 1.f, g, tok), P2);
+                    // (A^kk)^T = (I + R^T)^-1 = (I-M)(I+M^2)(I+M^4)(I+M^8), M = R^T, with fp16
+                    // operands and fp32 accumulation: the inverse's entries are bounded by 1
+                    // in magnitude (FlashKDA deep-dive, section 3), so fp16's range suffices
+                    const f32x4 M2 = mm16_h(R, RT);
+                    const f32x4 M2T = mm16_h(RT, R);
+                    const f32x4 M4 = mm16_h(M2T, M2);
+                    const f32x4 M4T = mm16_h(M2, M2T);
+                    const f32x4 M8T = mm16_h(M4, M4T);
+                    const f32x4 P1 = mm16_h(eye_plus(R, -1.f, g, tok), eye_plus(M2, 1.f, g, tok));
+                    const f32x4 P2 = mm16_h(eye_plus(M4T, 1.f, g, tok), P1);
+                    const f32x4 AT = mm16_h(eye_plus(M8T, 1.f, g, tok), P2);
                     f32x4 ABT;  // rk_b beta_a A^kk[b][a]: E' = Diag(rk) A^kk Diag(beta) Ebar
 #pragma unroll
                     for (int r = 0; r < 4; ++r) ABT[r] = rkb * beta_a[r] * AT[r];

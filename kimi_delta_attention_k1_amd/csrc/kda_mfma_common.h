@@ -123,6 +123,17 @@ __device__ __forceinline__ f32x4 mm16_bf(f32x4 xt, f32x4 y)
     return mma16(xh, yl, acc);
 }
 
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+// C = X Y for 16x16 tiles with fp16 operands and fp32 accumulation; xt holds X^T and
+// y holds Y in D layout (the 16x16x16 operand layout of both)
+__device__ __forceinline__ f32x4 mm16_h(f32x4 xt, f32x4 y)
+{
+    const f16x4 a = {(_Float16)xt[0], (_Float16)xt[1], (_Float16)xt[2], (_Float16)xt[3]};
+    const f16x4 b = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, z, 0, 0, 0);
+}
+
 // I + a*X in D layout (row 4g+r, column tok)
 __device__ __forceinline__ f32x4 eye_plus(f32x4 x, float a, int g, int tok)
 {
