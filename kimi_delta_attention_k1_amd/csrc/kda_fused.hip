@@ -403,9 +403,9 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
             const f32x4 rq4 = *reinterpret_cast<const f32x4 *>(L + kPSC + 64 + 16 * g);
             const bf16x8 ab = *reinterpret_cast<const bf16x8 *>(L + kPAB + lane * 16);
             const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(L + kPAQ + lane * 16);
-            const bf16x4 ab_h = {ab[0], ab[1], ab[2], ab[3]};
-            const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]};
-            bf16x8 e_hl[2];
+            const bf16x4 ab_h = {ab[0], ab[1], ab[2], ab[3]}, ab_l = {ab[4], ab[5], ab[6], ab[7]};
+            const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]}, aq_l = {aq[4], aq[5], aq[6], aq[7]};
+            bf16x4 eh[2], el[2];
             const int64_t rstride = (int64_t)H * kD;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -419,13 +419,16 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                     xq[u][r] *= rq4[r];
                 }
                 bf16x4 eb_h, eb_l, e_h, e_l;
-                split4t(eb, eb_h, eb_l);
-                f32x4 E = {0.f, 0.f, 0.f, 0.f};  // E' = Diag(rk) E
-                E = mma32(ab, cat8(eb_h, eb_h), E);
+                split4t_packed(eb, eb_h, eb_l);
+                f32x4 E = {0.f, 0.f, 0.f, 0.f};  // E' = Diag(rk) E: A_h eb_h + A_l eb_h + A_h eb_l
+                E = mma16(ab_h, eb_h, E);
+                E = mma16(ab_l, eb_h, E);
                 E = mma16(ab_h, eb_l, E);
-                split4t(E, e_h, e_l);
-                e_hl[u] = cat8(e_h, e_l);
-                f32x4 O = mma32(aq, cat8(e_h, e_h), xq[u]);
+                split4t_packed(E, e_h, e_l);
+                eh[u] = e_h;
+                el[u] = e_l;
+                f32x4 O = mma16(aq_h, e_h, xq[u]);
+                O = mma16(aq_l, e_h, O);
                 O = mma16(aq_h, e_l, O);
                 uint16_t *orow = out + ((int64_t)(t0 + 4 * g) * H + h) * kD + vcol;
                 if (len == kC) {
@@ -447,7 +450,7 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                     const bf16x4 kt = __builtin_bit_cast(bf16x4, hh ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]});
                     const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kPGM + (16 * t + 4 * g) * 4);
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) st[u][t] = mma32(cat8(kt, kt), e_hl[u], st[u][t] * gm);
+                    for (int u = 0; u < 2; ++u) st[u][t] = mma16(kt, el[u], mma16(kt, eh[u], st[u][t] * gm));
                 }
             }
         }

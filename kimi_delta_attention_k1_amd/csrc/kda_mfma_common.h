@@ -60,6 +60,21 @@ __device__ __forceinline__ void split4t(f32x4 x, bf16x4 &hi, bf16x4 &lo)
     }
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// truncating split of four values into packed bf16 pairs: hi = {x0|x1, x2|x3} (top 16
+// bits, one byte permute per pair), lo = the exact fp32 remainders, rounded pairwise
+__device__ __forceinline__ void split4t_packed(f32x4 x, bf16x4 &hi, bf16x4 &lo)
+{
+    const u32x4 u = __builtin_bit_cast(u32x4, x);
+    const u32x2 h = {__builtin_amdgcn_perm(u[1], u[0], 0x07060302u), __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
+    const f32x2 r01 = {x[0] - __uint_as_float(u[0] & 0xffff0000u), x[1] - __uint_as_float(u[1] & 0xffff0000u)};
+    const f32x2 r23 = {x[2] - __uint_as_float(u[2] & 0xffff0000u), x[3] - __uint_as_float(u[3] & 0xffff0000u)};
+    const bf16x2 l01 = __builtin_convertvector(r01, bf16x2), l23 = __builtin_convertvector(r23, bf16x2);
+    hi = __builtin_bit_cast(bf16x4, h);
+    lo = bf16x4{l01[0], l01[1], l23[0], l23[1]};
+}
+
 // {hi[0..3], lo[0..3]} with x = hi + lo: one 16x16x32 A operand that carries
 // both halves of a split 16x16 tile (its first half alone is the hi tile)
 __device__ __forceinline__ bf16x8 split8(f32x4 x)
