@@ -72,6 +72,16 @@ __device__ __forceinline__ int swz(int L) { return L ^ ((L >> 3) & 7); }
 // barrier that first completes this wave's own LDS traffic (not its global loads)
 __device__ __forceinline__ void tick_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// sum over the four lanes l with equal l % 16: two cross-row swaps (rows of 16 lanes),
+// no LDS round trip
+__device__ __forceinline__ float sum_rows4(float x)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // SG: scalar gate, g_raw is [T][H] and its one value per token and head applies to
 // every key channel (Gated DeltaNet, Doubleword section 3)
 template <typename TSt, bool SG>
@@ -258,10 +268,13 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                 if constexpr (SG) {  // one gate and one prefix sum serve every channel
                     const bool ghi = (reinterpret_cast<uintptr_t>(gb8 + eo) & 2) != 0;
                     float x = vmask * lb2 * sigmoid_fast(ghi ? bf_hi(ga[0]) : bf_lo(ga[0]));
+                    // rounded exactly as the per-channel gate below, step by step
+                    asm("" : "+v"(x));
                     x += row_shr<1>(x);
                     x += row_shr<2>(x);
                     x += row_shr<4>(x);
                     x += row_shr<8>(x);
+                    asm("" : "+v"(x));
 #pragma unroll
                     for (int i = 0; i < 8; ++i) gf[i] = x;
                 } else {
@@ -273,10 +286,14 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {  // gate (log2 units) and prefix sum over tokens
                         float x = vmask * lb2 * sigmoid_fast(gf[i]);
+                        // the empty asm statements keep x as computed, so each shifted add
+                        // below becomes a single DPP add
+                        asm("" : "+v"(x));
                         x += row_shr<1>(x);
                         x += row_shr<2>(x);
                         x += row_shr<4>(x);
                         x += row_shr<8>(x);
+                        asm("" : "+v"(x));
                         gf[i] = x;
                     }
                 }
@@ -286,10 +303,8 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                     nq += qf[i] * qf[i];
                     nk += kf[i] * kf[i];
                 }
-                nq += __shfl_xor(nq, 16);
-                nq += __shfl_xor(nq, 32);
-                nk += __shfl_xor(nk, 16);
-                nk += __shfl_xor(nk, 32);
+                nq = sum_rows4(nq);
+                nk = sum_rows4(nk);
 
                 char *X = parts + (c & 1) * kXBytes;
                 char *P = slots + (c % kFSlots) * kPBytes;
@@ -300,6 +315,7 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                 }
                 // decays relative to token 7 (each factor within e^{8|lb|}); K_end via token 15
                 bf16x8 kr_h, ki_h, qr_h;
+                float ke[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float gref = row_bcast<7>(gf[i]);
@@ -310,11 +326,20 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                     kr_h[i] = (__bf16)kr;
                     ki_h[i] = (__bf16)ki;
                     qr_h[i] = (__bf16)qr;
-                    // raw K_end = k e^{G_last - G}: consumer fragment (tile pair m), lane
-                    // (kc + 16 (t/4)), element (t%4) + 4 hi, channel 32m + 16 hi + kc
-                    const int cr = 8 * sg + i, kc = cr & 15, hi = cr >> 4;
-                    *reinterpret_cast<__bf16 *>(P + kPKE + m * 1024 + swz(kc + 16 * (t >> 2)) * 16 +
-                                                ((t & 3) + 4 * hi) * 2) = (__bf16)(ki * cl);
+                    ke[i] = ki * cl;
+                }
+                // raw K_end = k e^{G_last - G}: consumer fragment (tile pair m), lane
+                // (kc + 16 (t/4)), element (t%4) + 4 hi, channel 32m + 16 hi + kc; rounded
+                // in pairs, stored as halves
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    const uint32_t pk = pk_bf16(f32x2{ke[i], ke[i + 1]});
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int cr = 8 * sg + i + j, kc = cr & 15, hi = cr >> 4;
+                        *reinterpret_cast<uint16_t *>(P + kPKE + m * 1024 + swz(kc + 16 * (t >> 2)) * 16 +
+                                                      ((t & 3) + 4 * hi) * 2) = (uint16_t)(pk >> (16 * j));
+                    }
                 }
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 const f32x4 dR = mma32(kr_h, ki_h, z);
@@ -431,13 +456,16 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                 O = mma16(aq_l, e_h, O);
                 O = mma16(aq_h, e_l, O);
                 uint16_t *orow = out + ((int64_t)(t0 + 4 * g) * H + h) * kD + vcol;
+                const u32x2 ob = {pk_bf16(f32x2{O[0], O[1]}), pk_bf16(f32x2{O[2], O[3]})};
+                const uint16_t o4[4] = {(uint16_t)ob[0], (uint16_t)(ob[0] >> 16), (uint16_t)ob[1],
+                                        (uint16_t)(ob[1] >> 16)};
                 if (len == kC) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) orow[r * rstride] = __builtin_bit_cast(uint16_t, (__bf16)O[r]);
+                    for (int r = 0; r < 4; ++r) orow[r * rstride] = o4[r];
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (4 * g + r < len) orow[r * rstride] = __builtin_bit_cast(uint16_t, (__bf16)O[r]);
+                        if (4 * g + r < len) orow[r * rstride] = o4[r];
                 }
             }
             // S^T <- Diag(gamma) S^T + K_end^T E'

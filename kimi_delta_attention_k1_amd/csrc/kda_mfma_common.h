@@ -62,6 +62,12 @@ __device__ __forceinline__ void split4t(f32x4 x, bf16x4 &hi, bf16x4 &lo)
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two values rounded to bf16 (ties to even) as one packed word, x[0] in the low half
+__device__ __forceinline__ uint32_t pk_bf16(f32x2 x)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
 // truncating split of four values into packed bf16 pairs: hi = {x0|x1, x2|x3} (top 16
 // bits, one byte permute per pair), lo = the exact fp32 remainders, rounded pairwise
 __device__ __forceinline__ void split4t_packed(f32x4 x, bf16x4 &hi, bf16x4 &lo)
@@ -70,9 +76,10 @@ __device__ __forceinline__ void split4t_packed(f32x4 x, bf16x4 &hi, bf16x4 &lo)
     const u32x2 h = {__builtin_amdgcn_perm(u[1], u[0], 0x07060302u), __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
     const f32x2 r01 = {x[0] - __uint_as_float(u[0] & 0xffff0000u), x[1] - __uint_as_float(u[1] & 0xffff0000u)};
     const f32x2 r23 = {x[2] - __uint_as_float(u[2] & 0xffff0000u), x[3] - __uint_as_float(u[3] & 0xffff0000u)};
-    const bf16x2 l01 = __builtin_convertvector(r01, bf16x2), l23 = __builtin_convertvector(r23, bf16x2);
+    // each remainder pair is converted and kept as one packed word (one conversion per pair)
+    const u32x2 l = {pk_bf16(r01), pk_bf16(r23)};
     hi = __builtin_bit_cast(bf16x4, h);
-    lo = bf16x4{l01[0], l01[1], l23[0], l23[1]};
+    lo = __builtin_bit_cast(bf16x4, l);
 }
 
 // {hi[0..3], lo[0..3]} with x = hi + lo: one 16x16x32 A operand that carries
