@@ -237,28 +237,32 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
 // value channels evolve independently, so consumers never exchange state; they
 // share each chunk's operands through LDS.
 //
-// The producers copy every chunk's 14848-byte workspace unit and its 16 x 256-byte
-// v tile straight from global memory into a ring of kK2Slots LDS slots with
-// 16-byte-per-lane global-to-LDS loads, kK2Slots - 1 chunks ahead, and wait
-// with explicit counts of their own loads. One workgroup barrier per chunk
-// publishes a slot and recycles the previous one. The barrier is a bare
-// s_barrier: a fenced barrier would drain the prefetch queue every chunk.
+// The producers copy every chunk's 14848-byte workspace unit and the v rows of the
+// workgroup's value columns straight from global memory into a ring of LDS slots
+// with 16-byte-per-lane global-to-LDS loads, several chunks ahead, and wait with
+// explicit counts of their own loads. One workgroup barrier per chunk publishes a
+// slot and recycles the previous one. The barrier is a bare s_barrier: a fenced
+// barrier would drain the prefetch queue every chunk.
 // ---------------------------------------------------------------------------
-constexpr int kK2Slots = 6;
-constexpr int kSlotKB = 20;                        // 1 KB copy instructions per chunk
-constexpr int kSlotBytes = kSlotKB * 1024;         // unit 14848 | pad 512 | v 4096 | pad 1024
-constexpr int kVOff = 15 * 1024;                   // v tile offset inside a slot
-static_assert(kUnitBf16.bytes <= (size_t)kVOff, "unit must fit below the v tile");
+constexpr int kVOff = 15 * 1024;  // v rows offset inside a slot
+static_assert(kUnitBf16.bytes <= (size_t)kVOff, "unit must fit below the v rows");
 
 // Workgroup shape for CONS consumer waves (8 / CONS workgroups per (sequence, head)).
+// A slot holds the unit and the v rows of the workgroup's 16 CONS value columns
+// (32 CONS bytes per token row, at least 1 KB). Small workgroups, which run when few
+// (sequence, head) pairs share the chip, get four producer waves: the global-to-LDS
+// copy rate of one wave, not memory latency, bounds their chunk rate.
 template <int CONS> struct K2Shape {
-    static constexpr int producers = CONS >= 4 ? 2 : 1;
-    static constexpr int slots = producers == 2 ? kK2Slots : 5;
+    static constexpr int producers = CONS >= 4 ? 2 : 4;
+    static constexpr int v_kb = CONS >= 2 ? CONS / 2 : 1;
+    static constexpr int slot_kb = (kVOff / 1024 + v_kb + producers - 1) / producers * producers;
+    static constexpr int slot_bytes = slot_kb * 1024;
+    static constexpr int slots = producers == 2 ? 6 : 8;
     static constexpr int threads = 64 * (CONS + producers);
-    static constexpr int kb_per_producer = kSlotKB / producers;
+    static constexpr int kb_per_producer = slot_kb / producers;
     static constexpr int pending = (slots - 2) * kb_per_producer;  // loads allowed in flight
     static_assert(pending <= 63, "vmcnt holds at most 63 outstanding loads");
-    static_assert(kSlotKB % producers == 0, "producers split a slot evenly");
+    static_assert(slots * slot_bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
 
 // RS: bf16-resident state -- the state is rounded to bf16 when it is loaded and
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
 {
     using Sh = K2Shape<CONS>;
     constexpr int kGroups = 8 / CONS;  // workgroups per (sequence, head)
-    __shared__ __attribute__((aligned(1024))) char lds[Sh::slots][kSlotBytes];
+    __shared__ __attribute__((aligned(1024))) char lds[Sh::slots][Sh::slot_bytes];
     // the wave index is uniform over the wave: keep it scalar so role branches and
     // the address arithmetic built on it stay in scalar registers
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -308,10 +312,14 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                 if (b < kVOff / 1024) {
                     const int off = b * 1024 + lane * 16;
                     src = u + (off < (int)kUnitBf16.bytes ? off : 0);
-                } else if (b < kVOff / 1024 + 4) {
-                    const int r = 4 * (b - kVOff / 1024) + (lane >> 4);
+                } else if (b < kVOff / 1024 + Sh::v_kb) {
+                    // 16-byte piece `seg` of the v rows: token row seg / (2 CONS), columns
+                    // 16 wbase + 8 (seg % (2 CONS)) ..; a 1 KB region wider than the rows
+                    // (CONS = 1) repeats them
+                    const int seg = (b - kVOff / 1024) * 64 + lane;
+                    const int r = (seg / (2 * CONS)) & 15;
                     const int row = min(tb + j * kC + r, te - 1);
-                    src = vb + (((int64_t)row * H + h) * kD) * 2 + (lane & 15) * 16;
+                    src = vb + (((int64_t)row * H + h) * kD + 16 * wbase + 8 * (seg % (2 * CONS))) * 2;
                 } else {
                     src = u;  // filler: keeps every producer at the same load count
                 }
@@ -376,7 +384,8 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tr = 4 * g + r;
-            const uint16_t vr = *reinterpret_cast<const uint16_t *>(L + kVOff + tr * 256 + vcol * 2);
+            const uint16_t vr =
+                *reinterpret_cast<const uint16_t *>(L + kVOff + tr * (32 * CONS) + (vcol - 16 * wbase) * 2);
             eb[r] = (tr < len ? bf16_bits_to_f32(vr) : 0.f) - xk[r];
         }
         // A operands arrive as {hi, lo}: [hi | lo] x [x_hi ; x_hi] + hi x x_lo is the
