@@ -232,7 +232,7 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
 
 // ---------------------------------------------------------------------------
 // K2: one workgroup per (sequence, head): 8 consumer waves, wave w owning value
-// channels [16w, 16w+16), and 2 producer waves. Lane l of a consumer holds
+// channels [16w, 16w+16), and 2 producer waves (fewer pairs: see K2Shape). Lane l of a consumer holds
 // S^T[16t + 4g + r][16w + l%16] in accumulator tile t (t = 0..7, r = 0..3). The
 // value channels evolve independently, so consumers never exchange state; they
 // share each chunk's operands through LDS.
@@ -253,16 +253,24 @@ static_assert(kUnitBf16.bytes <= (size_t)kVOff, "unit must fit below the v rows"
 // (sequence, head) pairs share the chip, get four producer waves: the global-to-LDS
 // copy rate of one wave, not memory latency, bounds their chunk rate.
 template <int CONS> struct K2Shape {
+    // Up to four recurrence waves get an output wave each, which forms the outputs one
+    // chunk behind on its own copy of the state, off the recurrence's critical path.
+    static constexpr bool split_out = CONS <= 4;
+    static constexpr int consumers = split_out ? 2 * CONS : CONS;
     static constexpr int producers = CONS >= 4 ? 2 : 4;
     static constexpr int v_kb = CONS >= 2 ? CONS / 2 : 1;
     static constexpr int slot_kb = (kVOff / 1024 + v_kb + producers - 1) / producers * producers;
     static constexpr int slot_bytes = slot_kb * 1024;
     static constexpr int slots = producers == 2 ? 6 : 8;
-    static constexpr int threads = 64 * (CONS + producers);
+    static constexpr int threads = 64 * (consumers + producers);
     static constexpr int kb_per_producer = slot_kb / producers;
-    static constexpr int pending = (slots - 2) * kb_per_producer;  // loads allowed in flight
+    // chunks copied ahead of the recurrence: an output wave still reads the slot
+    // of the previous chunk
+    static constexpr int ahead = split_out ? slots - 2 : slots - 1;
+    static constexpr int pending = (ahead - 1) * kb_per_producer;  // loads allowed in flight
     static_assert(pending <= 63, "vmcnt holds at most 63 outstanding loads");
-    static_assert(slots * slot_bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    static constexpr int ebuf_bytes = split_out ? 2 * CONS * 1024 : 0;
+    static_assert(slots * slot_bytes + ebuf_bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
 
 // RS: bf16-resident state -- the state is rounded to bf16 when it is loaded and
@@ -278,6 +286,9 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
     using Sh = K2Shape<CONS>;
     constexpr int kGroups = 8 / CONS;  // workgroups per (sequence, head)
     __shared__ __attribute__((aligned(1024))) char lds[Sh::slots][Sh::slot_bytes];
+    // E of each recurrence wave's chunk for its output wave (fp32, D layout; the output
+    // wave splits it the same way), alternating by chunk parity
+    __shared__ f32x4 ebuf[Sh::split_out ? 2 : 1][CONS][64];
     // the wave index is uniform over the wave: keep it scalar so role branches and
     // the address arithmetic built on it stay in scalar registers
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -294,10 +305,10 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
     const int c0 = chunk_off[n], nch = chunk_off[n + 1] - c0;
     const int tb = tok_off[n], te = tok_off[n + 1];
 
-    if (w >= CONS) {
+    if (w >= Sh::consumers) {
         // ------------------------------------------------------------ producers
         if (nch == 0) return;  // uniform over the workgroup: nobody enters the barriers
-        const int pw = w - CONS;
+        const int pw = w - Sh::consumers;
         constexpr int kKBPerProducer = Sh::kb_per_producer;
         constexpr int kProdPending = Sh::pending;
         const char *ubase = units + ((int64_t)h * n_c_max + c0) * kUnitBf16.bytes;
@@ -327,12 +338,12 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
             }
         };
 #pragma unroll
-        for (int s = 0; s < Sh::slots - 1; ++s) copy_chunk(s, s);
+        for (int s = 0; s < Sh::ahead; ++s) copy_chunk(s, s);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kProdPending) : "memory");  // chunk 0 landed
         bar_sync();
 #pragma unroll 1
         for (int j = 0; j < nch; ++j) {
-            copy_chunk(j + Sh::slots - 1, (j + Sh::slots - 1) % Sh::slots);
+            copy_chunk(j + Sh::ahead, (j + Sh::ahead) % Sh::slots);
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kProdPending) : "memory");  // chunk j+1 landed
             bar_sync();
         }
@@ -341,7 +352,9 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
     }
 
     // ---------------------------------------------------------------- consumers
-    const int g = lane >> 4, vcol = 16 * (wbase + w) + (lane & 15);
+    const bool out_wave = Sh::split_out && w >= CONS;
+    const int wc = out_wave ? w - CONS : w;  // value-column tile within the workgroup
+    const int g = lane >> 4, vcol = 16 * (wbase + wc) + (lane & 15);
     const int64_t sbase = (((int64_t)n * H + h) * kD + vcol) * kD + 4 * g;
     f32x4 st[8];
 #pragma unroll
@@ -355,6 +368,122 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
         for (int t = 0; t < 8; ++t) st[t] = round_bf16x4(st[t]);
     }
     if (nch > 0) bar_sync();
+    if constexpr (Sh::split_out) {
+        // state -> bf16 B operands (tiles 2p, 2p+1 form k step p)
+        auto cast_state = [&](bf16x8(&sb)[4]) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sb[p][r] = (__bf16)st[2 * p][r];
+                    sb[p][4 + r] = (__bf16)st[2 * p + 1][r];
+                }
+            }
+        };
+        // S^T <- Diag(gamma) S^T + K_end^T (E_hi + E_lo): [K_end | K_end] x [E_hi ; E_lo]
+        auto update = [&](const char *L, bf16x8 e_hl) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const u32x4 kq = *reinterpret_cast<const u32x4 *>(L + kUnitBf16.ke + p * 1024 + lane * 16);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int t = 2 * p + hh;
+                    const bf16x4 kt = __builtin_bit_cast(bf16x4, hh ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]});
+                    const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kUnitBf16.gm + (16 * t + 4 * g) * 4);
+                    st[t] = mma32(cat8(kt, kt), e_hl, st[t] * gm);
+                    if constexpr (RS) st[t] = round_bf16x4(st[t]);
+                }
+            }
+        };
+        if (!out_wave) {
+            // ------------------------------------------------ recurrence wave
+#pragma unroll 1
+            for (int j = 0; j < nch; ++j) {
+                const char *L = lds[j % Sh::slots];
+                const int t0 = tb + j * kC;
+                const int len = min(kC, te - t0);
+                bf16x8 sb[4];
+                cast_state(sb);
+                f32x4 xk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const bf16x8 kb = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.kb + p * 1024 + lane * 16);
+                    xk = mma32(kb, sb[p], xk);
+                }
+                // Ebar = V - K_b S^T ; E = (A^kk Diag(beta)) Ebar with split operands
+                f32x4 eb;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tr = 4 * g + r;
+                    const uint16_t vr =
+                        *reinterpret_cast<const uint16_t *>(L + kVOff + tr * (32 * CONS) + (vcol - 16 * wbase) * 2);
+                    eb[r] = (tr < len ? bf16_bits_to_f32(vr) : 0.f) - xk[r];
+                }
+                bf16x4 eb_h, eb_l, e_h, e_l;
+                split4(eb, eb_h, eb_l);
+                const bf16x8 ab = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.ab + lane * 16);
+                const bf16x4 ab_h = {ab[0], ab[1], ab[2], ab[3]};
+                f32x4 E = {0.f, 0.f, 0.f, 0.f};
+                E = mma32(ab, cat8(eb_h, eb_h), E);
+                E = mma16(ab_h, eb_l, E);
+                split4(E, e_h, e_l);
+                const bf16x8 e_hl = cat8(e_h, e_l);
+                ebuf[j & 1][wc][lane] = E;
+                update(L, e_hl);
+                // the E tile is in LDS before the barrier publishes it
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                bar_sync();
+            }
+            if (s1) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) st_state4(s1 + sbase + 16 * t, st[t]);
+            }
+        } else {
+            // ---------------------------------------------------- output wave
+            // chunk c's outputs from the state before chunk c and the E tile its
+            // recurrence wave published; then the same state update, so this copy of
+            // the state stays bitwise equal to the recurrence wave's
+            auto out_step = [&](int c, bool upd) {
+                const char *L = lds[c % Sh::slots];
+                const int t0 = tb + c * kC;
+                const int len = min(kC, te - t0);
+                bf16x8 sb[4];
+                cast_state(sb);
+                f32x4 xq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.qb + p * 1024 + lane * 16);
+                    xq = mma32(qb, sb[p], xq);
+                }
+                bf16x4 e_h, e_l;
+                split4(ebuf[c & 1][wc][lane], e_h, e_l);
+                const bf16x8 e_hl = cat8(e_h, e_l);
+                // O = Q_b S^T + A^qk E
+                const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.aq + lane * 16);
+                const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]};
+                f32x4 O = mma32(aq, cat8(e_h, e_h), xq);
+                O = mma16(aq_h, e_l, O);
+                uint16_t *orow = out + ((int64_t)(t0 + 4 * g) * H + h) * kD + vcol;
+                const int64_t rstride = (int64_t)H * kD;
+                if (len == kC) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) orow[r * rstride] = __builtin_bit_cast(uint16_t, (__bf16)O[r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * g + r < len) orow[r * rstride] = __builtin_bit_cast(uint16_t, (__bf16)O[r]);
+                }
+                if (upd) update(L, e_hl);
+            };
+#pragma unroll 1
+            for (int j = 0; j < nch; ++j) {
+                if (j > 0) out_step(j - 1, true);
+                bar_sync();
+            }
+            if (nch > 0) out_step(nch - 1, false);
+        }
+        return;
+    }
 #pragma unroll 1
     for (int j = 0; j < nch; ++j) {
         const char *L = lds[j % Sh::slots];

@@ -282,10 +282,11 @@ def test_k1_intermediates_against_chunked_oracle(gpu):
             chunk += 1
 
 
-@pytest.mark.parametrize("nseq,H", [(12, 6), (30, 4), (50, 4)])
+@pytest.mark.parametrize("nseq,H", [(10, 4), (12, 6), (30, 4), (50, 4)])
 def test_pair_counts_select_each_recurrence_shape(gpu, nseq, H):
-    """(sequence, head) pair counts 72, 120 and 200 run the recurrence with 2, 4 and
-    8 consumer waves per workgroup (4, 2 and 1 workgroups per pair)."""
-    _banner(f"{nseq} sequences x {H} heads = {nseq * H} pairs")
+    """On the two-kernel path, (sequence, head) pair counts 40, 72, 120 and 200 run the
+    recurrence with 1, 2, 4 and 8 consumer waves per workgroup (8, 4, 2 and 1
+    workgroups per pair; four producer waves for the first two, two for the others)."""
+    _banner(f"split path: {nseq} sequences x {H} heads = {nseq * H} pairs")
     w = workloads.make(None, H, seed=41 + nseq, init_std=0.02, lens_drawn=(1, 70, nseq))
-    compare(w, *run_gpu(w, gpu), run_oracle(w), bf16_tol, f"{nseq * H} pairs")
+    compare(w, *run_gpu(w, gpu, path="split"), run_oracle(w), bf16_tol, f"{nseq * H} pairs")
