@@ -3,6 +3,7 @@
     python -m kimi_delta_attention_k1_amd.profsum stats  <kernel_stats.csv> <command...>
     python -m kimi_delta_attention_k1_amd.profsum traffic <fetch_counter_collection.csv>
            <write_counter_collection.csv> <workload> <copy_probe_mib>
+    python -m kimi_delta_attention_k1_amd.profsum util <counter_collection.csv>
 
 `stats` prints a Markdown table of per-kernel call counts and durations.
 `traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into HBM bytes per
@@ -11,6 +12,10 @@ of known size that bench.py --copy-probe-mib runs in the same process
 (the runtime's copy kernel; its last dispatches are the probe). The result is
 merged into profiles/traffic_counters.json, keyed by workload and kernel, with
 the SHA-256 of the kernel's sources so bench.py reports null once they change.
+`util` prints, per kernel, the matrix-core and vector-ALU utilisation from one
+counter pass (SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CU_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16,
+SQ_INSTS_VALU, SQ_ACTIVE_INST_VALU, SQ_INSTS_MFMA, SQ_WAVES, SQ_BUSY_CYCLES,
+GRBM_GUI_ACTIVE), averaged over the kernel's dispatches.
 """
 from __future__ import annotations
 
@@ -93,8 +98,38 @@ def traffic(fetch_csv, write_csv, workload, probe_mib):
     return ent
 
 
+def util(path: str) -> str:
+    """Counter-derived utilisation per kernel. SQ cycle counters are summed over
+    compute units (SQ_BUSY_CU_CYCLES) or SIMDs (SQ_VALU_MFMA_BUSY_CYCLES); a CU has
+    4 SIMDs and SQ_ACTIVE_INST_VALU counts in units of 4 cycles per wave
+    instruction, so both busy fractions divide by 4 x SQ_BUSY_CU_CYCLES.
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 counts 512-flop units of bf16 matrix work."""
+    per = {}
+    for r in csv.DictReader(open(path)):
+        k = short_name(r["Kernel_Name"])
+        per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = ["| kernel | dispatches | CU busy cycles | MFMA busy | VALU busy | VALU instr / wave | bf16 MFMA flop / dispatch |",
+           "|---|---|---|---|---|---|---|"]
+    for k, d in per.items():
+        if k in ("copy", "k0_chunk_map"):
+            continue
+        m = {c: sum(v) / len(v) for c, v in d.items()}
+        cu = m.get("SQ_BUSY_CU_CYCLES", 0.0)
+        if cu <= 0:
+            continue
+        mfma = m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4 * cu)
+        valu = m.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / (4 * cu)
+        per_wave = m.get("SQ_INSTS_VALU", 0.0) / max(m.get("SQ_WAVES", 1.0), 1.0)
+        flops = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        out.append(f"| {k} | {len(next(iter(d.values())))} | {cu:.3e} | {100 * mfma:.1f}% | {100 * valu:.1f}% | "
+                   f"{per_wave:.0f} | {flops:.3e} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats(sys.argv[2], " ".join(sys.argv[3:])))
     elif sys.argv[1] == "traffic":
         print(json.dumps(traffic(sys.argv[2], sys.argv[3], sys.argv[4], float(sys.argv[5])), indent=1))
+    elif sys.argv[1] == "util":
+        print(util(sys.argv[2]))
