@@ -232,7 +232,8 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
 
 // ---------------------------------------------------------------------------
 // K2: one workgroup per (sequence, head): 8 consumer waves, wave w owning value
-// channels [16w, 16w+16), and 2 producer waves (fewer pairs: see K2Shape). Lane l of a consumer holds
+// channels [16w, 16w+16), and 2 producer waves; with fewer pairs, 8 / CONS
+// workgroups of CONS consumer waves per pair (K2Shape). Lane l of a consumer holds
 // S^T[16t + 4g + r][16w + l%16] in accumulator tile t (t = 0..7, r = 0..3). The
 // value channels evolve independently, so consumers never exchange state; they
 // share each chunk's operands through LDS.
