@@ -28,10 +28,12 @@ METRIC = "KDA fwd tokens/sec at H=32, D=128 bf16; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E peak
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
 UNIT_BYTES = 14848           # workspace bytes per (chunk, head) unit, bf16 path
+KET_BYTES = 4096             # K_end in K_b order per unit, look-ahead recurrence only
+LOOK_MAX_PAIRS = 96          # fewer (sequence, head) pairs: look-ahead recurrence
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
-def algorithmic_work(w):
+def algorithmic_work(w, bf16_resident_state=False):
     """Bytes each kernel must move and the recurrence's matrix flops, per launch.
 
     Per (chunk, head) unit, 16 token rows of 128 channels:
@@ -46,16 +48,23 @@ def algorithmic_work(w):
     Recurrence flops per unit (both paths): K_b S^T and Q_b S^T
     (2 x 2*16*128*128), the state update K_end^T E (2*128*16*128), A^kk E and
     A^qk E (2 x 2*16*16*128) and the decay (128*128).
+    With fewer than 96 (sequence, head) pairs the two-kernel path runs the
+    look-ahead recurrence: the chunk kernel also writes K_end in K_b order
+    (4096 B per unit), the recurrence reads it and forms M = K_b K_end^T of the
+    previous chunk (2*16*16*128 flops per unit).
     """
     H = w.H
     units = sum((L + 15) // 16 for L in w.seq_lens) * H
     th = w.T_tot * H
     st = w.N * H * 128 * 128 * 4 * (2 if w.initial_state is not None else 1)
-    k1 = th * (3 * 256 + 2) + units * UNIT_BYTES
-    k2 = units * UNIT_BYTES + th * 512 + st
+    look = w.N * H < LOOK_MAX_PAIRS and not bf16_resident_state
+    unit = UNIT_BYTES + (KET_BYTES if look else 0)
+    k1 = th * (3 * 256 + 2) + units * unit
+    k2 = units * unit + th * 512 + st
     kf = th * (4 * 256 + 2 + 256) + st
     flops = units * (3 * 2 * 16 * 128 * 128 + 2 * 2 * 16 * 16 * 128 + 128 * 128)
-    return dict(units=units, k1_bytes=k1, k2_bytes=k2, kf_bytes=kf, flops=flops)
+    flops_split = flops + (units * 2 * 16 * 16 * 128 if look else 0)
+    return dict(units=units, k1_bytes=k1, k2_bytes=k2, kf_bytes=kf, flops=flops, flops_split=flops_split)
 
 
 def traffic_for(kernel, workload):
@@ -180,7 +189,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    work = algorithmic_work(w)
+    work = algorithmic_work(w, bf16_resident_state=args.bf16_resident_state)
     bytes_of = {"k1_mfma": work["k1_bytes"], "k2_mfma": work["k2_bytes"], "kf_fused": work["kf_bytes"],
                 "kr_recurrent": work["kf_bytes"]}
     per_kernel = {}
@@ -189,8 +198,9 @@ def main():
         ent = {"avg_ms": round(ms, 4), "algorithmic_bytes": bytes_of[name], "achieved_GBps": round(gbs, 1),
                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
         if name in ("k2_mfma", "kf_fused"):
-            tf = work["flops"] / (ms * 1e-3) / 1e12
-            ent.update({"algorithmic_flops": work["flops"], "achieved_TFLOPs": round(tf, 2),
+            fl = work["flops_split"] if name == "k2_mfma" else work["flops"]
+            tf = fl / (ms * 1e-3) / 1e12
+            ent.update({"algorithmic_flops": fl, "achieved_TFLOPs": round(tf, 2),
                         "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)})
         per_kernel[name] = ent
     dom = max(kern_ms, key=kern_ms.get)

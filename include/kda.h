@@ -82,7 +82,10 @@ enum {
     KDA_FLAG_FP32_COMPUTE = 1u,
     /* bf16-compute kda_fwd: run the two-kernel path (chunk-parallel kernel
      * writing the workspace, then the recurrence kernel), which is what
-     * kda_fwd_prepare + kda_fwd_recur run. */
+     * kda_fwd_prepare + kda_fwd_recur run. With fewer than 96 (sequence, head)
+     * pairs (and without KDA_FLAG_BF16_RESIDENT_STATE) the recurrence runs in
+     * look-ahead form and the workspace also holds 4096 B per (chunk, head);
+     * kda_fwd_workspace_size accounts for it. */
     KDA_FLAG_SPLIT = 2u,
     /* bf16-compute kda_fwd: run the single-pass kernel (one workgroup per
      * (sequence, head) prepares each chunk in on-chip memory and runs the

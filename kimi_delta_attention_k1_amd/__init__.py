@@ -110,9 +110,9 @@ def _flags(fp32_compute, path):
 
 
 def workspace_size(batch, seqlen, num_seqs, num_heads, io_dtype=DTYPE_BF16, state_dtype=DTYPE_FP32,
-                   fp32_compute=False, path="auto") -> int:
-    d = make_desc(batch, seqlen, num_seqs, num_heads, io_dtype, state_dtype, HEAD_DIM ** -0.5,
-                  _flags(fp32_compute, path))
+                   fp32_compute=False, path="auto", bf16_resident_state=False) -> int:
+    flags = _flags(fp32_compute, path) | (FLAG_BF16_RESIDENT_STATE if bf16_resident_state else 0)
+    d = make_desc(batch, seqlen, num_seqs, num_heads, io_dtype, state_dtype, HEAD_DIM ** -0.5, flags)
     return int(load_library().kda_fwd_workspace_size(ctypes.byref(d)))
 
 

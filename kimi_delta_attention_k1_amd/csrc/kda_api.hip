@@ -99,7 +99,9 @@ extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc)
         // their flags the same description is also valid for the two-stage
         // entry points
         const bool units = !(desc->flags & (KDA_FLAG_FUSED | KDA_FLAG_RECURRENT));
-        size_t b = kda::ws_layout(desc->num_seqs, desc->num_heads, units ? s.n_c_max : 0, s.f32_path).total;
+        const bool look = units && kda::use_lookahead(desc->num_seqs, desc->num_heads, s.f32_path,
+                                                       (desc->flags & KDA_FLAG_BF16_RESIDENT_STATE) != 0);
+        size_t b = kda::ws_layout(desc->num_seqs, desc->num_heads, units ? s.n_c_max : 0, s.f32_path, look).total;
         if (b > best) best = b;
     }
     return best;
@@ -137,7 +139,9 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
 
     if (s.T_tot > 0 && (!q || !k || !v || !g_raw || !beta_raw || !out)) return KDA_ERR_NULL_ARG;
     if (!workspace) return KDA_ERR_WORKSPACE;
-    const WsLayout lay = kda::ws_layout(N, H, no_units ? 0 : s.n_c_max, s.f32_path);
+    const bool look =
+        !no_units && kda::use_lookahead(N, H, s.f32_path, (desc->flags & KDA_FLAG_BF16_RESIDENT_STATE) != 0);
+    const WsLayout lay = kda::ws_layout(N, H, no_units ? 0 : s.n_c_max, s.f32_path, look);
     if (workspace_bytes < lay.total || !aligned(workspace, KDA_WORKSPACE_ALIGN)) return KDA_ERR_WORKSPACE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g_raw, sgate ? esz : 16) ||
         !aligned(out, 16) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(beta_raw, esz))

@@ -46,12 +46,22 @@ constexpr UnitLayout kUnitF32 = {0, 8192, 16384, 24576, 25600, 26624, 27136};
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Few (sequence, head) pairs: the bf16 recurrence runs in look-ahead form, which
+// also needs each chunk's K_end in K_b's order (4096 B per (chunk, head), after the
+// units). Decided from the shape and flags alone, so separate stage calls agree.
+constexpr int64_t kLookMaxPairs = 96;
+constexpr size_t kKetBytes = 4096;
+inline bool use_lookahead(int64_t N, int64_t H, bool f32_path, bool bf16_resident)
+{
+    return !f32_path && !bf16_resident && N * H < kLookMaxPairs;
+}
+
 struct WsLayout {
-    size_t tok_off, chunk_off, units, unit_bytes, total;
+    size_t tok_off, chunk_off, units, unit_bytes, ket, total;
     int64_t n_c_max;
 };
 
-inline WsLayout ws_layout(int64_t N, int64_t H, int64_t n_c_max, bool f32_path)
+inline WsLayout ws_layout(int64_t N, int64_t H, int64_t n_c_max, bool f32_path, bool lookahead)
 {
     WsLayout L;
     L.tok_off = kHeaderBytes;
@@ -59,7 +69,9 @@ inline WsLayout ws_layout(int64_t N, int64_t H, int64_t n_c_max, bool f32_path)
     L.units = align_up(L.chunk_off + sizeof(int32_t) * (size_t)(N + 1), 128);
     L.unit_bytes = f32_path ? kUnitF32.bytes : kUnitBf16.bytes;
     L.n_c_max = n_c_max;
-    L.total = L.units + L.unit_bytes * (size_t)H * (size_t)n_c_max;
+    const size_t end = L.units + L.unit_bytes * (size_t)H * (size_t)n_c_max;
+    L.ket = lookahead ? align_up(end, 128) : 0;
+    L.total = lookahead ? L.ket + kKetBytes * (size_t)H * (size_t)n_c_max : end;
     return L;
 }
 

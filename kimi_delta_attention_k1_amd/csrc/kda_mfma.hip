@@ -39,13 +39,17 @@ constexpr int kK1MaxWaves = 4;
 
 // SG: scalar gate, g_raw is [T][H] and its one value per token and head applies
 // to every key channel (Gated DeltaNet, Doubleword section 3)
-template <bool SG>
+// KET: also write K_end in K_b's 16x16x32 operand order (token-major) to `ket`, for
+// the look-ahead recurrence
+template <bool SG, bool KET>
 __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ graw,
     const uint16_t *__restrict__ braw, const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off,
-    int N, int H, int64_t n_c_max, float lb, float scale, char *__restrict__ units)
+    int N, int H, int64_t n_c_max, float lb, float scale, char *__restrict__ units, char *__restrict__ ket)
 {
     __shared__ __attribute__((aligned(16))) uint16_t sKE[kK1MaxWaves][kD][kC];  // K_end as [channel][token]
+    // each lane's own K_end values in K_b order (4 destination lanes x 8 elements)
+    __shared__ __attribute__((aligned(16))) uint16_t sKT[KET ? kK1MaxWaves : 1][64][32];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int c = blockIdx.x;
     const int h = blockIdx.y * (blockDim.x >> 6) + wv;  // blockDim.x / 64 divides H
@@ -154,7 +158,9 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
             const float dn = __builtin_amdgcn_exp2f(gref - gf[i]);
             const float cl = row_bcast<15>(up);  // e^{G_last - Gref} for this channel
             // K_end = khat e^{G_last - G} = khat e^{Gref - G} e^{G_last - Gref}, to LDS as [channel][token]
-            sKE[wv][32 * g + i][tok] = __builtin_bit_cast(uint16_t, (__bf16)(kf[i] * dn * cl));
+            const uint16_t keb = __builtin_bit_cast(uint16_t, (__bf16)(kf[i] * dn * cl));
+            sKE[wv][32 * g + i][tok] = keb;
+            if constexpr (KET) sKT[wv][lane][((i & 15) >> 2) * 8 + (i & 3) + 4 * (i >> 4)] = keb;
             const float kr = kf[i] * up, ki = kf[i] * dn, qr = qf[i] * up;
             kr_h[e] = (__bf16)kr;
             ki_h[e] = (__bf16)ki;
@@ -227,6 +233,13 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
         const u32x2 hi = *reinterpret_cast<const u32x2 *>(&sKE[wv][32 * p + 16 + tok][4 * g]);
         const u32x4 x = {lo[0], lo[1], hi[0], hi[1]};
         reinterpret_cast<u32x4 *>(u + kUnitBf16.ke + p * 1024)[lane] = x;
+    }
+    if constexpr (KET) {
+        // lane (tok, g) owns k step g; its element group gp goes to destination lane tok + 16 gp
+        char *kt = ket + ((int64_t)h * n_c_max + c) * kKetBytes + g * 1024;
+#pragma unroll
+        for (int gp = 0; gp < 4; ++gp)
+            *reinterpret_cast<u32x4 *>(kt + (tok + 16 * gp) * 16) = *reinterpret_cast<const u32x4 *>(&sKT[wv][lane][8 * gp]);
     }
 }
 
@@ -565,16 +578,273 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Look-ahead recurrence for few (sequence, head) pairs, where the chain of one
+// chunk's dependent steps, not throughput, sets the pace. With
+//   S_c^T = Diag(gamma_{c-1}) S_{c-1}^T + K_end,{c-1}^T E_{c-1},
+// the product the next E needs splits as
+//   K_b,c S_c^T = P_c + M_c E_{c-1},  P_c = K_b,c (Diag(gamma_{c-1}) S_{c-1}^T),
+//   M_c = K_b,c K_end,{c-1}^T,
+// where P_c needs only the previous state. Each 16-column tile gets four waves:
+//   E wave    : E_c from P_c + M_c E_{c-1} (the only chain from one E to the next)
+//   state waves (2): keys 0-63 and 64-127 of the state; each applies the update
+//               with E_{c-1}, then forms its halves of Q_b,c S_c^T and P_{c+1}
+//   output wave: M_{c+1} from K_end in K_b order (written by K1), and the outputs
+//               of chunk c-1 from Q_b S^T and E
+// Everything passes through LDS between barriers; each value is produced in one
+// iteration and used in the next. The state waves run one iteration ahead (an
+// extra first iteration forms P_0).
+// ---------------------------------------------------------------------------
+template <int CONS> struct KLShape {
+    static constexpr int producers = 4;
+    static constexpr int unit_kb = kVOff / 1024;                  // unit, then K_end in K_b order
+    static constexpr int v_kb = 1;                                // v rows of 16 CONS columns
+    static constexpr int slot_kb = unit_kb + 4 + v_kb;            // 20
+    static constexpr int slot_bytes = slot_kb * 1024;
+    static constexpr int slots = CONS == 1 ? 7 : 6;
+    static constexpr int consumers = 4 * CONS;
+    static constexpr int threads = 64 * (consumers + producers);
+    static constexpr int kb_per_producer = slot_kb / producers;
+    // chunk c + ahead is copied while chunks c - 1 .. c + 1 are read
+    static constexpr int ahead = slots - 2;
+    static constexpr int pending = (ahead - 2) * kb_per_producer;  // chunk c + 2 landed at barrier c + 1
+    static constexpr int xbuf_bytes = 2 * CONS * 6 * 1024;        // E, M, 2 x P, 2 x Q_b S^T, by parity
+    static_assert(slot_kb % producers == 0, "producers split a slot evenly");
+    static_assert(v_kb * 1024 >= 32 * CONS * kC, "v rows fit");
+    static_assert(pending <= 63 && ahead >= 3, "copy pipeline");
+    static_assert(slots * slot_bytes + xbuf_bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+};
+
+template <typename TSt, int CONS>
+__global__ __launch_bounds__(KLShape<CONS>::threads) void k2_look(
+    const uint16_t *__restrict__ v, const TSt *s0, TSt *s1, uint16_t *__restrict__ out,
+    const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off, int H, int pairs, int64_t n_c_max,
+    const char *__restrict__ units, const char *__restrict__ kets)
+{
+    using Sh = KLShape<CONS>;
+    constexpr int kGroups = 8 / CONS;
+    __shared__ __attribute__((aligned(1024))) char lds[Sh::slots][Sh::slot_bytes];
+    __shared__ f32x4 ebuf[2][CONS][64], mbuf[2][CONS][64], pbuf[2][2][CONS][64], xqbuf[2][2][CONS][64];
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b = blockIdx.x;
+    const int pair = (b & 7) + 8 * (b / (8 * kGroups));
+    const int wbase = ((b >> 3) % kGroups) * CONS;
+    if (pair >= pairs) return;  // whole workgroup: no barrier is entered
+    const int n = pair / H, h = pair % H;
+    const int c0 = chunk_off[n], nch = chunk_off[n + 1] - c0;
+    const int tb = tok_off[n], te = tok_off[n + 1];
+    constexpr int kKet = Sh::unit_kb * 1024;  // K_end in K_b order, inside a slot
+    constexpr int kV = kKet + 4096;           // v rows
+    const int role = w / CONS, wc = w % CONS;  // 0: E wave, 1-2: state waves, 3: output wave, 4+: producers
+    const int g = lane >> 4, vcol = 16 * (wbase + wc) + (lane & 15);
+    if (nch == 0) {  // uniform over the workgroup: no barrier is entered
+        if ((role == 1 || role == 2) && s1) {
+            const int64_t sb0 = (((int64_t)n * H + h) * kD + vcol) * kD + 64 * (role - 1) + 4 * g;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                st_state4(s1 + sb0 + 16 * t, s0 ? ld_state4(s0 + sb0 + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        return;
+    }
+
+    if (w >= Sh::consumers) {
+        // ------------------------------------------------------------ producers
+        const int pw = w - Sh::consumers;
+        constexpr int kKB = Sh::kb_per_producer;
+        const char *ubase = units + ((int64_t)h * n_c_max + c0) * kUnitBf16.bytes;
+        const char *kbase = kets + ((int64_t)h * n_c_max + c0) * kKetBytes;
+        const char *vb = reinterpret_cast<const char *>(v);
+        auto copy_chunk = [&](int j, int slot) {
+            j = min(j, nch - 1);  // past the end: re-read the last chunk into a free slot
+            const char *u = ubase + (int64_t)j * kUnitBf16.bytes;
+#pragma unroll
+            for (int i = 0; i < kKB; ++i) {
+                const int kb = pw * kKB + i;  // which KB of the slot
+                const char *src;
+                if (kb < Sh::unit_kb) {
+                    const int off = kb * 1024 + lane * 16;
+                    src = u + (off < (int)kUnitBf16.bytes ? off : 0);
+                } else if (kb < Sh::unit_kb + 4) {
+                    src = kbase + (int64_t)j * kKetBytes + (kb - Sh::unit_kb) * 1024 + lane * 16;
+                } else {
+                    // 16-byte piece `lane` of the v rows: token row lane / (2 CONS), columns
+                    // 16 wbase + 8 (lane % (2 CONS)) ..; lanes past the rows repeat them
+                    const int r = (lane / (2 * CONS)) & 15;
+                    const int row = min(tb + j * kC + r, te - 1);
+                    src = vb + (((int64_t)row * H + h) * kD + 16 * wbase + 8 * (lane % (2 * CONS))) * 2;
+                }
+                __builtin_amdgcn_global_load_lds(src, (lds_void *)(&lds[slot][kb * 1024]), 16, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int sl = 0; sl < Sh::ahead; ++sl) copy_chunk(sl, sl);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Sh::pending) : "memory");  // chunks 0 and 1 landed
+        bar_sync();
+        bar_sync();  // the state waves' first iteration
+#pragma unroll 1
+        for (int j = 0; j < nch; ++j) {
+            copy_chunk(j + Sh::ahead, (j + Sh::ahead) % Sh::slots);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Sh::pending) : "memory");  // chunk j+2 landed
+            bar_sync();
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // nothing in flight into LDS at exit
+        return;
+    }
+
+    bar_sync();
+
+    if (role == 0) {
+        // ---------------------------------------------------------------- E wave
+        bar_sync();  // the state waves form P_0
+        bf16x4 ep_h = {}, ep_l = {};  // previous chunk's E, split
+#pragma unroll 1
+        for (int c = 0; c < nch; ++c) {
+            const char *L = lds[c % Sh::slots];
+            const int t0 = tb + c * kC, len = min(kC, te - t0);
+            f32x4 xk = pbuf[c & 1][0][wc][lane] + pbuf[c & 1][1][wc][lane];
+            if (c > 0) {  // + M E_prev in split operands
+                bf16x4 m_h, m_l;
+                split4(mbuf[c & 1][wc][lane], m_h, m_l);
+                xk = mma32(cat8(m_h, m_l), cat8(ep_h, ep_h), xk);
+                xk = mma16(m_h, ep_l, xk);
+            }
+            f32x4 eb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tr = 4 * g + r;
+                const uint16_t vr =
+                    *reinterpret_cast<const uint16_t *>(L + kV + tr * (32 * CONS) + 32 * wc + 2 * (lane & 15));
+                eb[r] = (tr < len ? bf16_bits_to_f32(vr) : 0.f) - xk[r];
+            }
+            bf16x4 eb_h, eb_l;
+            split4(eb, eb_h, eb_l);
+            const bf16x8 ab = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.ab + lane * 16);
+            const bf16x4 ab_h = {ab[0], ab[1], ab[2], ab[3]};
+            f32x4 E = {0.f, 0.f, 0.f, 0.f};
+            E = mma32(ab, cat8(eb_h, eb_h), E);
+            E = mma16(ab_h, eb_l, E);
+            ebuf[c & 1][wc][lane] = E;
+            split4(E, ep_h, ep_l);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            bar_sync();
+        }
+        return;
+    }
+
+    if (role <= 2) {
+        // ------------------------------------------------------------ state waves
+        // tiles 4 i .. 4 i + 3 of the state (keys 64 i .. 64 i + 63), k steps 2 i, 2 i + 1
+        const int i = role - 1;
+        const int64_t sbase = (((int64_t)n * H + h) * kD + vcol) * kD + 64 * i + 4 * g;
+        f32x4 st[4], dec[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) st[t] = s0 ? ld_state4(s0 + sbase + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+        // half of Y X^T over this wave's 64 keys, X in fp32 tiles
+        auto half_prod = [&](const char *L, int off, const f32x4 (&x)[4]) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                bf16x8 sb;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sb[r] = (__bf16)x[2 * pp][r];
+                    sb[4 + r] = (__bf16)x[2 * pp + 1][r];
+                }
+                a = mma32(*reinterpret_cast<const bf16x8 *>(L + off + (2 * i + pp) * 1024 + lane * 16), sb, a);
+            }
+            return a;
+        };
+        // P_0 = K_b,0 S_0^T
+        pbuf[0][i][wc][lane] = half_prod(lds[0], kUnitBf16.kb, st);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        bar_sync();
+        // S^T <- Diag(gamma) S^T + K_end^T E for chunk cp, from the decayed state
+        auto update = [&](int cp) {
+            const char *Lp = lds[cp % Sh::slots];
+            bf16x4 e_h, e_l;
+            split4(ebuf[cp & 1][wc][lane], e_h, e_l);
+            const bf16x8 e_hl = cat8(e_h, e_l);
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const u32x4 kq = *reinterpret_cast<const u32x4 *>(Lp + kUnitBf16.ke + (2 * i + pp) * 1024 + lane * 16);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int t = 2 * pp + hh;
+                    const bf16x4 kt = __builtin_bit_cast(bf16x4, hh ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]});
+                    st[t] = mma32(cat8(kt, kt), e_hl, dec[t]);
+                }
+            }
+        };
+#pragma unroll 1
+        for (int c = 0; c < nch; ++c) {
+            const char *L = lds[c % Sh::slots];
+            if (c > 0) update(c - 1);
+            xqbuf[c & 1][i][wc][lane] = half_prod(L, kUnitBf16.qb, st);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                dec[t] = st[t] * *reinterpret_cast<const f32x4 *>(L + kUnitBf16.gm + (64 * i + 16 * t + 4 * g) * 4);
+            if (c + 1 < nch) pbuf[(c + 1) & 1][i][wc][lane] = half_prod(lds[(c + 1) % Sh::slots], kUnitBf16.kb, dec);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            bar_sync();
+        }
+        update(nch - 1);
+        if (s1) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) st_state4(s1 + sbase + 16 * t, st[t]);
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------------- output wave
+    bar_sync();  // the state waves form P_0
+    auto out_step = [&](int c) {
+        const char *L = lds[c % Sh::slots];
+        const int t0 = tb + c * kC, len = min(kC, te - t0);
+        bf16x4 e_h, e_l;
+        split4(ebuf[c & 1][wc][lane], e_h, e_l);
+        const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.aq + lane * 16);
+        const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]};
+        f32x4 O = mma32(aq, cat8(e_h, e_h), xqbuf[c & 1][0][wc][lane] + xqbuf[c & 1][1][wc][lane]);
+        O = mma16(aq_h, e_l, O);
+        uint16_t *orow = out + ((int64_t)(t0 + 4 * g) * H + h) * kD + vcol;
+        const int64_t rstride = (int64_t)H * kD;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (4 * g + r < len) orow[r * rstride] = __builtin_bit_cast(uint16_t, (__bf16)O[r]);
+    };
+#pragma unroll 1
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) {
+            // M_{c+1}^T = K_end,c K_b,{c+1}^T, whose D layout is M_{c+1} in A-operand order
+            const char *L = lds[c % Sh::slots];
+            const char *Ln = lds[(c + 1) % Sh::slots];
+            f32x4 mt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                mt = mma32(*reinterpret_cast<const bf16x8 *>(L + kKet + p * 1024 + lane * 16),
+                           *reinterpret_cast<const bf16x8 *>(Ln + kUnitBf16.kb + p * 1024 + lane * 16), mt);
+            mbuf[(c + 1) & 1][wc][lane] = mt;
+        }
+        if (c > 0) out_step(c - 1);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        bar_sync();
+    }
+    out_step(nch - 1);
+}
+
 hipError_t launch_prep_mfma(const Problem &p, hipStream_t s)
 {
     if (p.n_c_max == 0) return hipSuccess;
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
     const int wpb = (p.H % 4 == 0) ? 4 : (p.H % 2 == 0 ? 2 : 1);  // waves per block divide H
-    auto kern = p.scalar_gate ? k1_mfma<true> : k1_mfma<false>;
+    const bool look = use_lookahead(p.N, p.H, false, p.bf16_resident);
+    auto kern = p.scalar_gate ? (look ? k1_mfma<true, true> : k1_mfma<true, false>)
+                              : (look ? k1_mfma<false, true> : k1_mfma<false, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)p.n_c_max, p.H / wpb), dim3(64 * wpb), 0, s, (const uint16_t *)p.q,
                        (const uint16_t *)p.k, (const uint16_t *)p.g, (const uint16_t *)p.beta, tok, chk, (int)p.N,
-                       p.H, p.n_c_max, p.lb, p.scale, p.ws + p.lay.units);
+                       p.H, p.n_c_max, p.lb, p.scale, p.ws + p.lay.units, look ? p.ws + p.lay.ket : nullptr);
     return hipGetLastError();
 }
 
@@ -594,10 +864,27 @@ static hipError_t launch_k2(const Problem &p, hipStream_t s)
 
 // Consumer waves per workgroup: the largest that still puts about one
 // workgroup on every one of the 256 compute units.
+template <typename TSt, int CONS>
+static hipError_t launch_look(const Problem &p, hipStream_t s)
+{
+    const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
+    const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
+    const int pairs = (int)(p.N * p.H);
+    constexpr int groups = 8 / CONS;
+    const unsigned grid = (unsigned)((pairs + 7) / 8 * 8 * groups);
+    hipLaunchKernelGGL((k2_look<TSt, CONS>), dim3(grid), dim3(KLShape<CONS>::threads), 0, s, (const uint16_t *)p.v,
+                       (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H, pairs, p.n_c_max,
+                       (const char *)(p.ws + p.lay.units), (const char *)(p.ws + p.lay.ket));
+    return hipGetLastError();
+}
+
 template <typename TSt, bool RS>
 static hipError_t launch_recur_mfma_t(const Problem &p, hipStream_t s)
 {
     const int64_t pairs = p.N * p.H;
+    if (!RS && use_lookahead(p.N, p.H, false, false)) {
+        return pairs >= 48 ? launch_look<TSt, 2>(p, s) : launch_look<TSt, 1>(p, s);
+    }
     if (pairs >= 192) return launch_k2<TSt, 8, RS>(p, s);
     if (pairs >= 96) return launch_k2<TSt, 4, RS>(p, s);
     if (pairs >= 48) return launch_k2<TSt, 2, RS>(p, s);

@@ -50,19 +50,28 @@ def test_desc_struct_matches_header():
     assert ctypes.sizeof(kda.KdaDesc) == 48
 
 
-def _layout(N, H, n_c, unit):
+def _layout(N, H, n_c, unit, look=False):
+    """Header, token and chunk offsets, one unit per (chunk, head); with fewer than 96
+    bf16 (sequence, head) pairs the look-ahead recurrence also keeps 4096 B per
+    (chunk, head) of K_end in K_b order after the units."""
     tok = 128
     chk = (tok + 4 * (N + 1) + 127) // 128 * 128
     units = (chk + 4 * (N + 1) + 127) // 128 * 128
-    return units + unit * H * n_c
+    end = units + unit * H * n_c
+    return (end + 127) // 128 * 128 + 4096 * H * n_c if look else end
 
 
 def test_workspace_size_arithmetic(lib):
     # batch mode, one sequence of 64 tokens -> 4 chunks
     assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32) == _layout(1, 1, 4, 27136)
-    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_BF16) == _layout(1, 1, 4, 14848)
+    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_BF16) == _layout(1, 1, 4, 14848, look=True)
     # batch of 2 rows of 17 tokens -> 2 x 2 chunks
-    assert kda.workspace_size(2, 17, 2, 3) == _layout(2, 3, 4, 14848)
+    assert kda.workspace_size(2, 17, 2, 3) == _layout(2, 3, 4, 14848, look=True)
+    # 95 pairs still take the look-ahead recurrence, 96 do not
+    assert kda.workspace_size(1, 160, 5, 19) == _layout(5, 19, (160 + 15 * 5) // 16, 14848, look=True)
+    assert kda.workspace_size(1, 160, 6, 16) == _layout(6, 16, (160 + 15 * 6) // 16, 14848)
+    # the bf16-resident-state variant keeps the plain recurrence
+    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_BF16, bf16_resident_state=True) == _layout(1, 1, 4, 14848)
     # packed: 8 x 8192 tokens (bound (T + 15 N) / 16)
     assert kda.workspace_size(1, 65536, 8, 32) == _layout(8, 32, (65536 + 15 * 8) // 16, 14848)
     # fp32 compute flag selects the fp32 unit size
