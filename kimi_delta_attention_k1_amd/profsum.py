@@ -35,9 +35,11 @@ KERNEL_SOURCES = {
     "kf_fused": ("kda_fused.hip", "kda_mfma_common.h", "kda_internal.h"),
     "kr_recurrent": ("kda_recurrent.hip", "kda_internal.h"),
 }
-SHORT = {"k1_mfma": "kda::k1_mfma", "k2_mfma": "kda::k2_mfma", "kf_fused": "kda::kf_fused",
-         "kr_recurrent": "kda::kr_recurrent",
-         "k0_chunk_map": "kda::k0_chunk_map", "copy": "__amd_rocclr_copyBuffer"}
+# kernel-name fragments per reported kernel; the recurrence stage of the two-kernel
+# path is k2_mfma, or k2_look (its look-ahead form) when few pairs run
+SHORT = {"k1_mfma": ("kda::k1_mfma",), "k2_mfma": ("kda::k2_mfma", "kda::k2_look"),
+         "kf_fused": ("kda::kf_fused",), "kr_recurrent": ("kda::kr_recurrent",),
+         "k0_chunk_map": ("kda::k0_chunk_map",), "copy": ("__amd_rocclr_copyBuffer",)}
 
 
 def src_hash(kernel: str) -> str:
@@ -50,8 +52,8 @@ def src_hash(kernel: str) -> str:
 
 
 def short_name(kernel_name: str) -> str:
-    for short, key in SHORT.items():
-        if key in kernel_name:
+    for short, keys in SHORT.items():
+        if any(key in kernel_name for key in keys):
             return short
     return kernel_name.split("(")[0][:40]
 
