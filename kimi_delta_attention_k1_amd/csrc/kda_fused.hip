@@ -31,6 +31,8 @@
 // E' = Diag(rk) E, which is exactly what the state update needs with the raw
 // K_end (K_end^T E = K_end_raw^T E'), and A^qk / Diag(rk) applied to E' gives
 // the same outputs.
+#include <type_traits>
+
 #include "kda_mfma_common.h"
 
 namespace kda {
@@ -40,7 +42,7 @@ constexpr int kFPrep = 4;                             // stage-A waves
 constexpr int kFSolve = 2;                            // stage-B waves
 constexpr int kFThreads = 64 * (kFCons + kFPrep + kFSolve);  // 640
 constexpr int kFIn = 4;                               // input chunks in flight per prep wave
-constexpr int kFSlots = 3;                            // prepared-chunk slots
+constexpr int kFSlots = 3;                            // prepared-chunk slots (stage A steps through them unrolled)
 constexpr int kFDma = 5;                              // global-to-LDS loads per chunk per prep wave
 constexpr int kFPending = (kFIn - 1) * kFDma;         // loads allowed in flight at a stage-A start
 static_assert(kFPending <= 63, "vmcnt holds at most 63 outstanding loads");
@@ -236,147 +238,159 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
         read_inputs(0);
 
         const float lb2 = lb * kLog2e;
-#pragma unroll 1
-        for (int tau = 0; tau < ticks; ++tau) {
-            if (tau < nch) {
-                // ------------------------------------------------ stage A, chunk c = tau
-                const int c = tau;
-                // the registers hold chunk c (reads completed before the last barrier):
-                // refill its input slot with chunk c + kFIn
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                dma_chunk(c + kFIn, c % kFIn);
-                const int t0 = tb + c * kC, len = min(kC, te - t0);
-                // rows past the end of the sequence hold copies of its last row; zero
-                // gate and beta make them absent: they reach only the masked triangles
-                // of R and A^qk, rows of E' that come out exactly zero, and output rows
-                // that are never stored
-                const bool valid = t < len;
+        // one tick of stage A on chunk c. The prepared slot c % kFSlots is a compile-time
+        // constant (the loop below steps through the slots in turn), so the slot's LDS
+        // addresses fold into instruction offsets instead of being rebuilt every tick.
+        auto stage_a = [&](const int c, auto slot_tag) {
+            constexpr int slot = decltype(slot_tag)::value;
+            // the registers hold chunk c (reads completed before the last barrier):
+            // refill its input slot with chunk c + kFIn
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            dma_chunk(c + kFIn, c % kFIn);
+            const int t0 = tb + c * kC, len = min(kC, te - t0);
+            // rows past the end of the sequence hold copies of its last row; zero
+            // gate and beta make them absent: they reach only the masked triangles
+            // of R and A^qk, rows of E' that come out exactly zero, and output rows
+            // that are never stored
+            const bool valid = t < len;
 
-                const int brow = min(t0 + t, te - 1);
-                const int64_t eo = ((int64_t)brow * H + h) * 2;  // byte offset of [brow][h]
-                const bool bhi = (reinterpret_cast<uintptr_t>(bb8 + eo) & 2) != 0;
-                const float vmask = valid ? 1.f : 0.f;
-                float qf[8], kf[8], gf[8];
+            const int brow = min(t0 + t, te - 1);
+            const int64_t eo = ((int64_t)brow * H + h) * 2;  // byte offset of [brow][h]
+            const bool bhi = (reinterpret_cast<uintptr_t>(bb8 + eo) & 2) != 0;
+            const float vmask = valid ? 1.f : 0.f;
+            float qf[8], kf[8], gf[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qf[2 * e] = bf_lo(qa[e]);
+                qf[2 * e + 1] = bf_hi(qa[e]);
+                kf[2 * e] = bf_lo(ka[e]);
+                kf[2 * e + 1] = bf_hi(ka[e]);
+            }
+            const float beta = vmask * sigmoid_fast(bhi ? bf_hi(bw) : bf_lo(bw));
+            if constexpr (SG) {  // one gate and one prefix sum serve every channel
+                const bool ghi = (reinterpret_cast<uintptr_t>(gb8 + eo) & 2) != 0;
+                float x = vmask * lb2 * sigmoid_fast(ghi ? bf_hi(ga[0]) : bf_lo(ga[0]));
+                // rounded exactly as the per-channel gate below, step by step
+                asm("" : "+v"(x));
+                x += row_shr<1>(x);
+                x += row_shr<2>(x);
+                x += row_shr<4>(x);
+                x += row_shr<8>(x);
+                asm("" : "+v"(x));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) gf[i] = x;
+            } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    qf[2 * e] = bf_lo(qa[e]);
-                    qf[2 * e + 1] = bf_hi(qa[e]);
-                    kf[2 * e] = bf_lo(ka[e]);
-                    kf[2 * e + 1] = bf_hi(ka[e]);
+                    gf[2 * e] = bf_lo(ga[e]);
+                    gf[2 * e + 1] = bf_hi(ga[e]);
                 }
-                const float beta = vmask * sigmoid_fast(bhi ? bf_hi(bw) : bf_lo(bw));
-                if constexpr (SG) {  // one gate and one prefix sum serve every channel
-                    const bool ghi = (reinterpret_cast<uintptr_t>(gb8 + eo) & 2) != 0;
-                    float x = vmask * lb2 * sigmoid_fast(ghi ? bf_hi(ga[0]) : bf_lo(ga[0]));
-                    // rounded exactly as the per-channel gate below, step by step
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {  // gate (log2 units) and prefix sum over tokens
+                    float x = vmask * lb2 * sigmoid_fast(gf[i]);
+                    // the empty asm statements keep x as computed, so each shifted add
+                    // below becomes a single DPP add
                     asm("" : "+v"(x));
                     x += row_shr<1>(x);
                     x += row_shr<2>(x);
                     x += row_shr<4>(x);
                     x += row_shr<8>(x);
                     asm("" : "+v"(x));
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) gf[i] = x;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        gf[2 * e] = bf_lo(ga[e]);
-                        gf[2 * e + 1] = bf_hi(ga[e]);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {  // gate (log2 units) and prefix sum over tokens
-                        float x = vmask * lb2 * sigmoid_fast(gf[i]);
-                        // the empty asm statements keep x as computed, so each shifted add
-                        // below becomes a single DPP add
-                        asm("" : "+v"(x));
-                        x += row_shr<1>(x);
-                        x += row_shr<2>(x);
-                        x += row_shr<4>(x);
-                        x += row_shr<8>(x);
-                        asm("" : "+v"(x));
-                        gf[i] = x;
-                    }
+                    gf[i] = x;
                 }
-                float nq = 0.f, nk = 0.f;  // partial squared norms over this wave's 32 channels
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    nq += qf[i] * qf[i];
-                    nk += kf[i] * kf[i];
-                }
-                nq = sum_rows4(nq);
-                nk = sum_rows4(nk);
-
-                char *X = parts + (c & 1) * kXBytes;
-                char *P = slots + (c % kFSlots) * kPBytes;
-                if (sg == 0) {
-                    reinterpret_cast<float *>(X + m * kXWave + kXNQ)[t] = nq;
-                    reinterpret_cast<float *>(X + m * kXWave + kXNK)[t] = nk;
-                    if (m == 0) reinterpret_cast<float *>(X + kXBeta)[t] = beta;
-                }
-                // decays relative to token 7 (each factor within e^{8|lb|}); K_end via token 15
-                bf16x8 kr_h, ki_h, qr_h;
-                float ke[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float gref = row_bcast<7>(gf[i]);
-                    const float up = __builtin_amdgcn_exp2f(gf[i] - gref);
-                    const float dn = __builtin_amdgcn_exp2f(gref - gf[i]);
-                    const float cl = row_bcast<15>(up);  // e^{G_last - Gref}
-                    const float kr = kf[i] * up, ki = kf[i] * dn, qr = qf[i] * up;
-                    kr_h[i] = (__bf16)kr;
-                    ki_h[i] = (__bf16)ki;
-                    qr_h[i] = (__bf16)qr;
-                    ke[i] = ki * cl;
-                }
-                // raw K_end = k e^{G_last - G}: consumer fragment (tile pair m), lane
-                // (kc + 16 (t/4)), element (t%4) + 4 hi, channel 32m + 16 hi + kc; rounded
-                // in pairs, stored as halves
-#pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    const uint32_t pk = pk_bf16(f32x2{ke[i], ke[i + 1]});
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int cr = 8 * sg + i + j, kc = cr & 15, hi = cr >> 4;
-                        *reinterpret_cast<uint16_t *>(P + kPKE + m * 1024 + swz(kc + 16 * (t >> 2)) * 16 +
-                                                      ((t & 3) + 4 * hi) * 2) = (uint16_t)(pk >> (16 * j));
-                    }
-                }
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 dR = mma32(kr_h, ki_h, z);
-                const f32x4 dRT = mma32(ki_h, kr_h, z);
-                const f32x4 dAQT = mma32(ki_h, qr_h, z);
-                reinterpret_cast<f32x4 *>(X + m * kXWave + kXR)[lane] = dR;
-                reinterpret_cast<f32x4 *>(X + m * kXWave + kXRT)[lane] = dRT;
-                reinterpret_cast<f32x4 *>(X + m * kXWave + kXAQ)[lane] = dAQT;
-
-                // raw K_b = k e^{G}, Q_b = q e^{G} in the consumer's 16x16x32 A order
-                // (k step m); gamma = e^{G_last} from token 15; the v tile
-                bf16x4 kb4[2], qb4[2];
-                float dec[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    dec[i] = __builtin_amdgcn_exp2f(gf[i]);
-                    kb4[i >> 2][i & 3] = (__bf16)(kf[i] * dec[i]);
-                    qb4[i >> 2][i & 3] = (__bf16)(qf[i] * dec[i]);
-                }
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int q4 = 2 * sg + hf;                 // which 4 channels of the 32
-                    const int gd = q4 & 3, e0 = (q4 >> 2) * 4;  // consumer lane group, element
-                    const int o = m * 1024 + swz(t + 16 * gd) * 16 + e0 * 2;
-                    *reinterpret_cast<bf16x4 *>(P + kPKB + o) = kb4[hf];
-                    *reinterpret_cast<bf16x4 *>(P + kPQB + o) = qb4[hf];
-                }
-                if (t == 15) {
-                    float *gm = reinterpret_cast<float *>(P + kPGM) + 32 * m + 8 * sg;
-                    *reinterpret_cast<f32x4 *>(gm) = f32x4{dec[0], dec[1], dec[2], dec[3]};
-                    *reinterpret_cast<f32x4 *>(gm + 4) = f32x4{dec[4], dec[5], dec[6], dec[7]};
-                }
-                *reinterpret_cast<u32x4 *>(P + kPV + t * kVRow + (32 * m + 8 * sg) * 2) =
-                    valid ? va : u32x4{0u, 0u, 0u, 0u};
-                if (c + 1 < nch) read_inputs(c + 1);
             }
+            float nq = 0.f, nk = 0.f;  // partial squared norms over this wave's 32 channels
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                nq += qf[i] * qf[i];
+                nk += kf[i] * kf[i];
+            }
+            nq = sum_rows4(nq);
+            nk = sum_rows4(nk);
+
+            char *X = parts + (c & 1) * kXBytes;
+            char *P = slots + slot * kPBytes;
+            if (sg == 0) {
+                reinterpret_cast<float *>(X + m * kXWave + kXNQ)[t] = nq;
+                reinterpret_cast<float *>(X + m * kXWave + kXNK)[t] = nk;
+                if (m == 0) reinterpret_cast<float *>(X + kXBeta)[t] = beta;
+            }
+            // decays relative to token 7 (each factor within e^{8|lb|}); K_end via token 15
+            bf16x8 kr_h, ki_h, qr_h;
+            float ke[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float gref = row_bcast<7>(gf[i]);
+                const float up = __builtin_amdgcn_exp2f(gf[i] - gref);
+                const float dn = __builtin_amdgcn_exp2f(gref - gf[i]);
+                const float cl = row_bcast<15>(up);  // e^{G_last - Gref}
+                const float kr = kf[i] * up, ki = kf[i] * dn, qr = qf[i] * up;
+                kr_h[i] = (__bf16)kr;
+                ki_h[i] = (__bf16)ki;
+                qr_h[i] = (__bf16)qr;
+                ke[i] = ki * cl;
+            }
+            // raw K_end = k e^{G_last - G}: consumer fragment (tile pair m), lane
+            // (kc + 16 (t/4)), element (t%4) + 4 hi, channel 32m + 16 hi + kc; rounded
+            // in pairs, stored as halves
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                const uint32_t pk = pk_bf16(f32x2{ke[i], ke[i + 1]});
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int cr = 8 * sg + i + j, kc = cr & 15, hi = cr >> 4;
+                    *reinterpret_cast<uint16_t *>(P + kPKE + m * 1024 + swz(kc + 16 * (t >> 2)) * 16 +
+                                                  ((t & 3) + 4 * hi) * 2) = (uint16_t)(pk >> (16 * j));
+                }
+            }
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 dR = mma32(kr_h, ki_h, z);
+            const f32x4 dRT = mma32(ki_h, kr_h, z);
+            const f32x4 dAQT = mma32(ki_h, qr_h, z);
+            reinterpret_cast<f32x4 *>(X + m * kXWave + kXR)[lane] = dR;
+            reinterpret_cast<f32x4 *>(X + m * kXWave + kXRT)[lane] = dRT;
+            reinterpret_cast<f32x4 *>(X + m * kXWave + kXAQ)[lane] = dAQT;
+
+            // raw K_b = k e^{G}, Q_b = q e^{G} in the consumer's 16x16x32 A order
+            // (k step m); gamma = e^{G_last} from token 15; the v tile
+            bf16x4 kb4[2], qb4[2];
+            float dec[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                dec[i] = __builtin_amdgcn_exp2f(gf[i]);
+                kb4[i >> 2][i & 3] = (__bf16)(kf[i] * dec[i]);
+                qb4[i >> 2][i & 3] = (__bf16)(qf[i] * dec[i]);
+            }
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int q4 = 2 * sg + hf;                 // which 4 channels of the 32
+                const int gd = q4 & 3, e0 = (q4 >> 2) * 4;  // consumer lane group, element
+                const int o = m * 1024 + swz(t + 16 * gd) * 16 + e0 * 2;
+                *reinterpret_cast<bf16x4 *>(P + kPKB + o) = kb4[hf];
+                *reinterpret_cast<bf16x4 *>(P + kPQB + o) = qb4[hf];
+            }
+            if (t == 15) {
+                float *gm = reinterpret_cast<float *>(P + kPGM) + 32 * m + 8 * sg;
+                *reinterpret_cast<f32x4 *>(gm) = f32x4{dec[0], dec[1], dec[2], dec[3]};
+                *reinterpret_cast<f32x4 *>(gm + 4) = f32x4{dec[4], dec[5], dec[6], dec[7]};
+            }
+            *reinterpret_cast<u32x4 *>(P + kPV + t * kVRow + (32 * m + 8 * sg) * 2) =
+                valid ? va : u32x4{0u, 0u, 0u, 0u};
+            if (c + 1 < nch) read_inputs(c + 1);
+        };
+        // ticks past the last chunk only keep the barrier count
+#pragma unroll 1
+        for (int tau = 0; tau < ticks; tau += kFSlots) {
+            if (tau < nch) stage_a(tau, std::integral_constant<int, 0>{});
             tick_sync();
+            if (tau + 1 < ticks) {
+                if (tau + 1 < nch) stage_a(tau + 1, std::integral_constant<int, 1>{});
+                tick_sync();
+            }
+            if (tau + 2 < ticks) {
+                if (tau + 2 < nch) stage_a(tau + 2, std::integral_constant<int, 2>{});
+                tick_sync();
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // nothing still landing in LDS at exit
         return;
@@ -421,17 +435,19 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                         sb[4 + r] = (__bf16)st[u][2 * p + 1][r];
                     }
                     xk[u] = mma32(kb, sb, xk[u]);
-                    xq[u] = mma32(qb, sb, xq[u]);
+                    // operands swapped: (Q_b S^T)^T, lane (token, g) holds value channels 4g..4g+3
+                    xq[u] = mma32(sb, qb, xq[u]);
                 }
             }
             const f32x4 rk4 = *reinterpret_cast<const f32x4 *>(L + kPSC + 16 * g);
-            const f32x4 rq4 = *reinterpret_cast<const f32x4 *>(L + kPSC + 64 + 16 * g);
+            const float rq1 = reinterpret_cast<const float *>(L + kPSC + 64)[col];
             const bf16x8 ab = *reinterpret_cast<const bf16x8 *>(L + kPAB + lane * 16);
             const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(L + kPAQ + lane * 16);
             const bf16x4 ab_h = {ab[0], ab[1], ab[2], ab[3]}, ab_l = {ab[4], ab[5], ab[6], ab[7]};
             const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]}, aq_l = {aq[4], aq[5], aq[6], aq[7]};
             bf16x4 eh[2], el[2];
-            const int64_t rstride = (int64_t)H * kD;
+            // output row of this lane's token: value channels 32w + 16u + 4g .. +3 of tile u
+            uint16_t *orow = out + ((int64_t)(t0 + col) * H + h) * kD + 32 * w + 4 * g;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int vcol = 32 * w + 16 * u + col;
@@ -441,7 +457,7 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                     const uint16_t vr =
                         *reinterpret_cast<const uint16_t *>(L + kPV + (4 * g + r) * kVRow + vcol * 2);
                     eb[r] = bf16_bits_to_f32(vr) - rk4[r] * xk[u][r];  // rows past the end hold zeros
-                    xq[u][r] *= rq4[r];
+                    xq[u][r] *= rq1;
                 }
                 bf16x4 eb_h, eb_l, e_h, e_l;
                 split4t_packed(eb, eb_h, eb_l);
@@ -452,21 +468,13 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
                 split4t_packed(E, e_h, e_l);
                 eh[u] = e_h;
                 el[u] = e_l;
-                f32x4 O = mma16(aq_h, e_h, xq[u]);
-                O = mma16(aq_l, e_h, O);
-                O = mma16(aq_h, e_l, O);
-                uint16_t *orow = out + ((int64_t)(t0 + 4 * g) * H + h) * kD + vcol;
+                // O^T = (Q_b S^T)^T Diag(rq) + E'^T (A^qk / Diag(rk))^T: the D-layout E tiles are
+                // the A operand of the transposed product, the stored A^qk block its B operand
+                f32x4 O = mma16(e_h, aq_h, xq[u]);
+                O = mma16(e_h, aq_l, O);
+                O = mma16(e_l, aq_h, O);
                 const u32x2 ob = {pk_bf16(f32x2{O[0], O[1]}), pk_bf16(f32x2{O[2], O[3]})};
-                const uint16_t o4[4] = {(uint16_t)ob[0], (uint16_t)(ob[0] >> 16), (uint16_t)ob[1],
-                                        (uint16_t)(ob[1] >> 16)};
-                if (len == kC) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) orow[r * rstride] = o4[r];
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (4 * g + r < len) orow[r * rstride] = o4[r];
-                }
+                if (col < len) *reinterpret_cast<u32x2 *>(orow + 16 * u) = ob;
             }
             // S^T <- Diag(gamma) S^T + K_end^T E'
 #pragma unroll
