@@ -103,8 +103,11 @@ def time_path(call, path, steps, warmup):
     """Run `steps` timed forwards on `path`; returns wall ms per step and the
     event-measured average ms of each kernel call."""
     import torch
-    if path in ("fused", "recurrent"):
-        stages = [("kf_fused" if path == "fused" else "kr_recurrent", call.run)]
+    if path in ("fused", "recurrent", "segmented"):
+        # the segmented pass is one library call (chunk map, single pass over
+        # segments, segment scan, output correction); its interval is reported whole
+        stages = [({"fused": "kf_fused", "recurrent": "kr_recurrent", "segmented": "kf_fused_seg+finish"}[path],
+                   call.run)]
     else:
         stages = [("k1_mfma", call.prepare), ("k2_mfma", call.recur)]
     for _ in range(warmup):
@@ -131,7 +134,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5", "d1"])
-    ap.add_argument("--path", default="auto", choices=["auto", "fused", "split", "recurrent"],
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "split", "recurrent", "segmented"],
                     help="kernels of the timed step (auto: the library's rule)")
     ap.add_argument("--bf16-resident-state", action="store_true",
                     help="two-kernel path with the recurrence's state rounded to bf16 between chunks")
@@ -166,8 +169,12 @@ def main():
     if path == "auto":  # the library's rule, include/kda.h
         if w.T_tot <= kda.RECURRENT_MAX_AVG_TOKENS * w.N:
             path = "recurrent"
+        elif w.N * w.H >= kda.FUSED_MIN_PAIRS:
+            path = "fused"
         else:
-            path = "fused" if w.N * w.H >= kda.FUSED_MIN_PAIRS else "split"
+            n_c = sum((L + 15) // 16 for L in w.seq_lens) if not w.packed else (w.T_tot + 15 * w.N) // 16
+            seg_len = max(16, -(-n_c * w.H // 256))
+            path = "segmented" if n_c >= 2 * seg_len * w.N else "split"
     other = "split" if path != "split" else "fused"
     calls = {p: kda.prepare_call(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu, path=p,
                                  bf16_resident_state=args.bf16_resident_state and p == "split")
@@ -191,13 +198,13 @@ def main():
 
     work = algorithmic_work(w, bf16_resident_state=args.bf16_resident_state)
     bytes_of = {"k1_mfma": work["k1_bytes"], "k2_mfma": work["k2_bytes"], "kf_fused": work["kf_bytes"],
-                "kr_recurrent": work["kf_bytes"]}
+                "kr_recurrent": work["kf_bytes"], "kf_fused_seg+finish": work["kf_bytes"]}
     per_kernel = {}
     for name, ms in kern_ms.items():
         gbs = bytes_of[name] / (ms * 1e-3) / 1e9
         ent = {"avg_ms": round(ms, 4), "algorithmic_bytes": bytes_of[name], "achieved_GBps": round(gbs, 1),
                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-        if name in ("k2_mfma", "kf_fused"):
+        if name in ("k2_mfma", "kf_fused", "kf_fused_seg+finish"):
             fl = work["flops_split"] if name == "k2_mfma" else work["flops"]
             tf = fl / (ms * 1e-3) / 1e12
             ent.update({"algorithmic_flops": fl, "achieved_TFLOPs": round(tf, 2),

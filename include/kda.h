@@ -111,14 +111,31 @@ enum {
      * between updates does (FlashKDA deep-dive, section 3), instead of
      * carrying it in fp32. For measuring that choice; implies the two-kernel
      * path and is not valid with fp32 compute or another path flag. */
-    KDA_FLAG_BF16_RESIDENT_STATE = 32u
+    KDA_FLAG_BF16_RESIDENT_STATE = 32u,
+    /* bf16-compute kda_fwd: run the segmented single pass, for few (sequence,
+     * head) pairs over long sequences. Every sequence is cut into segments of
+     * equal chunk count, chosen so that about 256 (segment, head) workgroups
+     * run at once. Each segment runs the single-pass kernel twice over the
+     * same prepared chunks: from a zero state (the first segment: the initial
+     * state) with the inputs, and from the identity with v = 0, which gives
+     * the segment's key-space transfer (the product form of the transition,
+     * Doubleword page, section 4.1). A scan over the segments then forms each
+     * segment's true incoming state and the final state, and a last kernel
+     * adds the incoming state's contribution to the outputs. The workspace
+     * holds the chunk map, three fp32 [128][128] matrices per (segment, head)
+     * and a bf16 [B*T][H][128] buffer. Not valid with fp32 compute, another
+     * path flag or KDA_FLAG_BF16_RESIDENT_STATE, or for kda_fwd_prepare /
+     * kda_fwd_recur. */
+    KDA_FLAG_SEGMENTED = 64u
 };
 /* Without a path flag, kda_fwd runs the token-by-token kernel when the
  * sequences average at most KDA_RECURRENT_MAX_AVG_TOKENS tokens (batch mode:
  * seqlen; packed: T_tot / num_seqs), else, for bf16 compute, the single-pass
  * kernel when num_seqs * num_heads >= KDA_FUSED_MIN_PAIRS (enough (sequence,
- * head) pairs to occupy the GPU's compute units one pair each) and the
- * two-kernel path otherwise; fp32 compute uses the fp32 two-kernel path. The two paths evaluate the same chunkwise equations and
+ * head) pairs to occupy the GPU's compute units one pair each), the segmented
+ * single pass when fewer pairs hold sequences long enough for at least two
+ * segments each on average, and the two-kernel path otherwise; fp32 compute
+ * uses the fp32 two-kernel path. The two paths evaluate the same chunkwise equations and
  * agree to bf16 rounding; they are not bitwise identical (the single pass
  * applies the L2 normalisation after its in-chunk products instead of
  * before). */
@@ -156,9 +173,12 @@ typedef struct kda_desc {
  * function; no GPU call). The size is an upper bound computed from B, T, N
  * and H only, because the chunk count of a packed batch depends on device-side
  * cu_seqlens: at most (T_tot + 15 N) / 16 chunks. Unless flags hold
- * KDA_FLAG_FUSED or KDA_FLAG_RECURRENT, it covers the two-kernel path, so the
- * same workspace also serves kda_fwd_prepare / kda_fwd_recur; with either of
- * those flags it is only the chunk map (a few hundred bytes plus 8 (N + 1)). Returns 0 if the
+ * KDA_FLAG_FUSED, KDA_FLAG_RECURRENT or KDA_FLAG_SEGMENTED, it covers the
+ * two-kernel path, so the same workspace also serves kda_fwd_prepare /
+ * kda_fwd_recur, and also the segmented single pass when kda_fwd would pick
+ * it; with KDA_FLAG_FUSED or KDA_FLAG_RECURRENT it is only the chunk map (a
+ * few hundred bytes plus 8 (N + 1)), with KDA_FLAG_SEGMENTED the segmented
+ * pass's workspace. Returns 0 if the
  * description itself is invalid (NULL, bad shape, dtype or flags).
  */
 size_t kda_fwd_workspace_size(const kda_desc_t *desc);

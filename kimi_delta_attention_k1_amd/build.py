@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_ref.hip", "kda_mfma.hip", "kda_fused.hip", "kda_recurrent.hip"]
+SOURCES = ["kda_api.hip", "kda_ref.hip", "kda_mfma.hip", "kda_fused.hip", "kda_recurrent.hip", "kda_seg.hip"]
 ARCH = "gfx950"
 
 

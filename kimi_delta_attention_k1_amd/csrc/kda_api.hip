@@ -25,7 +25,7 @@ Range range_of(const void *p, size_t bytes)
 bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-enum Path { kSplit, kFused, kRecurrent };
+enum Path { kSplit, kFused, kRecurrent, kSeg };
 
 struct Shape {
     int64_t T_tot, n_c_max;
@@ -34,13 +34,24 @@ struct Shape {
 };
 
 // Which kernels kda_fwd runs (the rule is stated with KDA_FUSED_MIN_PAIRS).
-Path pick_path(const kda_desc_t *d, bool f32_path, int64_t T_tot)
+// Segmented single pass without a flag: fewer pairs than KDA_FUSED_MIN_PAIRS and
+// at least two segments per sequence on average.
+bool seg_worth(const kda_desc_t *d, int64_t n_c_max)
+{
+    const int64_t L = kda::seg_len_for(n_c_max, d->num_heads);
+    return n_c_max >= 2 * L * d->num_seqs;
+}
+
+Path pick_path(const kda_desc_t *d, bool f32_path, int64_t T_tot, int64_t n_c_max)
 {
     if (d->flags & KDA_FLAG_RECURRENT) return kRecurrent;
     if (d->flags & KDA_FLAG_FUSED) return kFused;
+    if (d->flags & KDA_FLAG_SEGMENTED) return kSeg;
     if (d->flags & (KDA_FLAG_SPLIT | KDA_FLAG_BF16_RESIDENT_STATE)) return kSplit;
     if (T_tot <= (int64_t)KDA_RECURRENT_MAX_AVG_TOKENS * d->num_seqs) return kRecurrent;
-    if (!f32_path && d->num_seqs * (int64_t)d->num_heads >= KDA_FUSED_MIN_PAIRS) return kFused;
+    if (f32_path) return kSplit;
+    if (d->num_seqs * (int64_t)d->num_heads >= KDA_FUSED_MIN_PAIRS) return kFused;
+    if (seg_worth(d, n_c_max)) return kSeg;
     return kSplit;
 }
 
@@ -55,12 +66,12 @@ kda_status_t check_desc(const kda_desc_t *d, bool varlen, Shape *out)
         (d->state_dtype != KDA_DTYPE_BF16 && d->state_dtype != KDA_DTYPE_FP32))
         return KDA_ERR_BAD_DTYPE;
     const uint32_t known = KDA_FLAG_FP32_COMPUTE | KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT |
-                           KDA_FLAG_SCALAR_GATE | KDA_FLAG_BF16_RESIDENT_STATE;
+                           KDA_FLAG_SCALAR_GATE | KDA_FLAG_BF16_RESIDENT_STATE | KDA_FLAG_SEGMENTED;
     if (d->flags & ~known) return KDA_ERR_BAD_ARG;
     const bool f32_path = d->io_dtype == KDA_DTYPE_FP32 || (d->flags & KDA_FLAG_FP32_COMPUTE);
-    const uint32_t paths = d->flags & (KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT);
+    const uint32_t paths = d->flags & (KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT | KDA_FLAG_SEGMENTED);
     if (paths & (paths - 1)) return KDA_ERR_BAD_ARG;  // more than one path flag
-    if ((d->flags & KDA_FLAG_FUSED) && f32_path) return KDA_ERR_BAD_ARG;
+    if ((d->flags & (KDA_FLAG_FUSED | KDA_FLAG_SEGMENTED)) && f32_path) return KDA_ERR_BAD_ARG;
     if ((d->flags & KDA_FLAG_BF16_RESIDENT_STATE) && (f32_path || (paths & ~(uint32_t)KDA_FLAG_SPLIT)))
         return KDA_ERR_BAD_ARG;
     int64_t T_tot, n_c_max;
@@ -81,7 +92,7 @@ kda_status_t check_desc(const kda_desc_t *d, bool varlen, Shape *out)
     out->T_tot = T_tot;
     out->n_c_max = n_c_max;
     out->f32_path = f32_path;
-    out->path = pick_path(d, f32_path, T_tot);
+    out->path = pick_path(d, f32_path, T_tot, n_c_max);
     return KDA_OK;
 }
 
@@ -98,10 +109,14 @@ extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc)
         // the single-pass and token-by-token paths need no units, but without
         // their flags the same description is also valid for the two-stage
         // entry points
-        const bool units = !(desc->flags & (KDA_FLAG_FUSED | KDA_FLAG_RECURRENT));
+        const bool units = !(desc->flags & (KDA_FLAG_FUSED | KDA_FLAG_RECURRENT | KDA_FLAG_SEGMENTED));
         const bool look = units && kda::use_lookahead(desc->num_seqs, desc->num_heads, s.f32_path,
                                                        (desc->flags & KDA_FLAG_BF16_RESIDENT_STATE) != 0);
         size_t b = kda::ws_layout(desc->num_seqs, desc->num_heads, units ? s.n_c_max : 0, s.f32_path, look).total;
+        if (s.path == kSeg) {
+            const size_t bs = kda::ws_layout_seg(desc->num_seqs, desc->num_heads, s.n_c_max, s.T_tot).total;
+            if (bs > b) b = bs;
+        }
         if (b > best) best = b;
     }
     return best;
@@ -120,7 +135,7 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     const bool varlen = cu_seqlens != nullptr;
     kda_status_t st = check_desc(desc, varlen, &s);
     if (st != KDA_OK) return st;
-    if (stages != (kPrepare | kRecur) && (desc->flags & (KDA_FLAG_FUSED | KDA_FLAG_RECURRENT)))
+    if (stages != (kPrepare | kRecur) && (desc->flags & (KDA_FLAG_FUSED | KDA_FLAG_RECURRENT | KDA_FLAG_SEGMENTED)))
         return KDA_ERR_BAD_ARG;
     const Path path = stages == (kPrepare | kRecur) ? s.path : kSplit;
     const bool no_units = path != kSplit;
@@ -141,7 +156,8 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     if (!workspace) return KDA_ERR_WORKSPACE;
     const bool look =
         !no_units && kda::use_lookahead(N, H, s.f32_path, (desc->flags & KDA_FLAG_BF16_RESIDENT_STATE) != 0);
-    const WsLayout lay = kda::ws_layout(N, H, no_units ? 0 : s.n_c_max, s.f32_path, look);
+    const WsLayout lay = path == kSeg ? kda::ws_layout_seg(N, H, s.n_c_max, s.T_tot)
+                                      : kda::ws_layout(N, H, no_units ? 0 : s.n_c_max, s.f32_path, look);
     if (workspace_bytes < lay.total || !aligned(workspace, KDA_WORKSPACE_ALIGN)) return KDA_ERR_WORKSPACE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g_raw, sgate ? esz : 16) ||
         !aligned(out, 16) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(beta_raw, esz))
@@ -177,6 +193,12 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     p.lay = lay;
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (path == kSeg) {
+        if (kda::launch_chunk_map(p, hs) != hipSuccess) return KDA_ERR_HIP;
+        if (s.T_tot > 0 && kda::launch_fused_seg(p, hs) != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_seg_finish(p, hs) != hipSuccess) return KDA_ERR_HIP;
+        return KDA_OK;
+    }
     if (path == kFused || path == kRecurrent) {
         if (kda::launch_chunk_map(p, hs) != hipSuccess) return KDA_ERR_HIP;
         if ((path == kFused ? kda::launch_fused(p, hs) : kda::launch_recurrent(p, hs)) != hipSuccess)

@@ -41,6 +41,7 @@ constexpr int kFCons = 4;                             // consumer waves (32 valu
 constexpr int kFPrep = 4;                             // stage-A waves
 constexpr int kFSolve = 2;                            // stage-B waves
 constexpr int kFThreads = 64 * (kFCons + kFPrep + kFSolve);  // 640
+constexpr int kFThreadsSeg = kFThreads + 64 * kFCons;         // 896: + the transfer-run consumers
 constexpr int kFIn = 4;                               // input chunks in flight per prep wave
 constexpr int kFSlots = 3;                            // prepared-chunk slots (stage A steps through them unrolled)
 constexpr int kFDma = 5;                              // global-to-LDS loads per chunk per prep wave
@@ -86,15 +87,28 @@ __device__ __forceinline__ float sum_rows4(float x)
 
 // SG: scalar gate, g_raw is [T][H] and its one value per token and head applies to
 // every key channel (Gated DeltaNet, Doubleword section 3)
-template <typename TSt, bool SG>
-__global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                                      const uint16_t *__restrict__ v,
-                                                      const uint16_t *__restrict__ graw,
-                                                      const uint16_t *__restrict__ braw, const TSt *s0, TSt *s1,
-                                                      uint16_t *__restrict__ out,
-                                                      const int32_t *__restrict__ tok_off,
-                                                      const int32_t *__restrict__ chunk_off, int H, float lb,
-                                                      float scale)
+//
+// SEG: one workgroup per (time segment, head) instead of per (sequence, head); a
+// sequence's chunks are cut into segments of seg_len chunks (segment g of sequence
+// n is the g-th entry after seg_off[n]). The state entering a segment is not known
+// yet, so the segment runs twice over the same prepared chunks, and the state
+// recurrence being linear in (S, v) makes the two runs add up to the true one:
+//   waves 0-3  : from S = 0 (segment 0: the initial state) with the inputs v,
+//                writing the outputs o0 to `out` and the final state S0 to sfin;
+//   waves 10-13: from S = I with v = 0, i.e. the key-space transfer of the
+//                segment, writing y_t = Phi_t (s qhat_t) to ybuf and the segment's
+//                transfer Phi to phi.
+// With S_in the true incoming state, S_t = S_in Phi_t + S0_t, hence
+// o_t = o0_t + S_in y_t; the scan and correction kernels (kda_seg.hip) finish it.
+// Segment 0 starts from the known initial state, so its waves 10-13 only keep
+// the barrier count.
+template <typename TSt, bool SG, bool SEG>
+__global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ graw, const uint16_t *__restrict__ braw, const TSt *s0, TSt *s1,
+    uint16_t *__restrict__ out, const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off, int H,
+    float lb, float scale, const int32_t *__restrict__ seg_off, int N, int seg_len, float *__restrict__ sfin,
+    float *__restrict__ phi, uint16_t *__restrict__ ybuf)
 {
     __shared__ __attribute__((aligned(1024))) char lds[kFLds];
     char *const slots = lds;
@@ -104,12 +118,25 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
     // the wave index is uniform over the wave: keep it scalar so role branches and
     // the address arithmetic built on it stay in scalar registers
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = blockIdx.x / H, h = blockIdx.x % H;
-    const int c0 = chunk_off[n], nch = chunk_off[n + 1] - c0;
-    const int tb = tok_off[n], te = tok_off[n + 1];
+    const int h = blockIdx.x % H;
+    int n, nch, tb, seg = 0, gseg = 0;
+    if constexpr (SEG) {
+        seg = blockIdx.x / H;
+        if (seg >= seg_off[N]) return;  // past the last segment: uniform, before any barrier
+        n = find_seq(seg_off, N, seg);
+        gseg = seg - seg_off[n];
+        const int cs = gseg * seg_len;
+        nch = min(seg_len, chunk_off[n + 1] - chunk_off[n] - cs);
+        tb = tok_off[n] + cs * kC;
+    } else {
+        n = blockIdx.x / H;
+        nch = chunk_off[n + 1] - chunk_off[n];
+        tb = tok_off[n];
+    }
+    const int te = tok_off[n + 1];
     const int ticks = nch > 0 ? nch + 2 : 0;
 
-    if (w >= kFCons + kFPrep) {
+    if (w >= kFCons + kFPrep && w < kFCons + kFPrep + kFSolve) {
         // ================================================================ stage-B waves
         if (nch == 0) return;  // uniform over the workgroup: no barrier is entered
         const int role = w - kFCons - kFPrep;
@@ -179,7 +206,7 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
         }
         return;
     }
-    if (w >= kFCons) {
+    if (w >= kFCons && w < kFCons + kFPrep) {
         // ================================================================ stage-A waves
         if (nch == 0) return;  // uniform over the workgroup: no barrier is entered
         const int m = w - kFCons;
@@ -397,21 +424,35 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
     }
 
     // ==================================================================== consumers
-    // Lane (col, g) of consumer wave w holds, for column tile u, rows 4g..4g+3 of
-    // the 16x16 state tiles st[u][t] = S^T[16t .., 32w + 16u + col] (D layout).
+    // Lane (col, g) of consumer wave cw holds, for column tile u, rows 4g..4g+3 of
+    // the 16x16 state tiles st[u][t] = S^T[16t .., 32cw + 16u + col] (D layout).
+    // MODE 0: the whole sequence; MODE 1: a segment's run from S = 0 (segment 0: the
+    // initial state); MODE 2: a segment's transfer run, from S = I with v = 0.
+    auto consume = [&](auto mode_tag, const int cw) {
+    constexpr int MODE = decltype(mode_tag)::value;
     const int g = lane >> 4, col = lane & 15, sl = swz(lane);
-    const int64_t sbase = (((int64_t)n * H + h) * kD + 32 * w + col) * kD + 4 * g;
+    const int64_t sbase = (((int64_t)n * H + h) * kD + 32 * cw + col) * kD + 4 * g;
+    // segment states and transfers: [segment][head][128][128] fp32
+    const int64_t fbase = (((int64_t)seg * H + h) * kD + 32 * cw + col) * kD + 4 * g;
     f32x4 st[2][8];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) st[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (s0 != nullptr) {
+        for (int t = 0; t < 8; ++t) {
+            if constexpr (MODE == 2) {  // identity: S^T[16t + 4g + r][32cw + 16u + col]
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[u][t][r] = (16 * t + 4 * g + r == 32 * cw + 16 * u + col) ? 1.f : 0.f;
+            } else {
+                st[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    if (MODE != 2 && s0 != nullptr && gseg == 0) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int t = 0; t < 8; ++t) st[u][t] = ld_state4(s0 + sbase + (int64_t)16 * kD * u + 16 * t);
     }
+    uint16_t *const obuf = MODE == 2 ? ybuf : out;
 #pragma unroll 1
     for (int tau = 0; tau < ticks; ++tau) {
         if (tau >= 2) {
@@ -447,16 +488,20 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
             const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]}, aq_l = {aq[4], aq[5], aq[6], aq[7]};
             bf16x4 eh[2], el[2];
             // output row of this lane's token: value channels 32w + 16u + 4g .. +3 of tile u
-            uint16_t *orow = out + ((int64_t)(t0 + col) * H + h) * kD + 32 * w + 4 * g;
+            uint16_t *orow = obuf + ((int64_t)(t0 + col) * H + h) * kD + 32 * cw + 4 * g;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const int vcol = 32 * w + 16 * u + col;
+                const int vcol = 32 * cw + 16 * u + col;
                 f32x4 eb;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const uint16_t vr =
-                        *reinterpret_cast<const uint16_t *>(L + kPV + (4 * g + r) * kVRow + vcol * 2);
-                    eb[r] = bf16_bits_to_f32(vr) - rk4[r] * xk[u][r];  // rows past the end hold zeros
+                    if constexpr (MODE == 2) {
+                        eb[r] = -rk4[r] * xk[u][r];
+                    } else {
+                        const uint16_t vr =
+                            *reinterpret_cast<const uint16_t *>(L + kPV + (4 * g + r) * kVRow + vcol * 2);
+                        eb[r] = bf16_bits_to_f32(vr) - rk4[r] * xk[u][r];  // rows past the end hold zeros
+                    }
                     xq[u][r] *= rq1;
                 }
                 bf16x4 eb_h, eb_l, e_h, e_l;
@@ -493,30 +538,64 @@ __global__ __launch_bounds__(kFThreads) void kf_fused(const uint16_t *__restrict
         // consumers write no LDS and use every value they read before this point
         bar_sync();
     }
-    if (s1) {
+    if constexpr (MODE == 0) {
+        if (s1) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) st_state4(s1 + sbase + (int64_t)16 * kD * u + 16 * t, st[u][t]);
+        }
+    } else {
+        float *const fin = MODE == 1 ? sfin : phi;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) st_state4(s1 + sbase + (int64_t)16 * kD * u + 16 * t, st[u][t]);
+            for (int t = 0; t < 8; ++t)
+                *reinterpret_cast<f32x4 *>(fin + fbase + (int64_t)16 * kD * u + 16 * t) = st[u][t];
+    }
+    };
+    if constexpr (SEG) {
+        if (w < kFCons) {
+            consume(std::integral_constant<int, 1>{}, w);
+        } else if (nch > 0) {  // transfer-run waves
+            if (gseg > 0) {
+                consume(std::integral_constant<int, 2>{}, w - (kFCons + kFPrep + kFSolve));
+            } else {
+#pragma unroll 1
+                for (int tau = 0; tau < ticks; ++tau) bar_sync();
+            }
+        }
+    } else {
+        consume(std::integral_constant<int, 0>{}, w);
     }
 }
 
-template <typename TSt, bool SG>
+template <typename TSt, bool SG, bool SEG>
 static hipError_t launch_fused_t(const Problem &p, hipStream_t s)
 {
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
-    hipLaunchKernelGGL((kf_fused<TSt, SG>), dim3((unsigned)(p.N * p.H)), dim3(kFThreads), 0, s, (const uint16_t *)p.q,
-                       (const uint16_t *)p.k, (const uint16_t *)p.v, (const uint16_t *)p.g,
+    const int32_t *seg = SEG ? reinterpret_cast<const int32_t *>(p.ws + p.lay.seg_off) : nullptr;
+    float *sfin = SEG ? reinterpret_cast<float *>(p.ws + p.lay.sfin) : nullptr;
+    float *phi = SEG ? reinterpret_cast<float *>(p.ws + p.lay.phi) : nullptr;
+    uint16_t *ybuf = SEG ? reinterpret_cast<uint16_t *>(p.ws + p.lay.ybuf) : nullptr;
+    const int64_t groups = (SEG ? p.lay.seg_max : p.N) * p.H;
+    hipLaunchKernelGGL((kf_fused<TSt, SG, SEG>), dim3((unsigned)groups), dim3(SEG ? kFThreadsSeg : kFThreads), 0, s,
+                       (const uint16_t *)p.q, (const uint16_t *)p.k, (const uint16_t *)p.v, (const uint16_t *)p.g,
                        (const uint16_t *)p.beta, (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H,
-                       p.lb, p.scale);
+                       p.lb, p.scale, seg, (int)p.N, (int)p.lay.seg_len, sfin, phi, ybuf);
     return hipGetLastError();
 }
 
-hipError_t launch_fused(const Problem &p, hipStream_t s)
+template <bool SEG>
+static hipError_t launch_fused_any(const Problem &p, hipStream_t s)
 {
-    if (p.scalar_gate) return p.st_bf16 ? launch_fused_t<uint16_t, true>(p, s) : launch_fused_t<float, true>(p, s);
-    return p.st_bf16 ? launch_fused_t<uint16_t, false>(p, s) : launch_fused_t<float, false>(p, s);
+    if (p.scalar_gate)
+        return p.st_bf16 ? launch_fused_t<uint16_t, true, SEG>(p, s) : launch_fused_t<float, true, SEG>(p, s);
+    return p.st_bf16 ? launch_fused_t<uint16_t, false, SEG>(p, s) : launch_fused_t<float, false, SEG>(p, s);
 }
+
+hipError_t launch_fused(const Problem &p, hipStream_t s) { return launch_fused_any<false>(p, s); }
+hipError_t launch_fused_seg(const Problem &p, hipStream_t s) { return launch_fused_any<true>(p, s); }
 
 }  // namespace kda

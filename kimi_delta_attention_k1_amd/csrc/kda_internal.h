@@ -56,9 +56,28 @@ inline bool use_lookahead(int64_t N, int64_t H, bool f32_path, bool bf16_residen
     return !f32_path && !bf16_resident && N * H < kLookMaxPairs;
 }
 
+// Segmented single pass (few (sequence, head) pairs, long sequences): each sequence
+// is cut into segments of seg_len chunks so that about kSegTargetGroups workgroups
+// run at once. Workspace after the chunk map:
+//   seg_off [N+1] int32             exclusive scan of segments per sequence
+//   sfin    [seg_max][H][128][128]  fp32, segment's final state from S = 0 (seg 0: S_0)
+//   phi     [seg_max][H][128][128]  fp32, segment's key-space transfer
+//   sin     [seg_max][H][128][128]  fp32, true state entering the segment
+//   ybuf    [T_tot][H][128]         bf16, y_t = Phi_t (s qhat_t) within the segment
+constexpr int64_t kSegTargetGroups = 256;
+constexpr int64_t kSegMinChunks = 16;
+inline int64_t seg_len_for(int64_t n_c_max, int64_t H)
+{
+    const int64_t l = (n_c_max * H + kSegTargetGroups - 1) / kSegTargetGroups;
+    return l > kSegMinChunks ? l : kSegMinChunks;
+}
+// upper bound of sum_n ceil(chunks_n / L) given sum_n chunks_n <= n_c_max
+inline int64_t seg_max_for(int64_t N, int64_t n_c_max, int64_t seg_len) { return n_c_max / seg_len + N; }
+
 struct WsLayout {
     size_t tok_off, chunk_off, units, unit_bytes, ket, total;
-    int64_t n_c_max;
+    size_t seg_off, sfin, phi, sin, ybuf;
+    int64_t n_c_max, seg_len, seg_max;
 };
 
 inline WsLayout ws_layout(int64_t N, int64_t H, int64_t n_c_max, bool f32_path, bool lookahead)
@@ -72,6 +91,25 @@ inline WsLayout ws_layout(int64_t N, int64_t H, int64_t n_c_max, bool f32_path, 
     const size_t end = L.units + L.unit_bytes * (size_t)H * (size_t)n_c_max;
     L.ket = lookahead ? align_up(end, 128) : 0;
     L.total = lookahead ? L.ket + kKetBytes * (size_t)H * (size_t)n_c_max : end;
+    L.seg_off = L.sfin = L.phi = L.sin = L.ybuf = 0;
+    L.seg_len = L.seg_max = 0;
+    return L;
+}
+
+// layout of the segmented single pass (no units)
+inline WsLayout ws_layout_seg(int64_t N, int64_t H, int64_t n_c_max, int64_t T_tot)
+{
+    WsLayout L = ws_layout(N, H, 0, false, false);
+    L.n_c_max = n_c_max;
+    L.seg_len = seg_len_for(n_c_max, H);
+    L.seg_max = seg_max_for(N, n_c_max, L.seg_len);
+    const size_t st = (size_t)L.seg_max * (size_t)H * kD * kD * sizeof(float);
+    L.seg_off = L.units;
+    L.sfin = align_up(L.seg_off + sizeof(int32_t) * (size_t)(N + 1), 128);
+    L.phi = L.sfin + st;
+    L.sin = L.phi + st;
+    L.ybuf = L.sin + st;
+    L.total = L.ybuf + (size_t)T_tot * (size_t)H * kD * sizeof(uint16_t);
     return L;
 }
 
@@ -98,6 +136,8 @@ hipError_t launch_prep_mfma(const Problem &p, hipStream_t s);   // bf16 K1
 hipError_t launch_recur_mfma(const Problem &p, hipStream_t s);  // bf16 K2
 hipError_t launch_fused(const Problem &p, hipStream_t s);       // bf16 single pass
 hipError_t launch_recurrent(const Problem &p, hipStream_t s);   // token-by-token (decode)
+hipError_t launch_fused_seg(const Problem &p, hipStream_t s);   // bf16 segmented single pass
+hipError_t launch_seg_finish(const Problem &p, hipStream_t s);  // segment scan and output correction
 
 // ---------------------------------------------------------------------------
 // Device helpers

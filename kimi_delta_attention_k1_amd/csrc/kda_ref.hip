@@ -16,7 +16,8 @@ namespace kda {
 // With cu_seqlens: tok_off[n] = min(T_tot, max_{m<=n} clamp(cu[m], 0, T_tot)),
 // tok_off[0] = 0, tok_off[N] = T_tot; flag = 1 iff cu already had that form.
 // Without: tok_off[n] = n*T. chunk_off is the exclusive scan of
-// ceil((tok_off[n+1]-tok_off[n]) / 16).
+// ceil((tok_off[n+1]-tok_off[n]) / 16); on the segmented path seg_off is the
+// exclusive scan of ceil(chunks of sequence n / seg_len).
 // ---------------------------------------------------------------------------
 constexpr int kMapThreads = 1024;
 
@@ -41,7 +42,8 @@ __device__ __forceinline__ int block_scan_incl(int x, int *sh, bool is_max)
 __global__ __launch_bounds__(kMapThreads) void k0_chunk_map(const int32_t *__restrict__ cu, int N, int T,
                                                              int T_tot, int32_t *__restrict__ hdr,
                                                              int32_t *__restrict__ tok_off,
-                                                             int32_t *__restrict__ chunk_off)
+                                                             int32_t *__restrict__ chunk_off, int seg_len,
+                                                             int32_t *__restrict__ seg_off)
 {
     __shared__ int sh[kMapThreads + 1];
     const int t = threadIdx.x;
@@ -84,6 +86,21 @@ __global__ __launch_bounds__(kMapThreads) void k0_chunk_map(const int32_t *__res
         carry += sh[kMapThreads];
         __syncthreads();
     }
+    if (seg_off != nullptr) {
+        // pass 3: segment offsets, the exclusive scan of ceil(chunks / seg_len)
+        __threadfence_block();
+        __syncthreads();
+        carry = 0;
+        for (int base = 0; base <= N; base += kMapThreads) {
+            const int n = base + t;
+            int cnt = 0;
+            if (n < N) cnt = (chunk_off[n + 1] - chunk_off[n] + seg_len - 1) / seg_len;
+            int s = block_scan_incl(cnt, sh, false);
+            if (n <= N) seg_off[n] = carry + s - cnt;
+            carry += sh[kMapThreads];
+            __syncthreads();
+        }
+    }
     if (t == 0) hdr[0] = bad ? 0 : 1;
 }
 
@@ -92,8 +109,9 @@ hipError_t launch_chunk_map(const Problem &p, hipStream_t s)
     int32_t *hdr = reinterpret_cast<int32_t *>(p.ws);
     int32_t *tok = reinterpret_cast<int32_t *>(p.ws + p.lay.tok_off);
     int32_t *chk = reinterpret_cast<int32_t *>(p.ws + p.lay.chunk_off);
+    int32_t *seg = p.lay.seg_len > 0 ? reinterpret_cast<int32_t *>(p.ws + p.lay.seg_off) : nullptr;
     hipLaunchKernelGGL(k0_chunk_map, dim3(1), dim3(kMapThreads), 0, s, p.cu, (int)p.N, (int)p.T,
-                       (int)p.T_tot, hdr, tok, chk);
+                       (int)p.T_tot, hdr, tok, chk, (int)p.lay.seg_len, seg);
     return hipGetLastError();
 }
 

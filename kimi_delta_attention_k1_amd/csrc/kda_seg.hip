@@ -1,0 +1,182 @@
+// kda_seg.hip -- the two kernels that finish the segmented single pass.
+//
+// The segmented pass (kf_fused with SEG, kda_fused.hip) cuts every sequence into
+// segments and runs each segment from a zero state (segment 0: the initial
+// state), giving its outputs o0, its final state S0 and, from a second run with
+// state I and v = 0, its key-space transfer Phi and the vectors y_t = Phi_t (s qhat_t).
+// The state recurrence of the Doubleword page "You Could Have Come Up with Kimi
+// Delta Attention" (section 4) is linear in (S, v) for fixed q, k, alpha and beta,
+// and its transition is the product form of section 4.1, so with S_in the true
+// state entering segment g:
+//   S at token t = S_in Phi_t + S0_t,      o_t = o0_t + S_in y_t,
+//   S_in(g+1) = S_in(g) Phi_g + S0_g,      S_in(0) = initial state.
+// kseg_scan walks that chain over the segments of each (sequence, head) with fp32
+// matrix-core products; kseg_correct adds S_in y_t to the outputs of every
+// segment after the first.
+#include "kda_mfma_common.h"
+
+namespace kda {
+
+constexpr int kScanRows = 16;   // value rows per scan workgroup
+constexpr int kScanLd = kD + 4;  // padded LDS row (floats)
+
+__device__ __forceinline__ f32x4 mma4f(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One workgroup (4 waves) per (sequence, head, 16 value rows). The state rows stay
+// in LDS; each step forms S Phi_g + S0_g: wave w owns key columns [32w, 32w+32) as
+// two 16x16 tiles and contracts over the 128 rows of Phi_g in 16x16x4 fp32 steps.
+template <typename TSt>
+__global__ __launch_bounds__(256) void kseg_scan(const TSt *s0, TSt *s1, const int32_t *__restrict__ seg_off, int H,
+                                                 const float *__restrict__ sfin, const float *__restrict__ phi,
+                                                 float *__restrict__ sin)
+{
+    __shared__ float S[kScanRows][kScanLd];
+    const int n = blockIdx.x / H, h = blockIdx.x % H, r0 = blockIdx.y * kScanRows;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
+    const int first = seg_off[n], G = seg_off[n + 1] - first;
+    const int64_t mat = (int64_t)kD * kD;
+    auto seg_off_of = [&](int sg) { return ((int64_t)sg * H + h) * mat; };
+
+    // state entering segment 1: segment 0's run started from the initial state
+    for (int i = tid; i < kScanRows * kD; i += 256) {
+        const int r = i / kD, c = i % kD;
+        float x;
+        if (G > 0)
+            x = sfin[seg_off_of(first) + (int64_t)(r0 + r) * kD + c];
+        else
+            x = s0 ? ld_elem(s0, ((int64_t)n * H + h) * mat + (int64_t)(r0 + r) * kD + c) : 0.f;
+        S[r][c] = x;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int gi = 1; gi < G; ++gi) {
+        const float *P = phi + seg_off_of(first + gi);
+        const float *Z = sfin + seg_off_of(first + gi);
+        float *Sin = sin + seg_off_of(first + gi);
+        for (int i = tid; i < kScanRows * kD; i += 256) Sin[(int64_t)(r0 + i / kD) * kD + i % kD] = S[i / kD][i % kD];
+        f32x4 acc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[j][r] = Z[(int64_t)(r0 + 4 * g + r) * kD + 32 * w + 16 * j + col];
+#pragma unroll 8
+        for (int ks = 0; ks < kD / 4; ++ks) {
+            const float a = S[col][4 * ks + g];  // A[m = row][k]
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[j] = mma4f(a, P[(int64_t)(4 * ks + g) * kD + 32 * w + 16 * j + col], acc[j]);
+        }
+        __syncthreads();  // every wave has read S
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[4 * g + r][32 * w + 16 * j + col] = acc[j][r];
+        __syncthreads();
+    }
+    if (s1) {
+        for (int i = tid; i < kScanRows * kD; i += 256)
+            st_elem(s1, ((int64_t)n * H + h) * mat + (int64_t)(r0 + i / kD) * kD + i % kD, S[i / kD][i % kD]);
+    }
+}
+
+constexpr int kCorrWaves = 8;
+constexpr int kCorrTok = 32 * kCorrWaves;  // tokens per workgroup
+constexpr int kCorrLd = kD + 8;            // padded LDS row (bf16): rows 4 banks apart
+
+// One workgroup per (segment after the first, head, 256 tokens): o_t += S_in y_t.
+// S_in is split into bf16 hi and lo halves in LDS; wave w takes 32 tokens and forms
+// (S_in y^T) for them as 16x16 tiles (rows: value channels, columns: tokens), so
+// each lane ends with four consecutive value channels of one token.
+__global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__restrict__ out,
+                                                                 const uint16_t *__restrict__ ybuf,
+                                                                 const float *__restrict__ sin,
+                                                                 const int32_t *__restrict__ tok_off,
+                                                                 const int32_t *__restrict__ seg_off, int N, int H,
+                                                                 int seg_len)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t Shi[kD][kCorrLd];
+    __shared__ __attribute__((aligned(16))) uint16_t Slo[kD][kCorrLd];
+    const int seg = blockIdx.x / H, h = blockIdx.x % H;
+    if (seg >= seg_off[N]) return;
+    const int n = find_seq(seg_off, N, seg), gi = seg - seg_off[n];
+    if (gi == 0) return;
+    const int tb = tok_off[n] + gi * seg_len * kC;
+    const int te = min(tok_off[n + 1], tb + seg_len * kC);
+    const int tlo = tb + blockIdx.y * kCorrTok;
+    if (tlo >= te) return;  // uniform over the workgroup, before any barrier
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
+    const float *Sg = sin + ((int64_t)seg * H + h) * kD * kD;
+    for (int i = tid; i < kD * kD / 4; i += 64 * kCorrWaves) {
+        const f32x4 x = reinterpret_cast<const f32x4 *>(Sg)[i];
+        const int r = (4 * i) / kD, c = (4 * i) % kD;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t u = __float_as_uint(x[e]);
+            const uint16_t hi = (uint16_t)(u >> 16);  // truncated: x - hi is exact in fp32
+            Shi[r][c + e] = hi;
+            Slo[r][c + e] = f32_to_bf16_bits(x[e] - __uint_as_float(u & 0xffff0000u));
+        }
+    }
+    __syncthreads();
+
+    const int64_t rowst = (int64_t)H * kD;
+#pragma unroll 1
+    for (int tt = 0; tt < 2; ++tt) {
+        const int t = tlo + 32 * w + 16 * tt + col;  // this lane's token (B column, D column)
+        const bool live = t < te;
+        const uint16_t *yrow = ybuf + ((int64_t)(live ? t : tb) * H + h) * kD;
+        f32x4 acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kD / 32; ++ks) {
+            const bf16x8 yb = *reinterpret_cast<const bf16x8 *>(yrow + 32 * ks + 8 * g);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(&Shi[16 * j + col][32 * ks + 8 * g]);
+                const bf16x8 al = *reinterpret_cast<const bf16x8 *>(&Slo[16 * j + col][32 * ks + 8 * g]);
+                acc[j] = mma32(ah, yb, acc[j]);
+                acc[j] = mma32(al, yb, acc[j]);
+            }
+        }
+        if (live) {
+            uint16_t *orow = out + (int64_t)t * rowst + (int64_t)h * kD;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                u32x2 *p = reinterpret_cast<u32x2 *>(orow + 16 * j + 4 * g);
+                const u32x2 o = *p;
+                const f32x2 lo = {bf_lo(o[0]) + acc[j][0], bf_hi(o[0]) + acc[j][1]};
+                const f32x2 hi = {bf_lo(o[1]) + acc[j][2], bf_hi(o[1]) + acc[j][3]};
+                *p = u32x2{pk_bf16(lo), pk_bf16(hi)};
+            }
+        }
+    }
+}
+
+template <typename TSt>
+static hipError_t launch_seg_finish_t(const Problem &p, hipStream_t s)
+{
+    const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
+    const int32_t *seg = reinterpret_cast<const int32_t *>(p.ws + p.lay.seg_off);
+    const float *sfin = reinterpret_cast<const float *>(p.ws + p.lay.sfin);
+    const float *phi = reinterpret_cast<const float *>(p.ws + p.lay.phi);
+    float *sin = reinterpret_cast<float *>(p.ws + p.lay.sin);
+    hipLaunchKernelGGL(kseg_scan<TSt>, dim3((unsigned)(p.N * p.H), kD / kScanRows), dim3(256), 0, s,
+                       (const TSt *)p.s0, (TSt *)p.s1, seg, p.H, sfin, phi, sin);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    const int64_t blocks = (p.lay.seg_len * kC + kCorrTok - 1) / kCorrTok;
+    hipLaunchKernelGGL(kseg_correct, dim3((unsigned)(p.lay.seg_max * p.H), (unsigned)blocks), dim3(64 * kCorrWaves),
+                       0, s, (uint16_t *)p.out, (const uint16_t *)(p.ws + p.lay.ybuf), (const float *)sin, tok, seg,
+                       (int)p.N, p.H, (int)p.lay.seg_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_finish(const Problem &p, hipStream_t s)
+{
+    return p.st_bf16 ? launch_seg_finish_t<uint16_t>(p, s) : launch_seg_finish_t<float>(p, s);
+}
+
+}  // namespace kda

@@ -142,7 +142,12 @@ def _desc(**kw):
     (dict(lb=float("nan")), BAD_ARG),
     (dict(desc=dict(scale=0.0)), BAD_ARG),
     (dict(desc=dict(scale=float("inf"))), BAD_ARG),
-    (dict(desc=dict(flags=64)), BAD_ARG),                    # unknown flag bit
+    (dict(desc=dict(flags=128)), BAD_ARG),                   # unknown flag bit
+    (dict(desc=dict(flags=kda.FLAG_SEGMENTED | kda.FLAG_FUSED)), BAD_ARG),
+    (dict(desc=dict(flags=kda.FLAG_SEGMENTED | kda.FLAG_SPLIT)), BAD_ARG),
+    (dict(desc=dict(flags=kda.FLAG_SEGMENTED | kda.FLAG_FP32_COMPUTE)), BAD_ARG),
+    (dict(desc=dict(flags=kda.FLAG_SEGMENTED | kda.FLAG_BF16_RESIDENT_STATE)), BAD_ARG),
+    (dict(desc=dict(io_dtype=1, flags=kda.FLAG_SEGMENTED)), BAD_ARG),  # fp32 I/O has no segmented pass
     (dict(desc=dict(flags=kda.FLAG_BF16_RESIDENT_STATE | kda.FLAG_FUSED)), BAD_ARG),
     (dict(desc=dict(flags=kda.FLAG_BF16_RESIDENT_STATE | kda.FLAG_RECURRENT)), BAD_ARG),
     (dict(desc=dict(flags=kda.FLAG_BF16_RESIDENT_STATE | kda.FLAG_FP32_COMPUTE)), BAD_ARG),
@@ -191,7 +196,32 @@ def test_path_flags_and_workspace(lib):
         kda.workspace_size(1, 64, 1, 1, path="both")
 
 
-@pytest.mark.parametrize("flag", [kda.FLAG_FUSED, kda.FLAG_RECURRENT])
+def _seg_layout(N, H, T_tot, n_c):
+    """Chunk map, segment offsets, three fp32 [128][128] matrices per (segment, head)
+    and a bf16 [T_tot][H][128] buffer; segments of max(16, ceil(n_c H / 256)) chunks,
+    at most n_c // L + N of them."""
+    L = max(16, -(-n_c * H // 256))
+    smax = n_c // L + N
+    seg = _layout(N, H, 0, 0)
+    sfin = (seg + 4 * (N + 1) + 127) // 128 * 128
+    return sfin + 3 * smax * H * 128 * 128 * 4 + T_tot * H * 128 * 2
+
+
+def test_segmented_path_workspace(lib):
+    # C4: one sequence of 131072 tokens, H=32 -> 8192 chunks, segments of 1024 chunks
+    assert kda.workspace_size(1, 131072, 1, 32, path="segmented") == _seg_layout(1, 32, 131072, 8192)
+    # the automatic rule picks the segmented pass there; the size covers it and the split path
+    split = _layout(1, 32, 8192, 14848, look=True)
+    assert kda.workspace_size(1, 131072, 1, 32) == max(split, _seg_layout(1, 32, 131072, 8192))
+    # packed few-pair batch: n_c bound (T + 15 N) / 16
+    n_c = (5000 + 15 * 3) // 16
+    assert kda.workspace_size(1, 5000, 3, 2, path="segmented") == _seg_layout(3, 2, 5000, n_c)
+    # 256 pairs: no segments needed, the size is the split path's
+    assert kda.workspace_size(1, 65536, 8, 32) == _layout(8, 32, (65536 + 15 * 8) // 16, 14848)
+    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32, path="segmented") == 0  # invalid: fp32 I/O
+
+
+@pytest.mark.parametrize("flag", [kda.FLAG_FUSED, kda.FLAG_RECURRENT, kda.FLAG_SEGMENTED])
 def test_stage_entry_points_reject_single_call_paths(lib, flag):
     desc = _desc(flags=flag)
     f = Fake(dict(x=1 << 20))

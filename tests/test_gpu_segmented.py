@@ -1,0 +1,125 @@
+"""GPU parity of the segmented single pass (path="segmented", KDA_FLAG_SEGMENTED)
+against the fp64 oracle, through the C ABI.
+
+The segmented pass cuts each sequence into time segments, runs every segment
+from a zero state and from the identity (the segment's key-space transfer),
+then scans the segments and corrects the outputs; the result must meet the
+same bounds as every bf16 path (max|x_gpu - x_ref| <= 1e-2 max|x_ref| + 1e-3
+for o and the final state). Segments are 16 chunks long or more, so the small
+cases below already span several segments and ragged segment ends.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_k1_amd as kda
+from kimi_delta_attention_k1_amd import workloads
+from tests.gpu_helpers import bf16_tol, compare, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _banner(name):
+    print(f"\n[case] segmented: {name}", flush=True)
+
+
+def test_c2_full_auto_picks_segmented(gpu):
+    _banner("c2 B=1 T=4096 H=16, automatic rule, all pairs")
+    w = workloads.c2()
+    ref = run_oracle(w)
+    o, s = run_gpu(w, gpu)  # 16 pairs of 256 chunks: the rule picks the segmented pass
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    compare(w, o, s, ref, bf16_tol, "c2 segmented (auto)")
+    o2, s2 = run_gpu(w, gpu, path="segmented")
+    assert torch.equal(o, o2) and torch.equal(s, s2)  # the rule did pick it; runs are deterministic
+
+
+def test_c4_long_context_sampled_and_against_split(gpu):
+    _banner("c4 long context T=131072, H=32 (sampled heads), segmented vs split")
+    w = workloads.c4()
+    ref = run_oracle(w, pairs=[(0, 0), (0, 13), (0, 31)])
+    o, s = run_gpu(w, gpu, path="segmented")
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    compare(w, o, s, ref, bf16_tol, "c4 segmented sampled")
+    o2, s2 = run_gpu(w, gpu, path="split")
+    for a, b, what in ((o, o2, "o"), (s, s2, "state")):
+        a32, b32 = a.float(), b.float()
+        err = (a32 - b32).abs().max().item()
+        tol = 1e-2 * b32.abs().max().item() + 1e-3
+        print(f"c4 segmented vs split {what}: max diff {err:.3e} (bound {tol:.3e})", flush=True)
+        assert err <= tol
+
+
+@pytest.mark.parametrize("lb", [-5.0, -1.0, 0.0])
+def test_ragged_segments_and_empty_sequences(gpu, lb):
+    _banner(f"ragged lengths around the 256-token segment, empty sequences, lb={lb}")
+    lens = [0, 1, 255, 256, 257, 700, 1000, 33, 0, 513]
+    w = workloads.make(lens, 3, seed=11, init_std=0.02, beta_mean=0.5, lower_bound=lb)
+    ref = run_oracle(w)
+    o, s = run_gpu(w, gpu, path="segmented")
+    compare(w, o, s, ref, bf16_tol, f"segmented ragged lb={lb}")
+    for n in (0, 8):  # empty sequences: final = initial
+        assert torch.equal(s[n].cpu(), w.initial_state[n])
+
+
+def test_batch_mode_no_initial_state_no_final(gpu):
+    _banner("batch mode B=2 T=1000 H=4, no initial state, no final state")
+    w = workloads.make([1000, 1000], 4, seed=12, packed=False)
+    ref = run_oracle(w)
+    o, s = run_gpu(w, gpu, path="segmented", final=False)
+    assert s is None
+    compare(w, o, None, ref, bf16_tol, "segmented batch mode")
+
+
+def test_bf16_state_streaming_in_place(gpu):
+    _banner("bf16 states, in-place streaming over two calls of 1200 + 900 tokens, H=2")
+    w = workloads.make([2100], 2, seed=13, init_std=0.02)
+    ref = run_oracle(w)
+    dev = gpu
+    st = w.initial_state.to(dev, torch.bfloat16).contiguous()
+    cut = 1200
+    outs = []
+    for a, e in ((0, cut), (cut, 2100)):
+        sl = lambda t: t[a:e].contiguous().to(dev)  # noqa: E731
+        o, _ = kda.fwd(sl(w.q)[None], sl(w.k)[None], sl(w.v)[None], sl(w.g_raw)[None], sl(w.beta_raw)[None],
+                       lower_bound=w.lower_bound, initial_state=st, final_state=st, path="segmented")
+        outs.append(o[0])
+    torch.cuda.synchronize(dev)
+    o = torch.cat(outs)
+    compare(w, o, st.float(), ref, bf16_tol, "segmented bf16 streaming in place")
+
+
+def test_scalar_gate(gpu):
+    _banner("scalar per-head gate, lengths 600 and 300, H=3")
+    w = workloads.make([600, 300], 3, seed=14, init_std=0.02, scalar_gate=True)
+    ref = run_oracle(w)
+    o, s = run_gpu(w, gpu, path="segmented")
+    compare(w, o, s, ref, bf16_tol, "segmented scalar gate")
+    # bitwise the same as the same gate broadcast over the 128 channels
+    wb = workloads.make([600, 300], 3, seed=14, init_std=0.02, scalar_gate=True)
+    wb.g_raw = wb.g_raw[..., None].expand(*wb.g_raw.shape, 128).contiguous()
+    ob, sb = run_gpu(wb, gpu, path="segmented")
+    assert torch.equal(o, ob) and torch.equal(s, sb)
+
+
+def test_guard_bytes_around_outputs_and_workspace(gpu):
+    _banner("guard bytes after out, final state and the workspace")
+    w = workloads.make([300, 45], 2, seed=15, init_std=0.02)
+    dev = gpu
+    T, H = w.T_tot, w.H
+    cu = w.cu_seqlens().to(dev)
+    ws_bytes = kda.workspace_size(1, T, w.N, H, path="segmented")
+    guard = 4096
+    ws = torch.full((ws_bytes + guard,), 0x5A, dtype=torch.uint8, device=dev)
+    ob = torch.full((T * H * 128 + guard // 2,), 7.0, dtype=torch.bfloat16, device=dev)
+    sb = torch.full((w.N * H * 128 * 128 + guard // 4,), 3.0, dtype=torch.float32, device=dev)
+    out = ob[:T * H * 128].view(T, H, 128)
+    fs = sb[:w.N * H * 128 * 128].view(w.N, H, 128, 128)
+    o, s = kda.fwd(w.q.to(dev), w.k.to(dev), w.v.to(dev), w.g_raw.to(dev), w.beta_raw.to(dev),
+                   lower_bound=w.lower_bound, initial_state=w.initial_state.to(dev), cu_seqlens=cu, out=out,
+                   final_state=fs, workspace=ws[:ws_bytes], path="segmented")
+    torch.cuda.synchronize(dev)
+    assert (ws[ws_bytes:] == 0x5A).all()
+    assert (ob[T * H * 128:] == 7.0).all()
+    assert (sb[w.N * H * 128 * 128:] == 3.0).all()
+    compare(w, o, s, run_oracle(w), bf16_tol, "segmented with guards")
