@@ -85,10 +85,11 @@ constexpr int kCorrWaves = 8;
 constexpr int kCorrTok = 32 * kCorrWaves;  // tokens per workgroup
 constexpr int kCorrLd = kD + 8;            // padded LDS row (bf16): rows 4 banks apart
 
-// One workgroup per (segment after the first, head, 256 tokens): o_t += S_in y_t.
-// S_in is split into bf16 hi and lo halves in LDS; wave w takes 32 tokens and forms
-// (S_in y^T) for them as 16x16 tiles (rows: value channels, columns: tokens), so
-// each lane ends with four consecutive value channels of one token.
+// o_t += S_in y_t for every segment after the first. Workgroup (segment, head, j)
+// splits S_in once into bf16 hi and lo halves in LDS, then walks the segment's
+// token blocks j, j + gridDim.y, ... of 256 tokens: wave w takes 32 tokens and
+// forms (S_in y^T) for them as 16x16 tiles (rows: value channels, columns:
+// tokens), so each lane ends with four consecutive value channels of one token.
 __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__restrict__ out,
                                                                  const uint16_t *__restrict__ ybuf,
                                                                  const float *__restrict__ sin,
@@ -104,53 +105,73 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
     if (gi == 0) return;
     const int tb = tok_off[n] + gi * seg_len * kC;
     const int te = min(tok_off[n + 1], tb + seg_len * kC);
-    const int tlo = tb + blockIdx.y * kCorrTok;
-    if (tlo >= te) return;  // uniform over the workgroup, before any barrier
+    if (tb + (int)blockIdx.y * kCorrTok >= te) return;  // uniform over the workgroup, before any barrier
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
     const float *Sg = sin + ((int64_t)seg * H + h) * kD * kD;
     for (int i = tid; i < kD * kD / 4; i += 64 * kCorrWaves) {
         const f32x4 x = reinterpret_cast<const f32x4 *>(Sg)[i];
         const int r = (4 * i) / kD, c = (4 * i) % kD;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t u = __float_as_uint(x[e]);
-            const uint16_t hi = (uint16_t)(u >> 16);  // truncated: x - hi is exact in fp32
-            Shi[r][c + e] = hi;
-            Slo[r][c + e] = f32_to_bf16_bits(x[e] - __uint_as_float(u & 0xffff0000u));
-        }
+        const u32x4 u = __builtin_bit_cast(u32x4, x);
+        // hi truncated (x - hi is exact in fp32), lo the remainder rounded
+        const u32x2 hi = {__builtin_amdgcn_perm(u[1], u[0], 0x07060302u), __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
+        const f32x2 r01 = {x[0] - __uint_as_float(u[0] & 0xffff0000u), x[1] - __uint_as_float(u[1] & 0xffff0000u)};
+        const f32x2 r23 = {x[2] - __uint_as_float(u[2] & 0xffff0000u), x[3] - __uint_as_float(u[3] & 0xffff0000u)};
+        *reinterpret_cast<u32x2 *>(&Shi[r][c]) = hi;
+        *reinterpret_cast<u32x2 *>(&Slo[r][c]) = u32x2{pk_bf16(r01), pk_bf16(r23)};
     }
     __syncthreads();
 
     const int64_t rowst = (int64_t)H * kD;
 #pragma unroll 1
-    for (int tt = 0; tt < 2; ++tt) {
-        const int t = tlo + 32 * w + 16 * tt + col;  // this lane's token (B column, D column)
-        const bool live = t < te;
-        const uint16_t *yrow = ybuf + ((int64_t)(live ? t : tb) * H + h) * kD;
-        f32x4 acc[8];
+    for (int tlo = tb + blockIdx.y * kCorrTok; tlo < te; tlo += gridDim.y * kCorrTok) {
+        // every load of the block's two token tiles is issued before any product, so
+        // each wave keeps 2 x (512 B y + 256 B o) per lane-row in flight at once
+        bf16x8 yb[2][kD / 32];
+        u32x2 ov[2][8];
+        bool live[2];
+        uint16_t *orow[2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = tlo + 32 * w + 16 * tt + col;  // this lane's token (B column, D column)
+            live[tt] = t < te;
+            const int tc = live[tt] ? t : tb;
+            const uint16_t *yrow = ybuf + ((int64_t)tc * H + h) * kD;
+            orow[tt] = out + (int64_t)tc * rowst + (int64_t)h * kD;
+#pragma unroll
+            for (int ks = 0; ks < kD / 32; ++ks) yb[tt][ks] = *reinterpret_cast<const bf16x8 *>(yrow + 32 * ks + 8 * g);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ov[tt][j] = *reinterpret_cast<const u32x2 *>(orow[tt] + 16 * j + 4 * g);
+        }
+        f32x4 acc[2][8];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < kD / 32; ++ks) {
-            const bf16x8 yb = *reinterpret_cast<const bf16x8 *>(yrow + 32 * ks + 8 * g);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 8; ++j) {  // each S_in fragment pair serves both token tiles
                 const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(&Shi[16 * j + col][32 * ks + 8 * g]);
                 const bf16x8 al = *reinterpret_cast<const bf16x8 *>(&Slo[16 * j + col][32 * ks + 8 * g]);
-                acc[j] = mma32(ah, yb, acc[j]);
-                acc[j] = mma32(al, yb, acc[j]);
-            }
-        }
-        if (live) {
-            uint16_t *orow = out + (int64_t)t * rowst + (int64_t)h * kD;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                u32x2 *p = reinterpret_cast<u32x2 *>(orow + 16 * j + 4 * g);
-                const u32x2 o = *p;
-                const f32x2 lo = {bf_lo(o[0]) + acc[j][0], bf_hi(o[0]) + acc[j][1]};
-                const f32x2 hi = {bf_lo(o[1]) + acc[j][2], bf_hi(o[1]) + acc[j][3]};
-                *p = u32x2{pk_bf16(lo), pk_bf16(hi)};
+                for (int tt = 0; tt < 2; ++tt) {
+                    acc[tt][j] = mma32(ah, yb[tt][ks], acc[tt][j]);
+                    acc[tt][j] = mma32(al, yb[tt][ks], acc[tt][j]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep one k-step's LDS fragments live at a time
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            if (live[tt]) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const u32x2 o = ov[tt][j];
+                    const f32x2 lo = {bf_lo(o[0]) + acc[tt][j][0], bf_hi(o[0]) + acc[tt][j][1]};
+                    const f32x2 hi = {bf_lo(o[1]) + acc[tt][j][2], bf_hi(o[1]) + acc[tt][j][3]};
+                    *reinterpret_cast<u32x2 *>(orow[tt] + 16 * j + 4 * g) = u32x2{pk_bf16(lo), pk_bf16(hi)};
+                }
             }
         }
     }
@@ -167,7 +188,10 @@ static hipError_t launch_seg_finish_t(const Problem &p, hipStream_t s)
     hipLaunchKernelGGL(kseg_scan<TSt>, dim3((unsigned)(p.N * p.H), kD / kScanRows), dim3(256), 0, s,
                        (const TSt *)p.s0, (TSt *)p.s1, seg, p.H, sfin, phi, sin);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    const int64_t blocks = (p.lay.seg_len * kC + kCorrTok - 1) / kCorrTok;
+    // token blocks of a segment spread over enough workgroups to fill the GPU about twice
+    const int64_t per_seg = (p.lay.seg_len * kC + kCorrTok - 1) / kCorrTok;
+    const int64_t want = (2 * kSegTargetGroups + p.lay.seg_max * p.H - 1) / (p.lay.seg_max * p.H);
+    const int64_t blocks = want < per_seg ? want : per_seg;
     hipLaunchKernelGGL(kseg_correct, dim3((unsigned)(p.lay.seg_max * p.H), (unsigned)blocks), dim3(64 * kCorrWaves),
                        0, s, (uint16_t *)p.out, (const uint16_t *)(p.ws + p.lay.ybuf), (const float *)sin, tok, seg,
                        (int)p.N, p.H, (int)p.lay.seg_len);
