@@ -64,7 +64,13 @@ def algorithmic_work(w, bf16_resident_state=False):
     kf = th * (4 * 256 + 2 + 256) + st
     flops = units * (3 * 2 * 16 * 128 * 128 + 2 * 2 * 16 * 16 * 128 + 128 * 128)
     flops_split = flops + (units * 2 * 16 * 16 * 128 if look else 0)
-    return dict(units=units, k1_bytes=k1, k2_bytes=k2, kf_bytes=kf, flops=flops, flops_split=flops_split)
+    # segmented pass: the single pass's inputs and outputs (the initial state read, if
+    # given; the final state comes from the finish stage, whose only algorithmic bytes
+    # are that write: its segment-state, transfer and y traffic is the price of the split)
+    fin = w.N * H * 128 * 128 * 4
+    seg = kf - fin
+    return dict(units=units, k1_bytes=k1, k2_bytes=k2, kf_bytes=kf, flops=flops, flops_split=flops_split,
+                seg_bytes=seg, fin_bytes=fin)
 
 
 def traffic_for(kernel, workload):
@@ -103,11 +109,10 @@ def time_path(call, path, steps, warmup):
     """Run `steps` timed forwards on `path`; returns wall ms per step and the
     event-measured average ms of each kernel call."""
     import torch
-    if path in ("fused", "recurrent", "segmented"):
-        # the segmented pass is one library call (chunk map, single pass over
-        # segments, segment scan, output correction); its interval is reported whole
-        stages = [({"fused": "kf_fused", "recurrent": "kr_recurrent", "segmented": "kf_fused_seg+finish"}[path],
-                   call.run)]
+    if path in ("fused", "recurrent"):
+        stages = [("kf_fused" if path == "fused" else "kr_recurrent", call.run)]
+    elif path == "segmented":  # chunk map + single pass over segments; segment scan + output correction
+        stages = [("kf_fused_seg", call.seg_pass), ("kseg_finish", call.seg_finish)]
     else:
         stages = [("k1_mfma", call.prepare), ("k2_mfma", call.recur)]
     for _ in range(warmup):
@@ -198,13 +203,14 @@ def main():
 
     work = algorithmic_work(w, bf16_resident_state=args.bf16_resident_state)
     bytes_of = {"k1_mfma": work["k1_bytes"], "k2_mfma": work["k2_bytes"], "kf_fused": work["kf_bytes"],
-                "kr_recurrent": work["kf_bytes"], "kf_fused_seg+finish": work["kf_bytes"]}
+                "kr_recurrent": work["kf_bytes"], "kf_fused_seg": work["seg_bytes"],
+                "kseg_finish": work["fin_bytes"]}
     per_kernel = {}
     for name, ms in kern_ms.items():
         gbs = bytes_of[name] / (ms * 1e-3) / 1e9
         ent = {"avg_ms": round(ms, 4), "algorithmic_bytes": bytes_of[name], "achieved_GBps": round(gbs, 1),
                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-        if name in ("k2_mfma", "kf_fused", "kf_fused_seg+finish"):
+        if name in ("k2_mfma", "kf_fused", "kf_fused_seg"):
             fl = work["flops_split"] if name == "k2_mfma" else work["flops"]
             tf = fl / (ms * 1e-3) / 1e12
             ent.update({"algorithmic_flops": fl, "achieved_TFLOPs": round(tf, 2),

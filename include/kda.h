@@ -252,6 +252,41 @@ kda_status_t kda_fwd_recur(const void *q, const void *k, const void *v,
                            void *workspace, size_t workspace_bytes,
                            void *stream);
 
+/*
+ * The two stages of kda_fwd on the segmented single pass (see
+ * KDA_FLAG_SEGMENTED), for callers that time them: kda_fwd_seg_pass runs the
+ * chunk map and the single-pass kernel over every (segment, head), writing
+ * out (complete for each sequence's first segment, without the incoming
+ * state's share elsewhere) and the segments' states, transfers and y vectors
+ * into the workspace; kda_fwd_seg_finish scans the segments (true incoming
+ * states, final_state) and adds each incoming state's share to out. On that
+ * path kda_fwd(args) is exactly kda_fwd_seg_pass(args) followed by
+ * kda_fwd_seg_finish(args), ordered as kda_fwd_prepare / kda_fwd_recur are.
+ * Both take kda_fwd's arguments with the same meaning and checks, run the
+ * segmented stages whether or not desc->flags holds KDA_FLAG_SEGMENTED, and
+ * reject any other path flag, KDA_FLAG_BF16_RESIDENT_STATE and fp32 compute
+ * with KDA_ERR_BAD_ARG. The workspace must be the size kda_fwd_workspace_size
+ * reports with KDA_FLAG_SEGMENTED.
+ */
+kda_status_t kda_fwd_seg_pass(const void *q, const void *k, const void *v,
+                              const void *g_raw, const void *beta_raw,
+                              const int32_t *cu_seqlens,
+                              const void *initial_state,
+                              void *out, void *final_state,
+                              float lower_bound,
+                              const kda_desc_t *desc,
+                              void *workspace, size_t workspace_bytes,
+                              void *stream);
+kda_status_t kda_fwd_seg_finish(const void *q, const void *k, const void *v,
+                                const void *g_raw, const void *beta_raw,
+                                const int32_t *cu_seqlens,
+                                const void *initial_state,
+                                void *out, void *final_state,
+                                float lower_bound,
+                                const kda_desc_t *desc,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_str(kda_status_t status);
 

@@ -85,7 +85,7 @@ def load_library():
     vp = ctypes.c_void_p
     lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(KdaDesc)]
-    for name in ("kda_fwd", "kda_fwd_prepare", "kda_fwd_recur"):
+    for name in ("kda_fwd", "kda_fwd_prepare", "kda_fwd_recur", "kda_fwd_seg_pass", "kda_fwd_seg_finish"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.POINTER(KdaDesc),
@@ -135,7 +135,8 @@ def _ptr(t):
 
 
 class Call:
-    """A marshalled kda_fwd argument list; run() / prepare() / recur() enqueue it.
+    """A marshalled kda_fwd argument list; run() / prepare() / recur() / seg_pass() /
+    seg_finish() enqueue it.
 
     Holds references to every tensor it points at, so the buffers stay alive
     while the object does.
@@ -158,6 +159,12 @@ class Call:
 
     def recur(self):
         self._go(self._lib.kda_fwd_recur)
+
+    def seg_pass(self):
+        self._go(self._lib.kda_fwd_seg_pass)
+
+    def seg_finish(self):
+        self._go(self._lib.kda_fwd_seg_finish)
 
 
 def fwd(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | None = None,

@@ -124,7 +124,7 @@ extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc)
 
 namespace {
 
-enum Stage { kPrepare = 1, kRecur = 2 };
+enum Stage { kPrepare = 1, kRecur = 2, kSegStage = 4 };  // kSegStage: the segmented path's stages
 
 kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw, const void *beta_raw,
                  const int32_t *cu_seqlens, const void *initial_state, void *out, void *final_state,
@@ -133,11 +133,19 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
 {
     Shape s;
     const bool varlen = cu_seqlens != nullptr;
+    const bool seg_stage = (stages & kSegStage) != 0;
+    stages &= kPrepare | kRecur;
     kda_status_t st = check_desc(desc, varlen, &s);
     if (st != KDA_OK) return st;
-    if (stages != (kPrepare | kRecur) && (desc->flags & (KDA_FLAG_FUSED | KDA_FLAG_RECURRENT | KDA_FLAG_SEGMENTED)))
+    if (seg_stage) {
+        if (s.f32_path || (desc->flags & (KDA_FLAG_SPLIT | KDA_FLAG_FUSED | KDA_FLAG_RECURRENT |
+                                          KDA_FLAG_BF16_RESIDENT_STATE)))
+            return KDA_ERR_BAD_ARG;
+    } else if (stages != (kPrepare | kRecur) &&
+               (desc->flags & (KDA_FLAG_FUSED | KDA_FLAG_RECURRENT | KDA_FLAG_SEGMENTED))) {
         return KDA_ERR_BAD_ARG;
-    const Path path = stages == (kPrepare | kRecur) ? s.path : kSplit;
+    }
+    const Path path = seg_stage ? kSeg : stages == (kPrepare | kRecur) ? s.path : kSplit;
     const bool no_units = path != kSplit;
     if (!isfinite(lower_bound) || lower_bound < KDA_LOWER_BOUND_MIN || lower_bound > KDA_LOWER_BOUND_MAX)
         return KDA_ERR_BAD_ARG;
@@ -194,9 +202,11 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (path == kSeg) {
-        if (kda::launch_chunk_map(p, hs) != hipSuccess) return KDA_ERR_HIP;
-        if (s.T_tot > 0 && kda::launch_fused_seg(p, hs) != hipSuccess) return KDA_ERR_HIP;
-        if (kda::launch_seg_finish(p, hs) != hipSuccess) return KDA_ERR_HIP;
+        if (stages & kPrepare) {
+            if (kda::launch_chunk_map(p, hs) != hipSuccess) return KDA_ERR_HIP;
+            if (s.T_tot > 0 && kda::launch_fused_seg(p, hs) != hipSuccess) return KDA_ERR_HIP;
+        }
+        if ((stages & kRecur) && kda::launch_seg_finish(p, hs) != hipSuccess) return KDA_ERR_HIP;
         return KDA_OK;
     }
     if (path == kFused || path == kRecurrent) {
@@ -230,6 +240,8 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
 extern "C" kda_status_t kda_fwd(KDA_ARGS) { return run(KDA_PASS, kPrepare | kRecur); }
 extern "C" kda_status_t kda_fwd_prepare(KDA_ARGS) { return run(KDA_PASS, kPrepare); }
 extern "C" kda_status_t kda_fwd_recur(KDA_ARGS) { return run(KDA_PASS, kRecur); }
+extern "C" kda_status_t kda_fwd_seg_pass(KDA_ARGS) { return run(KDA_PASS, kSegStage | kPrepare); }
+extern "C" kda_status_t kda_fwd_seg_finish(KDA_ARGS) { return run(KDA_PASS, kSegStage | kRecur); }
 
 extern "C" const char *kda_status_str(kda_status_t status)
 {

@@ -51,28 +51,55 @@ __global__ __launch_bounds__(256) void kseg_scan(const TSt *s0, TSt *s1, const i
         S[r][c] = x;
     }
     __syncthreads();
-#pragma unroll 1
-    for (int gi = 1; gi < G; ++gi) {
+    // the loads of step gi + 1 (Phi and S0 of the next segment) are issued before the
+    // products of step gi, so the chain over segments waits on no memory round trip
+    float pb[kD / 4][2];
+    f32x4 z[2];
+    auto load_step = [&](int gi) {
         const float *P = phi + seg_off_of(first + gi);
         const float *Z = sfin + seg_off_of(first + gi);
-        float *Sin = sin + seg_off_of(first + gi);
-        for (int i = tid; i < kScanRows * kD; i += 256) Sin[(int64_t)(r0 + i / kD) * kD + i % kD] = S[i / kD][i % kD];
-        f32x4 acc[2];
+#pragma unroll
+        for (int ks = 0; ks < kD / 4; ++ks)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) pb[ks][j] = P[(int64_t)(4 * ks + g) * kD + 32 * w + 16 * j + col];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[j][r] = Z[(int64_t)(r0 + 4 * g + r) * kD + 32 * w + 16 * j + col];
-#pragma unroll 8
+            for (int r = 0; r < 4; ++r) z[j][r] = Z[(int64_t)(r0 + 4 * g + r) * kD + 32 * w + 16 * j + col];
+    };
+    if (G > 1) load_step(1);
+#pragma unroll 1
+    for (int gi = 1; gi < G; ++gi) {
+        float *Sin = sin + seg_off_of(first + gi);
+        for (int i = tid; i < kScanRows * kD; i += 256) Sin[(int64_t)(r0 + i / kD) * kD + i % kD] = S[i / kD][i % kD];
+        float pc[kD / 4][2];
+        f32x4 zc[2];
+#pragma unroll
+        for (int ks = 0; ks < kD / 4; ++ks)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) pc[ks][j] = pb[ks][j];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) zc[j] = z[j];
+        if (gi + 1 < G) load_step(gi + 1);
+        // four independent accumulation chains per tile (k steps 4i + c go to chain c)
+        f32x4 acc[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int ks = 0; ks < kD / 4; ++ks) {
             const float a = S[col][4 * ks + g];  // A[m = row][k]
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[j] = mma4f(a, P[(int64_t)(4 * ks + g) * kD + 32 * w + 16 * j + col], acc[j]);
+            for (int j = 0; j < 2; ++j) acc[j][ks & 3] = mma4f(a, pc[ks][j], acc[j][ks & 3]);
         }
         __syncthreads();  // every wave has read S
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
+            const f32x4 sum = ((acc[j][0] + acc[j][1]) + (acc[j][2] + acc[j][3])) + zc[j];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[4 * g + r][32 * w + 16 * j + col] = acc[j][r];
+            for (int r = 0; r < 4; ++r) S[4 * g + r][32 * w + 16 * j + col] = sum[r];
+        }
         __syncthreads();
     }
     if (s1) {

@@ -34,12 +34,16 @@ KERNEL_SOURCES = {
     "k2_mfma": ("kda_mfma.hip", "kda_mfma_common.h", "kda_internal.h"),
     "kf_fused": ("kda_fused.hip", "kda_mfma_common.h", "kda_internal.h"),
     "kr_recurrent": ("kda_recurrent.hip", "kda_internal.h"),
+    "kf_fused_seg": ("kda_fused.hip", "kda_mfma_common.h", "kda_internal.h"),
+    "kseg_scan": ("kda_seg.hip", "kda_mfma_common.h", "kda_internal.h"),
+    "kseg_correct": ("kda_seg.hip", "kda_mfma_common.h", "kda_internal.h"),
 }
 # kernel-name fragments per reported kernel; the recurrence stage of the two-kernel
 # path is k2_mfma, or k2_look (its look-ahead form) when few pairs run
 SHORT = {"k1_mfma": ("kda::k1_mfma",), "k2_mfma": ("kda::k2_mfma", "kda::k2_look"),
          "kf_fused": ("kda::kf_fused",), "kr_recurrent": ("kda::kr_recurrent",),
-         "k0_chunk_map": ("kda::k0_chunk_map",), "copy": ("__amd_rocclr_copyBuffer",)}
+         "k0_chunk_map": ("kda::k0_chunk_map",), "kseg_scan": ("kda::kseg_scan",),
+         "kseg_correct": ("kda::kseg_correct",), "copy": ("__amd_rocclr_copyBuffer",)}
 
 
 def src_hash(kernel: str) -> str:
@@ -52,6 +56,9 @@ def src_hash(kernel: str) -> str:
 
 
 def short_name(kernel_name: str) -> str:
+    # the segmented instantiations of the single pass end their template list with "true>"
+    if "kda::kf_fused<" in kernel_name and kernel_name.split("(")[0].endswith("true>"):
+        return "kf_fused_seg"
     for short, keys in SHORT.items():
         if any(key in kernel_name for key in keys):
             return short

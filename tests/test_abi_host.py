@@ -230,3 +230,16 @@ def test_stage_entry_points_reject_single_call_paths(lib, flag):
         rc = fn(a, a, a, a, a, None, None, a, None, ctypes.c_float(-5.0), ctypes.byref(desc), a,
                 ctypes.c_size_t(1 << 30), None)
         assert rc == BAD_ARG, kda.status_str(rc)
+
+
+@pytest.mark.parametrize("desc_kw", [dict(flags=kda.FLAG_FUSED), dict(flags=kda.FLAG_RECURRENT),
+                                     dict(flags=kda.FLAG_SPLIT), dict(flags=kda.FLAG_BF16_RESIDENT_STATE),
+                                     dict(flags=kda.FLAG_FP32_COMPUTE), dict(io_dtype=1)])
+def test_segmented_stage_entry_points_reject_other_paths(lib, desc_kw):
+    desc = _desc(**desc_kw)
+    f = Fake(dict(x=1 << 20))
+    a = ctypes.c_void_p(f.addr["x"])
+    for fn in (lib.kda_fwd_seg_pass, lib.kda_fwd_seg_finish):
+        rc = fn(a, a, a, a, a, None, None, a, None, ctypes.c_float(-5.0), ctypes.byref(desc), a,
+                ctypes.c_size_t(1 << 30), None)
+        assert rc == BAD_ARG, kda.status_str(rc)

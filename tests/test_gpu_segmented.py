@@ -123,3 +123,20 @@ def test_guard_bytes_around_outputs_and_workspace(gpu):
     assert (ob[T * H * 128:] == 7.0).all()
     assert (sb[w.N * H * 128 * 128:] == 3.0).all()
     compare(w, o, s, run_oracle(w), bf16_tol, "segmented with guards")
+
+
+def test_stage_entry_points_compose_to_kda_fwd(gpu):
+    _banner("kda_fwd_seg_pass + kda_fwd_seg_finish == kda_fwd (bitwise), lengths 700 and 260, H=2")
+    w = workloads.make([700, 260], 2, seed=16, init_std=0.02)
+    dev = gpu
+    args = [t.to(dev) for t in (w.q, w.k, w.v, w.g_raw, w.beta_raw)]
+    cu = w.cu_seqlens().to(dev)
+    s0 = w.initial_state.to(dev)
+    whole = kda.prepare_call(*args, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu, path="segmented")
+    whole.run()
+    staged = kda.prepare_call(*args, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu, path="segmented")
+    staged.seg_pass()
+    staged.seg_finish()
+    torch.cuda.synchronize(dev)
+    assert torch.equal(whole.out, staged.out) and torch.equal(whole.final_state, staged.final_state)
+    compare(w, staged.out, staged.final_state, run_oracle(w), bf16_tol, "segmented staged")
