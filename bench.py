@@ -178,8 +178,7 @@ def main():
             path = "fused"
         else:
             n_c = sum((L + 15) // 16 for L in w.seq_lens) if not w.packed else (w.T_tot + 15 * w.N) // 16
-            seg_len = max(16, -(-n_c * w.H // 256))
-            path = "segmented" if n_c >= 2 * seg_len * w.N else "split"
+            path = "segmented" if n_c >= kda.SEGMENTED_MIN_AVG_CHUNKS * w.N else "split"
     other = "split" if path != "split" else "fused"
     calls = {p: kda.prepare_call(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu, path=p,
                                  bf16_resident_state=args.bf16_resident_state and p == "split")

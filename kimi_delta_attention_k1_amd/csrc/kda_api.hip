@@ -35,11 +35,10 @@ struct Shape {
 
 // Which kernels kda_fwd runs (the rule is stated with KDA_FUSED_MIN_PAIRS).
 // Segmented single pass without a flag: fewer pairs than KDA_FUSED_MIN_PAIRS and
-// at least two segments per sequence on average.
+// sequences of at least KDA_SEGMENTED_MIN_AVG_CHUNKS chunks on average.
 bool seg_worth(const kda_desc_t *d, int64_t n_c_max)
 {
-    const int64_t L = kda::seg_len_for(n_c_max, d->num_heads);
-    return n_c_max >= 2 * L * d->num_seqs;
+    return n_c_max >= (int64_t)KDA_SEGMENTED_MIN_AVG_CHUNKS * d->num_seqs;
 }
 
 Path pick_path(const kda_desc_t *d, bool f32_path, int64_t T_tot, int64_t n_c_max)

@@ -57,8 +57,9 @@ inline bool use_lookahead(int64_t N, int64_t H, bool f32_path, bool bf16_residen
 }
 
 // Segmented single pass (few (sequence, head) pairs, long sequences): each sequence
-// is cut into segments of seg_len chunks so that about kSegTargetGroups workgroups
-// run at once. Workspace after the chunk map:
+// is cut into G = max(2, kSegTargetGroups / pairs) segments of equal chunk count L
+// (from the average sequence), so that at most about kSegTargetGroups (segment,
+// head) workgroups, one per compute unit, run at once. Workspace after the chunk map:
 //   seg_off [N+1] int32             exclusive scan of segments per sequence
 //   sfin    [seg_max][H][128][128]  fp32, segment's final state from S = 0 (seg 0: S_0)
 //   phi     [seg_max][H][128][128]  fp32, segment's key-space transfer
@@ -66,9 +67,13 @@ inline bool use_lookahead(int64_t N, int64_t H, bool f32_path, bool bf16_residen
 //   ybuf    [T_tot][H][128]         bf16, y_t = Phi_t (s qhat_t) within the segment
 constexpr int64_t kSegTargetGroups = 256;
 constexpr int64_t kSegMinChunks = 16;
-inline int64_t seg_len_for(int64_t n_c_max, int64_t H)
+inline int64_t seg_len_for(int64_t N, int64_t H, int64_t n_c_max)
 {
-    const int64_t l = (n_c_max * H + kSegTargetGroups - 1) / kSegTargetGroups;
+    const int64_t pairs = N * H;
+    int64_t G = kSegTargetGroups / pairs;
+    if (G < 2) G = 2;
+    const int64_t avg = (n_c_max + N - 1) / N;
+    const int64_t l = (avg + G - 1) / G;
     return l > kSegMinChunks ? l : kSegMinChunks;
 }
 // upper bound of sum_n ceil(chunks_n / L) given sum_n chunks_n <= n_c_max
@@ -101,7 +106,7 @@ inline WsLayout ws_layout_seg(int64_t N, int64_t H, int64_t n_c_max, int64_t T_t
 {
     WsLayout L = ws_layout(N, H, 0, false, false);
     L.n_c_max = n_c_max;
-    L.seg_len = seg_len_for(n_c_max, H);
+    L.seg_len = seg_len_for(N, H, n_c_max);
     L.seg_max = seg_max_for(N, n_c_max, L.seg_len);
     const size_t st = (size_t)L.seg_max * (size_t)H * kD * kD * sizeof(float);
     L.seg_off = L.units;

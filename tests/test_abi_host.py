@@ -198,9 +198,10 @@ def test_path_flags_and_workspace(lib):
 
 def _seg_layout(N, H, T_tot, n_c):
     """Chunk map, segment offsets, three fp32 [128][128] matrices per (segment, head)
-    and a bf16 [T_tot][H][128] buffer; segments of max(16, ceil(n_c H / 256)) chunks,
-    at most n_c // L + N of them."""
-    L = max(16, -(-n_c * H // 256))
+    and a bf16 [T_tot][H][128] buffer; G = max(2, 256 // (N H)) segments of
+    L = max(16, ceil(ceil(n_c / N) / G)) chunks per sequence, at most n_c // L + N."""
+    G = max(2, 256 // (N * H))
+    L = max(16, -(-(-(-n_c // N)) // G))
     smax = n_c // L + N
     seg = _layout(N, H, 0, 0)
     sfin = (seg + 4 * (N + 1) + 127) // 128 * 128
@@ -208,7 +209,7 @@ def _seg_layout(N, H, T_tot, n_c):
 
 
 def test_segmented_path_workspace(lib):
-    # C4: one sequence of 131072 tokens, H=32 -> 8192 chunks, segments of 1024 chunks
+    # C4: one sequence of 131072 tokens, H=32 -> 8192 chunks, 8 segments of 1024 chunks
     assert kda.workspace_size(1, 131072, 1, 32, path="segmented") == _seg_layout(1, 32, 131072, 8192)
     # the automatic rule picks the segmented pass there; the size covers it and the split path
     split = _layout(1, 32, 8192, 14848, look=True)
@@ -218,6 +219,8 @@ def test_segmented_path_workspace(lib):
     assert kda.workspace_size(1, 5000, 3, 2, path="segmented") == _seg_layout(3, 2, 5000, n_c)
     # 256 pairs: no segments needed, the size is the split path's
     assert kda.workspace_size(1, 65536, 8, 32) == _layout(8, 32, (65536 + 15 * 8) // 16, 14848)
+    # 32 pairs of 64 chunks: below the 128-chunk average the rule keeps the split path
+    assert kda.workspace_size(2, 1024, 2, 16) == _layout(2, 16, 128, 14848, look=True)
     assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32, path="segmented") == 0  # invalid: fp32 I/O
 
 
