@@ -89,7 +89,8 @@ enum {
     KDA_FLAG_SPLIT = 2u,
     /* bf16-compute kda_fwd: run the single-pass kernel (one workgroup per
      * (sequence, head) prepares each chunk in on-chip memory and runs the
-     * recurrence on it; the workspace holds only the chunk map). Not valid
+     * recurrence on it; the workspace holds only the chunk map and the order
+     * in which the workgroups take the sequences, longest first). Not valid
      * with fp32 compute, with KDA_FLAG_SPLIT, or for kda_fwd_prepare /
      * kda_fwd_recur. */
     KDA_FLAG_FUSED = 4u,
@@ -178,9 +179,10 @@ typedef struct kda_desc {
  * KDA_FLAG_FUSED, KDA_FLAG_RECURRENT or KDA_FLAG_SEGMENTED, it covers the
  * two-kernel path, so the same workspace also serves kda_fwd_prepare /
  * kda_fwd_recur, and also the segmented single pass when kda_fwd would pick
- * it; with KDA_FLAG_FUSED or KDA_FLAG_RECURRENT it is only the chunk map (a
- * few hundred bytes plus 8 (N + 1)), with KDA_FLAG_SEGMENTED the segmented
- * pass's workspace. Returns 0 if the
+ * it; with KDA_FLAG_RECURRENT it is only the chunk map (a few hundred bytes
+ * plus 8 (N + 1)), with KDA_FLAG_FUSED the chunk map and the order in which the
+ * single pass takes the sequences (longest first, 4 N more), with
+ * KDA_FLAG_SEGMENTED the segmented pass's workspace. Returns 0 if the
  * description itself is invalid (NULL, bad shape, dtype or flags).
  */
 size_t kda_fwd_workspace_size(const kda_desc_t *desc);

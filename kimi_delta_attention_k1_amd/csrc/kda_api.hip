@@ -112,6 +112,10 @@ extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc)
         const bool look = units && kda::use_lookahead(desc->num_seqs, desc->num_heads, s.f32_path,
                                                        (desc->flags & KDA_FLAG_BF16_RESIDENT_STATE) != 0);
         size_t b = kda::ws_layout(desc->num_seqs, desc->num_heads, units ? s.n_c_max : 0, s.f32_path, look).total;
+        if (s.path == kFused) {
+            const size_t bf = kda::ws_layout_fused(desc->num_seqs, desc->num_heads).total;
+            if (bf > b) b = bf;
+        }
         if (s.path == kSeg) {
             const size_t bs = kda::ws_layout_seg(desc->num_seqs, desc->num_heads, s.n_c_max, s.T_tot).total;
             if (bs > b) b = bs;
@@ -163,8 +167,9 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     if (!workspace) return KDA_ERR_WORKSPACE;
     const bool look =
         !no_units && kda::use_lookahead(N, H, s.f32_path, (desc->flags & KDA_FLAG_BF16_RESIDENT_STATE) != 0);
-    const WsLayout lay = path == kSeg ? kda::ws_layout_seg(N, H, s.n_c_max, s.T_tot)
-                                      : kda::ws_layout(N, H, no_units ? 0 : s.n_c_max, s.f32_path, look);
+    const WsLayout lay = path == kSeg     ? kda::ws_layout_seg(N, H, s.n_c_max, s.T_tot)
+                         : path == kFused ? kda::ws_layout_fused(N, H)
+                                          : kda::ws_layout(N, H, no_units ? 0 : s.n_c_max, s.f32_path, look);
     if (workspace_bytes < lay.total || !aligned(workspace, KDA_WORKSPACE_ALIGN)) return KDA_ERR_WORKSPACE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g_raw, sgate ? esz : 16) ||
         !aligned(out, 16) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(beta_raw, esz))

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
     const uint16_t *__restrict__ graw, const uint16_t *__restrict__ braw, const TSt *s0, TSt *s1,
     uint16_t *__restrict__ out, const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off, int H,
     float lb, float scale, const int32_t *__restrict__ seg_off, int N, int seg_len, float *__restrict__ sfin,
-    float *__restrict__ phi, uint16_t *__restrict__ ybuf)
+    float *__restrict__ phi, uint16_t *__restrict__ ybuf, const int32_t *__restrict__ order)
 {
     __shared__ __attribute__((aligned(1024))) char lds[kFLds];
     char *const slots = lds;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
         nch = min(seg_len, chunk_off[n + 1] - chunk_off[n] - cs);
         tb = tok_off[n] + cs * kC;
     } else {
-        n = blockIdx.x / H;
+        n = order[blockIdx.x / H];  // longest sequences first
         nch = chunk_off[n + 1] - chunk_off[n];
         tb = tok_off[n];
     }
@@ -583,7 +583,8 @@ static hipError_t launch_fused_t(const Problem &p, hipStream_t s)
     hipLaunchKernelGGL((kf_fused<TSt, SG, SEG>), dim3((unsigned)groups), dim3(SEG ? kFThreadsSeg : kFThreads), 0, s,
                        (const uint16_t *)p.q, (const uint16_t *)p.k, (const uint16_t *)p.v, (const uint16_t *)p.g,
                        (const uint16_t *)p.beta, (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H,
-                       p.lb, p.scale, seg, (int)p.N, (int)p.lay.seg_len, sfin, phi, ybuf);
+                       p.lb, p.scale, seg, (int)p.N, (int)p.lay.seg_len, sfin, phi, ybuf,
+                       SEG ? nullptr : reinterpret_cast<const int32_t *>(p.ws + p.lay.order));
     return hipGetLastError();
 }
 

@@ -82,6 +82,7 @@ inline int64_t seg_max_for(int64_t N, int64_t n_c_max, int64_t seg_len) { return
 struct WsLayout {
     size_t tok_off, chunk_off, units, unit_bytes, ket, total;
     size_t seg_off, sfin, phi, sin, ybuf;
+    size_t order;  // single pass: sequences longest first, [N] int32 (0: not kept)
     int64_t n_c_max, seg_len, seg_max;
 };
 
@@ -97,7 +98,19 @@ inline WsLayout ws_layout(int64_t N, int64_t H, int64_t n_c_max, bool f32_path, 
     L.ket = lookahead ? align_up(end, 128) : 0;
     L.total = lookahead ? L.ket + kKetBytes * (size_t)H * (size_t)n_c_max : end;
     L.seg_off = L.sfin = L.phi = L.sin = L.ybuf = 0;
+    L.order = 0;
     L.seg_len = L.seg_max = 0;
+    return L;
+}
+
+// layout of the single pass: the chunk map and the order in which its (sequence,
+// head) workgroups take the sequences, longest first, so the ragged tail of a batch
+// with more workgroups than compute units is short ones
+inline WsLayout ws_layout_fused(int64_t N, int64_t H)
+{
+    WsLayout L = ws_layout(N, H, 0, false, false);
+    L.order = L.units;
+    L.total = align_up(L.order + sizeof(int32_t) * (size_t)N, 128);
     return L;
 }
 

@@ -17,7 +17,8 @@ namespace kda {
 // tok_off[0] = 0, tok_off[N] = T_tot; flag = 1 iff cu already had that form.
 // Without: tok_off[n] = n*T. chunk_off is the exclusive scan of
 // ceil((tok_off[n+1]-tok_off[n]) / 16); on the segmented path seg_off is the
-// exclusive scan of ceil(chunks of sequence n / seg_len).
+// exclusive scan of ceil(chunks of sequence n / seg_len); on the single pass,
+// order lists the sequences longest first.
 // ---------------------------------------------------------------------------
 constexpr int kMapThreads = 1024;
 
@@ -43,7 +44,8 @@ __global__ __launch_bounds__(kMapThreads) void k0_chunk_map(const int32_t *__res
                                                              int T_tot, int32_t *__restrict__ hdr,
                                                              int32_t *__restrict__ tok_off,
                                                              int32_t *__restrict__ chunk_off, int seg_len,
-                                                             int32_t *__restrict__ seg_off)
+                                                             int32_t *__restrict__ seg_off,
+                                                             int32_t *__restrict__ order)
 {
     __shared__ int sh[kMapThreads + 1];
     const int t = threadIdx.x;
@@ -101,6 +103,25 @@ __global__ __launch_bounds__(kMapThreads) void k0_chunk_map(const int32_t *__res
             __syncthreads();
         }
     }
+    if (order != nullptr) {
+        // pass 4: sequences by chunk count, longest first (ties: lower index first);
+        // beyond one sequence per thread the input order is kept
+        __threadfence_block();
+        __syncthreads();
+        if (N <= kMapThreads) {
+            if (t < N) {
+                const int ct = chunk_off[t + 1] - chunk_off[t];
+                int rank = 0;
+                for (int m = 0; m < N; ++m) {
+                    const int cm = chunk_off[m + 1] - chunk_off[m];
+                    rank += (cm > ct || (cm == ct && m < t)) ? 1 : 0;
+                }
+                order[rank] = t;
+            }
+        } else {
+            for (int n = t; n < N; n += kMapThreads) order[n] = n;
+        }
+    }
     if (t == 0) hdr[0] = bad ? 0 : 1;
 }
 
@@ -110,8 +131,9 @@ hipError_t launch_chunk_map(const Problem &p, hipStream_t s)
     int32_t *tok = reinterpret_cast<int32_t *>(p.ws + p.lay.tok_off);
     int32_t *chk = reinterpret_cast<int32_t *>(p.ws + p.lay.chunk_off);
     int32_t *seg = p.lay.seg_len > 0 ? reinterpret_cast<int32_t *>(p.ws + p.lay.seg_off) : nullptr;
+    int32_t *ord = p.lay.order > 0 ? reinterpret_cast<int32_t *>(p.ws + p.lay.order) : nullptr;
     hipLaunchKernelGGL(k0_chunk_map, dim3(1), dim3(kMapThreads), 0, s, p.cu, (int)p.N, (int)p.T,
-                       (int)p.T_tot, hdr, tok, chk, (int)p.lay.seg_len, seg);
+                       (int)p.T_tot, hdr, tok, chk, (int)p.lay.seg_len, seg, ord);
     return hipGetLastError();
 }
 

@@ -185,7 +185,9 @@ def test_null_desc(lib):
 
 def test_path_flags_and_workspace(lib):
     # the single pass needs only the chunk map; without its flag the size covers the split path
-    assert kda.workspace_size(1, 65536, 8, 32, path="fused") == _layout(8, 32, 0, 14848)
+    # ... plus the longest-first order of the sequences, [N] int32
+    fused = (_layout(8, 32, 0, 14848) + 4 * 8 + 127) // 128 * 128
+    assert kda.workspace_size(1, 65536, 8, 32, path="fused") == fused
     assert kda.workspace_size(1, 65536, 8, 32, path="split") == kda.workspace_size(1, 65536, 8, 32)
     assert kda.workspace_size(1, 65536, 8, 32, path="auto") == _layout(8, 32, (65536 + 15 * 8) // 16, 14848)
     assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32, path="fused") == 0  # invalid: fp32 I/O
