@@ -169,3 +169,15 @@ def test_automatic_rule_picks_fused_from_256_pairs(gpu):
     os_, ss = run_gpu(w, gpu, path="split")
     assert not torch.equal(oa, os_)  # the two paths round differently
     compare(w, oa, sa, run_oracle(w, pairs=[(0, 0), (63, 3), (31, 2)]), bf16_tol, "auto at 256 pairs")
+
+
+def test_more_sequences_than_the_longest_first_ranking(gpu):
+    """Beyond 1024 sequences the chunk map keeps the input order for the single pass."""
+    _banner("1100 packed sequences of 5..40 tokens, H=1 (input order), and 1000 (ranked)")
+    import random
+    rng = random.Random(44)
+    for count in (1100, 1000):
+        lens = [rng.randint(5, 40) for _ in range(count)]
+        w = workloads.make(lens, 1, seed=44 + count, init_std=0.02)
+        o, s = run_gpu(w, gpu, path="fused")
+        compare(w, o, s, run_oracle(w), bf16_tol, f"fused, {count} sequences")
