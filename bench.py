@@ -174,11 +174,12 @@ def main():
     if path == "auto":  # the library's rule, include/kda.h
         if w.T_tot <= kda.RECURRENT_MAX_AVG_TOKENS * w.N:
             path = "recurrent"
-        elif w.N * w.H >= kda.FUSED_MIN_PAIRS:
-            path = "fused"
         else:
             n_c = sum((L + 15) // 16 for L in w.seq_lens) if not w.packed else (w.T_tot + 15 * w.N) // 16
-            path = "segmented" if n_c >= kda.SEGMENTED_MIN_AVG_CHUNKS * w.N else "split"
+            if w.N * w.H <= kda.SEGMENTED_MAX_PAIRS and n_c >= kda.SEGMENTED_MIN_AVG_CHUNKS * w.N:
+                path = "segmented"
+            else:
+                path = "fused" if w.N * w.H >= kda.FUSED_MIN_PAIRS else "split"
     other = "split" if path != "split" else "fused"
     calls = {p: kda.prepare_call(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu, path=p,
                                  bf16_resident_state=args.bf16_resident_state and p == "split")

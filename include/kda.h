@@ -115,9 +115,10 @@ enum {
     KDA_FLAG_BF16_RESIDENT_STATE = 32u,
     /* bf16-compute kda_fwd: run the segmented single pass, for few (sequence,
      * head) pairs over long sequences. Every sequence is cut into
-     * max(2, 256 / (num_seqs * num_heads)) segments of equal chunk count (at
-     * least 16 chunks, from the average sequence), so that about 256 (segment,
-     * head) workgroups, one per compute unit, run at once. Each segment runs the single-pass kernel twice over the
+     * max(2, 256 / (num_seqs * num_heads)) segments (from the average
+     * sequence; at least 16 chunks each, the first a quarter longer than the
+     * others), so that about 256 (segment, head) workgroups, one per compute
+     * unit, run at once. Each segment runs the single-pass kernel twice over the
      * same prepared chunks: from a zero state (the first segment: the initial
      * state) with the inputs, and from the identity with v = 0, which gives
      * the segment's key-space transfer (the product form of the transition,
@@ -133,15 +134,17 @@ enum {
 /* Without a path flag, kda_fwd runs the token-by-token kernel when the
  * sequences average at most KDA_RECURRENT_MAX_AVG_TOKENS tokens (batch mode:
  * seqlen; packed: T_tot / num_seqs), else, for bf16 compute, the single-pass
- * kernel when num_seqs * num_heads >= KDA_FUSED_MIN_PAIRS, the segmented
- * single pass when fewer pairs hold sequences of at least
- * KDA_SEGMENTED_MIN_AVG_CHUNKS 16-token chunks on average (chunk bound / num_seqs),
- * and the two-kernel path otherwise; fp32 compute uses the fp32 two-kernel
- * path. The thresholds are where each path measured fastest on MI355X. The two paths evaluate the same chunkwise equations and
+ * segmented single pass when num_seqs * num_heads <= KDA_SEGMENTED_MAX_PAIRS
+ * and the sequences average at least KDA_SEGMENTED_MIN_AVG_CHUNKS 16-token
+ * chunks (chunk bound / num_seqs), else the single-pass kernel when
+ * num_seqs * num_heads >= KDA_FUSED_MIN_PAIRS, and the two-kernel path
+ * otherwise; fp32 compute uses the fp32 two-kernel path. The thresholds are
+ * where each path measured fastest on MI355X. The two paths evaluate the same chunkwise equations and
  * agree to bf16 rounding; they are not bitwise identical (the single pass
  * applies the L2 normalisation after its in-chunk products instead of
  * before). */
 #define KDA_FUSED_MIN_PAIRS 96
+#define KDA_SEGMENTED_MAX_PAIRS 128
 #define KDA_SEGMENTED_MIN_AVG_CHUNKS 128
 #define KDA_RECURRENT_MAX_AVG_TOKENS 4
 

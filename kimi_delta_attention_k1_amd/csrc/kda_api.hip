@@ -34,11 +34,13 @@ struct Shape {
 };
 
 // Which kernels kda_fwd runs (the rule is stated with KDA_FUSED_MIN_PAIRS).
-// Segmented single pass without a flag: fewer pairs than KDA_FUSED_MIN_PAIRS and
+// Segmented single pass without a flag: at most KDA_SEGMENTED_MAX_PAIRS pairs (two
+// segments per pair still fit one round of workgroups on the compute units) and
 // sequences of at least KDA_SEGMENTED_MIN_AVG_CHUNKS chunks on average.
 bool seg_worth(const kda_desc_t *d, int64_t n_c_max)
 {
-    return n_c_max >= (int64_t)KDA_SEGMENTED_MIN_AVG_CHUNKS * d->num_seqs;
+    return d->num_seqs * (int64_t)d->num_heads <= KDA_SEGMENTED_MAX_PAIRS &&
+           n_c_max >= (int64_t)KDA_SEGMENTED_MIN_AVG_CHUNKS * d->num_seqs;
 }
 
 Path pick_path(const kda_desc_t *d, bool f32_path, int64_t T_tot, int64_t n_c_max)
@@ -49,8 +51,8 @@ Path pick_path(const kda_desc_t *d, bool f32_path, int64_t T_tot, int64_t n_c_ma
     if (d->flags & (KDA_FLAG_SPLIT | KDA_FLAG_BF16_RESIDENT_STATE)) return kSplit;
     if (T_tot <= (int64_t)KDA_RECURRENT_MAX_AVG_TOKENS * d->num_seqs) return kRecurrent;
     if (f32_path) return kSplit;
-    if (d->num_seqs * (int64_t)d->num_heads >= KDA_FUSED_MIN_PAIRS) return kFused;
     if (seg_worth(d, n_c_max)) return kSeg;
+    if (d->num_seqs * (int64_t)d->num_heads >= KDA_FUSED_MIN_PAIRS) return kFused;
     return kSplit;
 }
 

@@ -89,7 +89,8 @@ __device__ __forceinline__ float sum_rows4(float x)
 // every key channel (Gated DeltaNet, Doubleword section 3)
 //
 // SEG: one workgroup per (time segment, head) instead of per (sequence, head); a
-// sequence's chunks are cut into segments of seg_len chunks (segment g of sequence
+// sequence's chunks are cut into segments of seg_len chunks, the first one seg_first
+// chunks long (segment g of sequence
 // n is the g-th entry after seg_off[n]). The state entering a segment is not known
 // yet, so the segment runs twice over the same prepared chunks, and the state
 // recurrence being linear in (S, v) makes the two runs add up to the true one:
@@ -107,7 +108,8 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const uint16_t *__restrict__ graw, const uint16_t *__restrict__ braw, const TSt *s0, TSt *s1,
     uint16_t *__restrict__ out, const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off, int H,
-    float lb, float scale, const int32_t *__restrict__ seg_off, int N, int seg_len, float *__restrict__ sfin,
+    float lb, float scale, const int32_t *__restrict__ seg_off, int N, int seg_len, int seg_first,
+    float *__restrict__ sfin,
     float *__restrict__ phi, uint16_t *__restrict__ ybuf, const int32_t *__restrict__ order)
 {
     __shared__ __attribute__((aligned(1024))) char lds[kFLds];
@@ -125,8 +127,8 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
         if (seg >= seg_off[N]) return;  // past the last segment: uniform, before any barrier
         n = find_seq(seg_off, N, seg);
         gseg = seg - seg_off[n];
-        const int cs = gseg * seg_len;
-        nch = min(seg_len, chunk_off[n + 1] - chunk_off[n] - cs);
+        const int cs = seg_start(gseg, seg_len, seg_first);
+        nch = min(gseg == 0 ? seg_first : seg_len, chunk_off[n + 1] - chunk_off[n] - cs);
         tb = tok_off[n] + cs * kC;
     } else {
         n = order[blockIdx.x / H];  // longest sequences first
@@ -583,7 +585,7 @@ static hipError_t launch_fused_t(const Problem &p, hipStream_t s)
     hipLaunchKernelGGL((kf_fused<TSt, SG, SEG>), dim3((unsigned)groups), dim3(SEG ? kFThreadsSeg : kFThreads), 0, s,
                        (const uint16_t *)p.q, (const uint16_t *)p.k, (const uint16_t *)p.v, (const uint16_t *)p.g,
                        (const uint16_t *)p.beta, (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H,
-                       p.lb, p.scale, seg, (int)p.N, (int)p.lay.seg_len, sfin, phi, ybuf,
+                       p.lb, p.scale, seg, (int)p.N, (int)p.lay.seg_len, (int)p.lay.seg_first, sfin, phi, ybuf,
                        SEG ? nullptr : reinterpret_cast<const int32_t *>(p.ws + p.lay.order));
     return hipGetLastError();
 }

@@ -57,9 +57,11 @@ inline bool use_lookahead(int64_t N, int64_t H, bool f32_path, bool bf16_residen
 }
 
 // Segmented single pass (few (sequence, head) pairs, long sequences): each sequence
-// is cut into G = max(2, kSegTargetGroups / pairs) segments of equal chunk count L
-// (from the average sequence), so that at most about kSegTargetGroups (segment,
-// head) workgroups, one per compute unit, run at once. Workspace after the chunk map:
+// is cut into G = max(2, kSegTargetGroups / pairs) segments (from the average
+// sequence), so that at most about kSegTargetGroups (segment, head) workgroups, one
+// per compute unit, run at once. Every segment after the first is L chunks long;
+// the first is L0 = L + L/4 long, because its workgroups skip the transfer run and
+// take about a quarter less time per chunk. Workspace after the chunk map:
 //   seg_off [N+1] int32             exclusive scan of segments per sequence
 //   sfin    [seg_max][H][128][128]  fp32, segment's final state from S = 0 (seg 0: S_0)
 //   phi     [seg_max][H][128][128]  fp32, segment's key-space transfer
@@ -67,23 +69,34 @@ inline bool use_lookahead(int64_t N, int64_t H, bool f32_path, bool bf16_residen
 //   ybuf    [T_tot][H][128]         bf16, y_t = Phi_t (s qhat_t) within the segment
 constexpr int64_t kSegTargetGroups = 256;
 constexpr int64_t kSegMinChunks = 16;
+inline int64_t seg_first_for(int64_t seg_len) { return seg_len + (seg_len + 3) / 4; }
 inline int64_t seg_len_for(int64_t N, int64_t H, int64_t n_c_max)
 {
     const int64_t pairs = N * H;
     int64_t G = kSegTargetGroups / pairs;
     if (G < 2) G = 2;
     const int64_t avg = (n_c_max + N - 1) / N;
-    const int64_t l = (avg + G - 1) / G;
+    // L0 + (G - 1) L = avg with L0 = 5 L / 4
+    const int64_t l = (4 * avg + 4 * G) / (4 * G + 1);
     return l > kSegMinChunks ? l : kSegMinChunks;
 }
-// upper bound of sum_n ceil(chunks_n / L) given sum_n chunks_n <= n_c_max
+// upper bound of the segment count given sum_n chunks_n <= n_c_max: every segment
+// but a sequence's last holds at least L chunks
 inline int64_t seg_max_for(int64_t N, int64_t n_c_max, int64_t seg_len) { return n_c_max / seg_len + N; }
+
+// first chunk of segment g within its sequence, and the number of segments of a
+// sequence of nc chunks
+__host__ __device__ inline int seg_start(int g, int L, int L0) { return g == 0 ? 0 : L0 + (g - 1) * L; }
+__host__ __device__ inline int seg_count(int nc, int L, int L0)
+{
+    return nc <= 0 ? 0 : nc <= L0 ? 1 : 1 + (nc - L0 + L - 1) / L;
+}
 
 struct WsLayout {
     size_t tok_off, chunk_off, units, unit_bytes, ket, total;
     size_t seg_off, sfin, phi, sin, ybuf;
     size_t order;  // single pass: sequences longest first, [N] int32 (0: not kept)
-    int64_t n_c_max, seg_len, seg_max;
+    int64_t n_c_max, seg_len, seg_first, seg_max;
 };
 
 inline WsLayout ws_layout(int64_t N, int64_t H, int64_t n_c_max, bool f32_path, bool lookahead)
@@ -99,7 +112,7 @@ inline WsLayout ws_layout(int64_t N, int64_t H, int64_t n_c_max, bool f32_path, 
     L.total = lookahead ? L.ket + kKetBytes * (size_t)H * (size_t)n_c_max : end;
     L.seg_off = L.sfin = L.phi = L.sin = L.ybuf = 0;
     L.order = 0;
-    L.seg_len = L.seg_max = 0;
+    L.seg_len = L.seg_first = L.seg_max = 0;
     return L;
 }
 
@@ -120,6 +133,7 @@ inline WsLayout ws_layout_seg(int64_t N, int64_t H, int64_t n_c_max, int64_t T_t
     WsLayout L = ws_layout(N, H, 0, false, false);
     L.n_c_max = n_c_max;
     L.seg_len = seg_len_for(N, H, n_c_max);
+    L.seg_first = seg_first_for(L.seg_len);
     L.seg_max = seg_max_for(N, n_c_max, L.seg_len);
     const size_t st = (size_t)L.seg_max * (size_t)H * kD * kD * sizeof(float);
     L.seg_off = L.units;

@@ -17,7 +17,7 @@ namespace kda {
 // tok_off[0] = 0, tok_off[N] = T_tot; flag = 1 iff cu already had that form.
 // Without: tok_off[n] = n*T. chunk_off is the exclusive scan of
 // ceil((tok_off[n+1]-tok_off[n]) / 16); on the segmented path seg_off is the
-// exclusive scan of ceil(chunks of sequence n / seg_len); on the single pass,
+// exclusive scan of the segments of each sequence (seg_count); on the single pass,
 // order lists the sequences longest first.
 // ---------------------------------------------------------------------------
 constexpr int kMapThreads = 1024;
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kMapThreads) void k0_chunk_map(const int32_t *__res
                                                              int T_tot, int32_t *__restrict__ hdr,
                                                              int32_t *__restrict__ tok_off,
                                                              int32_t *__restrict__ chunk_off, int seg_len,
-                                                             int32_t *__restrict__ seg_off,
+                                                             int seg_first, int32_t *__restrict__ seg_off,
                                                              int32_t *__restrict__ order)
 {
     __shared__ int sh[kMapThreads + 1];
@@ -89,14 +89,14 @@ __global__ __launch_bounds__(kMapThreads) void k0_chunk_map(const int32_t *__res
         __syncthreads();
     }
     if (seg_off != nullptr) {
-        // pass 3: segment offsets, the exclusive scan of ceil(chunks / seg_len)
+        // pass 3: segment offsets, the exclusive scan of the segments per sequence
         __threadfence_block();
         __syncthreads();
         carry = 0;
         for (int base = 0; base <= N; base += kMapThreads) {
             const int n = base + t;
             int cnt = 0;
-            if (n < N) cnt = (chunk_off[n + 1] - chunk_off[n] + seg_len - 1) / seg_len;
+            if (n < N) cnt = seg_count(chunk_off[n + 1] - chunk_off[n], seg_len, seg_first);
             int s = block_scan_incl(cnt, sh, false);
             if (n <= N) seg_off[n] = carry + s - cnt;
             carry += sh[kMapThreads];
@@ -133,7 +133,7 @@ hipError_t launch_chunk_map(const Problem &p, hipStream_t s)
     int32_t *seg = p.lay.seg_len > 0 ? reinterpret_cast<int32_t *>(p.ws + p.lay.seg_off) : nullptr;
     int32_t *ord = p.lay.order > 0 ? reinterpret_cast<int32_t *>(p.ws + p.lay.order) : nullptr;
     hipLaunchKernelGGL(k0_chunk_map, dim3(1), dim3(kMapThreads), 0, s, p.cu, (int)p.N, (int)p.T,
-                       (int)p.T_tot, hdr, tok, chk, (int)p.lay.seg_len, seg, ord);
+                       (int)p.T_tot, hdr, tok, chk, (int)p.lay.seg_len, (int)p.lay.seg_first, seg, ord);
     return hipGetLastError();
 }
 

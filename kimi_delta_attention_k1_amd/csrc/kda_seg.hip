@@ -122,7 +122,7 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
                                                                  const float *__restrict__ sin,
                                                                  const int32_t *__restrict__ tok_off,
                                                                  const int32_t *__restrict__ seg_off, int N, int H,
-                                                                 int seg_len)
+                                                                 int seg_len, int seg_first)
 {
     __shared__ __attribute__((aligned(16))) uint16_t Shi[kD][kCorrLd];
     __shared__ __attribute__((aligned(16))) uint16_t Slo[kD][kCorrLd];
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
     if (seg >= seg_off[N]) return;
     const int n = find_seq(seg_off, N, seg), gi = seg - seg_off[n];
     if (gi == 0) return;
-    const int tb = tok_off[n] + gi * seg_len * kC;
+    const int tb = tok_off[n] + seg_start(gi, seg_len, seg_first) * kC;  // segments after the first: seg_len chunks
     const int te = min(tok_off[n + 1], tb + seg_len * kC);
     if (tb + (int)blockIdx.y * kCorrTok >= te) return;  // uniform over the workgroup, before any barrier
 
@@ -221,7 +221,7 @@ static hipError_t launch_seg_finish_t(const Problem &p, hipStream_t s)
     const int64_t blocks = want < per_seg ? want : per_seg;
     hipLaunchKernelGGL(kseg_correct, dim3((unsigned)(p.lay.seg_max * p.H), (unsigned)blocks), dim3(64 * kCorrWaves),
                        0, s, (uint16_t *)p.out, (const uint16_t *)(p.ws + p.lay.ybuf), (const float *)sin, tok, seg,
-                       (int)p.N, p.H, (int)p.lay.seg_len);
+                       (int)p.N, p.H, (int)p.lay.seg_len, (int)p.lay.seg_first);
     return hipGetLastError();
 }
 
