@@ -140,3 +140,19 @@ def test_stage_entry_points_compose_to_kda_fwd(gpu):
     torch.cuda.synchronize(dev)
     assert torch.equal(whole.out, staged.out) and torch.equal(whole.final_state, staged.final_state)
     compare(w, staged.out, staged.final_state, run_oracle(w), bf16_tol, "segmented staged")
+
+
+@pytest.mark.parametrize("N,H,T,expect", [
+    (64, 2, 2048, "segmented"),  # 128 pairs, 128 chunks per sequence
+    (43, 3, 2048, "fused"),      # 129 pairs: two segments per pair no longer fit one round
+    (32, 3, 2032, "fused"),      # 96 pairs, 127 chunks per sequence: too short to segment
+    (19, 5, 2032, "split"),      # 95 pairs, too short to segment
+])
+def test_automatic_rule_boundaries(gpu, N, H, T, expect):
+    """Without a path flag, kda_fwd runs exactly the path the rule names (bitwise
+    equal to the forced call) on either side of each threshold."""
+    _banner(f"automatic rule: {N} x {T} tokens, H={H} ({N * H} pairs) -> {expect}")
+    w = workloads.make([T] * N, H, seed=17, packed=False)
+    oa, sa = run_gpu(w, gpu)
+    oe, se = run_gpu(w, gpu, path=expect)
+    assert torch.equal(oa, oe) and torch.equal(sa, se)
