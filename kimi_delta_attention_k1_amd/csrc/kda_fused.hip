@@ -15,19 +15,21 @@
 // chunk c is handled at
 //   tick c    : stage A -- gate, prefix sums, decays, partial 16x16 products
 //               over the wave's 32 channels, K_b / Q_b / K_end / gamma / v into
-//               prepared slot c % 3
-//   tick c+1  : stage B -- sum the four partials; one wave forms R, the
-//               inverse and (A^kk Diag(beta))^T, the other (A^qk)^T and the
-//               per-token scales, into slot c % 3
+//               prepared slot c % 3; the consumers -- the per-token scales
+//               rk = 1/|k|, s rq = s/|q| of chunk c from the raw inputs, stage B
+//               role 1 -- its beta
+//   tick c+1  : stage B -- sum the four partials; role 0 forms R, the inverse
+//               and (A^kk Diag(beta))^T, role 1 (A^qk)^T, into slot c % 3
 //   tick c+2  : consumers run the recurrence step on slot c % 3.
 // Each stage-A wave streams its 32-channel slices of q, k, g_raw, v and
-// beta_raw with global-to-LDS loads kFIn chunks ahead and waits on exact counts
-// of its own loads.
+// beta_raw with global-to-LDS loads kFIn - 1 chunks ahead and waits on exact
+// counts of its own loads; a ring slot is refilled one tick after its chunk's
+// stage-A tick, since the consumers and stage B role 1 read it during that tick.
 //
-// L2 normalisation is deferred: stage A works on raw q, k; stage B forms the
-// per-token scales rk = 1/|k|, rq = s/|q| (the read scale s folded in) from the
-// summed partial norms and folds them into R, (A^kk Diag(beta))^T and
-// (A^qk)^T; the consumers scale K_b S^T by rk and Q_b S^T by rq per row. The recurrence then runs on
+// L2 normalisation is deferred: stage A works on raw q, k; the consumers form
+// rk and s rq (the read scale s folded in) a tick ahead of stage B, which folds
+// them into R, (A^kk Diag(beta))^T and (A^qk)^T; the consumers scale K_b S^T by
+// rk and Q_b S^T by rq per row. The recurrence then runs on
 // E' = Diag(rk) E, which is exactly what the state update needs with the raw
 // K_end (K_end^T E = K_end_raw^T E'), and A^qk / Diag(rk) applied to E' gives
 // the same outputs.
@@ -45,7 +47,10 @@ constexpr int kFThreadsSeg = kFThreads + 64 * kFCons;         // 896: + the tran
 constexpr int kFIn = 4;                               // input chunks in flight per prep wave
 constexpr int kFSlots = 3;                            // prepared-chunk slots (stage A steps through them unrolled)
 constexpr int kFDma = 5;                              // global-to-LDS loads per chunk per prep wave
-constexpr int kFPending = (kFIn - 1) * kFDma;         // loads allowed in flight at a stage-A start
+// a ring slot is refilled one tick after its chunk's stage-A tick (stage B role 1 reads the
+// raw q, k and beta_raw of chunk c from the rings during tick c), so kFIn - 1 chunks are in
+// flight: waiting for chunk c + 1 at the end of tick c leaves two chunks' loads outstanding
+constexpr int kFPending = (kFIn - 2) * kFDma;         // loads allowed in flight when chunk c+1 must have landed
 static_assert(kFPending <= 63, "vmcnt holds at most 63 outstanding loads");
 
 // prepared slot
@@ -142,6 +147,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
         // ================================================================ stage-B waves
         if (nch == 0) return;  // uniform over the workgroup: no barrier is entered
         const int role = w - kFCons - kFPrep;
+        bar_sync();  // start: the stage-A waves have waited for chunk 0 in their rings
 #pragma unroll 1
         for (int tau = 0; tau < ticks; ++tau) {
             if (tau >= 1 && tau - 1 < nch) {
@@ -166,14 +172,15 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                     const f32x4 Rs = sum4(kXR), RTs = sum4(kXRT);
                     const f32x4 beta_a = *reinterpret_cast<const f32x4 *>(X + kXBeta + 16 * g);
                     const float beta_b = reinterpret_cast<const float *>(X + kXBeta)[tok];
-                    const float rkb = __builtin_amdgcn_rsqf(tok_sum(kXNK, tok) + kL2Eps);
+                    // rk = 1 / |k| per token, formed by the consumers in the previous tick
+                    const float rkb = reinterpret_cast<const float *>(P + kPSC)[tok];
+                    const f32x4 rka = *reinterpret_cast<const f32x4 *>(P + kPSC + 16 * g);
                     f32x4 R, RT;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int a = 4 * g + r;
-                        const float rka = __builtin_amdgcn_rsqf(tok_sum(kXNK, a) + kL2Eps);
-                        R[r] = (tok < a) ? beta_a[r] * rka * rkb * Rs[r] : 0.f;
-                        RT[r] = (a < tok) ? beta_b * rkb * rka * RTs[r] : 0.f;
+                        R[r] = (tok < a) ? beta_a[r] * rka[r] * rkb * Rs[r] : 0.f;
+                        RT[r] = (a < tok) ? beta_b * rkb * rka[r] * RTs[r] : 0.f;
                     }
                     // (A^kk)^T = (I + R^T)^-1 = (I-M)(I+M^2)(I+M^4)(I+M^8), M = R^T, with fp16
                     // operands and fp32 accumulation: the inverse's entries are bounded by 1
@@ -192,17 +199,25 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                     reinterpret_cast<bf16x8 *>(P + kPAB)[lane] = split8(ABT);
                 } else {
                     const f32x4 AQs = sum4(kXAQ);
-                    const float rqb = scale * __builtin_amdgcn_rsqf(tok_sum(kXNQ, tok) + kL2Eps);
+                    const float rqb = reinterpret_cast<const float *>(P + kPSC + 64)[tok];  // s rq
                     f32x4 AQT;  // chi_{b,a} / rk_a = s rq_b (q_b . k_a decayed), a <= b
 #pragma unroll
                     for (int r = 0; r < 4; ++r) AQT[r] = (4 * g + r <= tok) ? rqb * AQs[r] : 0.f;
                     reinterpret_cast<bf16x8 *>(P + kPAQ)[lane] = split8(AQT);
-                    if (lane < 32) {  // rk (lanes 0-15) and s rq (lanes 16-31)
-                        const float nn = tok_sum(lane < 16 ? kXNK : kXNQ, tok);
-                        reinterpret_cast<float *>(P + kPSC)[lane] =
-                            (lane < 16 ? 1.f : scale) * __builtin_amdgcn_rsqf(nn + kL2Eps);
-                    }
                 }
+            }
+            if (role == 1 && tau < nch && lane < 16) {
+                // beta of chunk c = tau from the raw beta_raw in stage-A wave 0's ring (landed
+                // before the last barrier, refilled only next tick): the low or high half of
+                // the aligned dword; rows past the end of the sequence get beta = 0 (absent)
+                const int c = tau, t = lane;
+                const int t0 = tb + c * kC;
+                const int brow = min(t0 + t, te - 1);
+                const int64_t eo = ((int64_t)brow * H + h) * 2;
+                const bool bhi = (reinterpret_cast<uintptr_t>(reinterpret_cast<const char *>(braw) + eo) & 2) != 0;
+                const uint32_t bw = *reinterpret_cast<const uint32_t *>(inring + (c % kFIn) * kIBytes + kIB + t * 4);
+                const float beta = (t0 + t < te) ? sigmoid_fast(bhi ? bf_hi(bw) : bf_lo(bw)) : 0.f;
+                reinterpret_cast<float *>(parts + (c & 1) * kXBytes + kXBeta)[t] = beta;
             }
             tick_sync();
         }
@@ -246,11 +261,10 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                                              (lds_void *)(dst + kIB), 4, 0, 0);
         };
 #pragma unroll
-        for (int i = 0; i < kFIn; ++i) dma_chunk(i, i);
+        for (int i = 0; i < kFIn - 1; ++i) dma_chunk(i, i);
         // The inputs of chunk c are read from LDS into registers at the end of tick
         // c - 1 (chunk 0: here), so their LDS latency overlaps the other waves' work.
         u32x4 qa, ka, ga, va;
-        uint32_t bw;
         auto read_inputs = [&](int c) {
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kFPending) : "memory");  // chunk c landed
             const char *I = myin + (c % kFIn) * kIBytes;
@@ -262,9 +276,9 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 ga = *reinterpret_cast<const u32x4 *>(I + kIG + t * 64 + sg * 16);
             }
             va = *reinterpret_cast<const u32x4 *>(I + kIV + t * 64 + sg * 16);
-            bw = *reinterpret_cast<const uint32_t *>(I + kIB + t * 4);
         };
         read_inputs(0);
+        tick_sync();  // start: chunk 0 has landed in this wave's ring (role 1 reads every ring)
 
         const float lb2 = lb * kLog2e;
         // one tick of stage A on chunk c. The prepared slot c % kFSlots is a compile-time
@@ -272,10 +286,10 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
         // addresses fold into instruction offsets instead of being rebuilt every tick.
         auto stage_a = [&](const int c, auto slot_tag) {
             constexpr int slot = decltype(slot_tag)::value;
-            // the registers hold chunk c (reads completed before the last barrier):
-            // refill its input slot with chunk c + kFIn
+            // chunk c - 1's slot is free (its inputs were read before the last barrier,
+            // by this wave and by stage B role 1): refill it with chunk c + kFIn - 1
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            dma_chunk(c + kFIn, c % kFIn);
+            dma_chunk(c + kFIn - 1, (c + kFIn - 1) % kFIn);
             const int t0 = tb + c * kC, len = min(kC, te - t0);
             // rows past the end of the sequence hold copies of its last row; zero
             // gate and beta make them absent: they reach only the masked triangles
@@ -283,9 +297,6 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
             // that are never stored
             const bool valid = t < len;
 
-            const int brow = min(t0 + t, te - 1);
-            const int64_t eo = ((int64_t)brow * H + h) * 2;  // byte offset of [brow][h]
-            const bool bhi = (reinterpret_cast<uintptr_t>(bb8 + eo) & 2) != 0;
             const float vmask = valid ? 1.f : 0.f;
             float qf[8], kf[8], gf[8];
 #pragma unroll
@@ -295,8 +306,9 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 kf[2 * e] = bf_lo(ka[e]);
                 kf[2 * e + 1] = bf_hi(ka[e]);
             }
-            const float beta = vmask * sigmoid_fast(bhi ? bf_hi(bw) : bf_lo(bw));
             if constexpr (SG) {  // one gate and one prefix sum serve every channel
+                const int grow = min(t0 + t, te - 1);
+                const int64_t eo = ((int64_t)grow * H + h) * 2;  // byte offset of [grow][h]
                 const bool ghi = (reinterpret_cast<uintptr_t>(gb8 + eo) & 2) != 0;
                 float x = vmask * lb2 * sigmoid_fast(ghi ? bf_hi(ga[0]) : bf_lo(ga[0]));
                 // rounded exactly as the per-channel gate below, step by step
@@ -328,22 +340,8 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                     gf[i] = x;
                 }
             }
-            float nq = 0.f, nk = 0.f;  // partial squared norms over this wave's 32 channels
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                nq += qf[i] * qf[i];
-                nk += kf[i] * kf[i];
-            }
-            nq = sum_rows4(nq);
-            nk = sum_rows4(nk);
-
             char *X = parts + (c & 1) * kXBytes;
             char *P = slots + slot * kPBytes;
-            if (sg == 0) {
-                reinterpret_cast<float *>(X + m * kXWave + kXNQ)[t] = nq;
-                reinterpret_cast<float *>(X + m * kXWave + kXNK)[t] = nk;
-                if (m == 0) reinterpret_cast<float *>(X + kXBeta)[t] = beta;
-            }
             // decays relative to token 7 (each factor within e^{8|lb|}); K_end via token 15
             bf16x8 kr_h, ki_h, qr_h;
             float ke[8];
@@ -455,8 +453,43 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
             for (int t = 0; t < 8; ++t) st[u][t] = ld_state4(s0 + sbase + (int64_t)16 * kD * u + 16 * t);
     }
     uint16_t *const obuf = MODE == 2 ? ybuf : out;
+    if (ticks > 0) bar_sync();  // start: the stage-A waves have waited for chunk 0 in their rings
 #pragma unroll 1
     for (int tau = 0; tau < ticks; ++tau) {
+        if (MODE != 2 && tau < nch) {
+            // per-token scales of chunk tau from the raw inputs in the stage-A rings
+            // (landed before the last barrier, refilled only next tick): wave cw takes
+            // tokens 4cw..4cw+3, lane (token, cg) channels [8cg, 8cg+8), summed over the
+            // 16-lane row; rk = 1/|k| and s rq = s/|q| go to the chunk's slot for stage B
+            // (next tick) and for the consumers' own step two ticks later
+            const int tk = 4 * cw + g, cg = col;
+            const char *I = inring + ((cg >> 2) * kFIn + tau % kFIn) * kIBytes + tk * 64 + (cg & 3) * 16;
+            const u32x4 qv = *reinterpret_cast<const u32x4 *>(I + kIQ);
+            const u32x4 kv = *reinterpret_cast<const u32x4 *>(I + kIK);
+            float nq = 0.f, nk = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float q0 = bf_lo(qv[e]), q1 = bf_hi(qv[e]), k0 = bf_lo(kv[e]), k1 = bf_hi(kv[e]);
+                nq += q0 * q0;
+                nq += q1 * q1;
+                nk += k0 * k0;
+                nk += k1 * k1;
+            }
+            asm("" : "+v"(nq), "+v"(nk));
+            nq += row_shr<1>(nq);
+            nk += row_shr<1>(nk);
+            nq += row_shr<2>(nq);
+            nk += row_shr<2>(nk);
+            nq += row_shr<4>(nq);
+            nk += row_shr<4>(nk);
+            nq += row_shr<8>(nq);
+            nk += row_shr<8>(nk);
+            if (col == 15) {  // the row's total
+                float *sc = reinterpret_cast<float *>(slots + (tau % kFSlots) * kPBytes + kPSC);
+                sc[tk] = __builtin_amdgcn_rsqf(nk + kL2Eps);
+                sc[16 + tk] = scale * __builtin_amdgcn_rsqf(nq + kL2Eps);
+            }
+        }
         if (tau >= 2) {
             const int c = tau - 2;
             const char *L = slots + (c % kFSlots) * kPBytes;
@@ -564,7 +597,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 consume(std::integral_constant<int, 2>{}, w - (kFCons + kFPrep + kFSolve));
             } else {
 #pragma unroll 1
-                for (int tau = 0; tau < ticks; ++tau) bar_sync();
+                for (int tau = 0; tau <= ticks; ++tau) bar_sync();  // the start barrier and every tick's
             }
         }
     } else {
