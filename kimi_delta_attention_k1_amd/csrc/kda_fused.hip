@@ -13,13 +13,14 @@
 // serves two tiles), 4 stage-A waves (wave m owns key channels [32m, 32m+32))
 // and 2 stage-B waves; waves w, w+4 (and w+8) share a SIMD. Time advances in ticks separated by one workgroup barrier;
 // chunk c is handled at
-//   tick c    : stage A -- gate, prefix sums, decays, partial 16x16 products
-//               over the wave's 32 channels, K_b / Q_b / K_end / gamma / v into
-//               prepared slot c % 3; the consumers -- the per-token scales
+//   tick c    : stage A -- gate, prefix sums, decays; the wave's 32-channel
+//               slices of the in-chunk operands, and K_b / Q_b / K_end / gamma / v
+//               into prepared slot c % 3; the consumers -- the per-token scales
 //               rk = 1/|k|, s rq = s/|q| of chunk c from the raw inputs, stage B
 //               role 1 -- its beta
-//   tick c+1  : stage B -- sum the four partials; role 0 forms R, the inverse
-//               and (A^kk Diag(beta))^T, role 1 (A^qk)^T, into slot c % 3
+//   tick c+1  : stage B -- contracts the operands over the 128 channels; role 0
+//               forms R, the inverse and (A^kk Diag(beta))^T, role 1 (A^qk)^T,
+//               into slot c % 3
 //   tick c+2  : consumers run the recurrence step on slot c % 3.
 // Each stage-A wave streams its 32-channel slices of q, k, g_raw, v and
 // beta_raw with global-to-LDS loads kFIn - 1 chunks ahead and waits on exact
@@ -64,8 +65,11 @@ constexpr int kPBytes = kPV + kC * kVRow;
 // beta_raw as one aligned dword per lane (the token's element in its low or high half);
 // a scalar g_raw takes the same dword form at the start of its block
 constexpr int kIQ = 0, kIK = 1024, kIG = 2048, kIV = 3072, kIB = 4096, kIBytes = 4352;
-// partial-product buffer (two, alternating by chunk parity)
-constexpr int kXR = 0, kXRT = 1024, kXAQ = 2048, kXNQ = 3072, kXNK = 3136, kXWave = 3200;
+// in-chunk operand buffer (two, alternating by chunk parity): per stage-A wave, its
+// 32-channel slices of K_r = k e^{G - Gref}, K_inv = k e^{Gref - G} and Q_r = q e^{G - Gref}
+// as bf16 16x16x32 operands (lane = token, 8 channels), which stage B contracts over
+// all 128 channels for R, R^T and A^qk
+constexpr int kXKR = 0, kXKI = 1024, kXQR = 2048, kXWave = 3072;
 constexpr int kXBeta = kFPrep * kXWave;
 constexpr int kXBytes = kXBeta + 64;
 constexpr int kFLds = kFSlots * kPBytes + kFPrep * kFIn * kIBytes + 2 * kXBytes;
@@ -155,21 +159,18 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 const char *X = parts + (c & 1) * kXBytes;
                 char *P = slots + (c % kFSlots) * kPBytes;
                 const int tok = lane & 15, g = lane >> 4;  // D layout: rows 4g+r, column tok
-                // sum of the four waves' partials of one lane-ordered block / one token vector
-                auto sum4 = [&](int off) {
-                    f32x4 a = reinterpret_cast<const f32x4 *>(X + off)[lane];
+                // A B^T over the 128 key channels: the four waves' 32-channel operand slices,
+                // one chained 16x16x32 product each (fp32 accumulation)
+                auto contract = [&](int offa, int offb) {
+                    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int mm = 1; mm < kFPrep; ++mm) a += reinterpret_cast<const f32x4 *>(X + mm * kXWave + off)[lane];
-                    return a;
-                };
-                auto tok_sum = [&](int off, int i) {
-                    float a = reinterpret_cast<const float *>(X + off)[i];
-#pragma unroll
-                    for (int mm = 1; mm < kFPrep; ++mm) a += reinterpret_cast<const float *>(X + mm * kXWave + off)[i];
+                    for (int mm = 0; mm < kFPrep; ++mm)
+                        a = mma32(reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offa)[lane],
+                                  reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offb)[lane], a);
                     return a;
                 };
                 if (role == 0) {
-                    const f32x4 Rs = sum4(kXR), RTs = sum4(kXRT);
+                    const f32x4 Rs = contract(kXKR, kXKI), RTs = contract(kXKI, kXKR);
                     const f32x4 beta_a = *reinterpret_cast<const f32x4 *>(X + kXBeta + 16 * g);
                     const float beta_b = reinterpret_cast<const float *>(X + kXBeta)[tok];
                     // rk = 1 / |k| per token, formed by the consumers in the previous tick
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                     for (int r = 0; r < 4; ++r) ABT[r] = rkb * beta_a[r] * AT[r];
                     reinterpret_cast<bf16x8 *>(P + kPAB)[lane] = split8(ABT);
                 } else {
-                    const f32x4 AQs = sum4(kXAQ);
+                    const f32x4 AQs = contract(kXKI, kXQR);
                     const float rqb = reinterpret_cast<const float *>(P + kPSC + 64)[tok];  // s rq
                     f32x4 AQT;  // chi_{b,a} / rk_a = s rq_b (q_b . k_a decayed), a <= b
 #pragma unroll
@@ -370,13 +371,9 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                                                   ((t & 3) + 4 * hi) * 2) = (uint16_t)(pk >> (16 * j));
                 }
             }
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 dR = mma32(kr_h, ki_h, z);
-            const f32x4 dRT = mma32(ki_h, kr_h, z);
-            const f32x4 dAQT = mma32(ki_h, qr_h, z);
-            reinterpret_cast<f32x4 *>(X + m * kXWave + kXR)[lane] = dR;
-            reinterpret_cast<f32x4 *>(X + m * kXWave + kXRT)[lane] = dRT;
-            reinterpret_cast<f32x4 *>(X + m * kXWave + kXAQ)[lane] = dAQT;
+            reinterpret_cast<bf16x8 *>(X + m * kXWave + kXKR)[lane] = kr_h;
+            reinterpret_cast<bf16x8 *>(X + m * kXWave + kXKI)[lane] = ki_h;
+            reinterpret_cast<bf16x8 *>(X + m * kXWave + kXQR)[lane] = qr_h;
 
             // raw K_b = k e^{G}, Q_b = q e^{G} in the consumer's 16x16x32 A order
             // (k step m); gamma = e^{G_last} from token 15; the v tile
