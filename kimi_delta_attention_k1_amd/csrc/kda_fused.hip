@@ -11,19 +11,22 @@
 // Workgroup: 4 consumer waves (the recurrence; wave w owns value channels
 // [32w, 32w+32) as two 16-wide column tiles, so every operand read from LDS
 // serves two tiles), 4 stage-A waves (wave m owns key channels [32m, 32m+32))
-// and 2 stage-B waves; waves w, w+4 (and w+8) share a SIMD. Time advances in ticks separated by one workgroup barrier;
-// chunk c is handled at
+// and 3 stage-B waves: 8 and 10 (14 in the segmented form) invert the even and
+// the odd chunks, 9 forms A^qk and beta. Waves w, w+4, w+8 (and w+12) share a
+// SIMD, so the two inverse waves sit on different SIMDs. Time advances in ticks
+// separated by one workgroup barrier; chunk c is handled at
 //   tick c    : stage A -- gate, prefix sums, decays; the wave's 32-channel
 //               slices of the in-chunk operands, and K_b / Q_b / K_end / gamma / v
-//               into prepared slot c % 3; the consumers -- the per-token scales
-//               rk = 1/|k|, s rq = s/|q| of chunk c from the raw inputs, stage B
-//               role 1 -- its beta
-//   tick c+1  : stage B -- contracts the operands over the 128 channels; role 0
-//               forms R, the inverse and (A^kk Diag(beta))^T, role 1 (A^qk)^T,
-//               into slot c % 3
-//   tick c+2  : consumers run the recurrence step on slot c % 3.
+//               into prepared slot c % 4; the consumers -- the per-token scales
+//               rk = 1/|k|, s rq = s/|q| of chunk c from the raw inputs; stage B
+//               wave 9 -- its beta
+//   tick c+1  : stage B -- contracts the operands over the 128 channels; wave 9
+//               forms (A^qk)^T; the chunk's inverse wave forms R, R^T, M^2 and
+//               (I - M)(I + M^2)
+//   tick c+2  : the inverse wave completes (A^kk Diag(beta))^T into slot c % 4
+//   tick c+3  : consumers run the recurrence step on slot c % 4.
 // Each stage-A wave streams its 32-channel slices of q, k, g_raw, v and
-// beta_raw with global-to-LDS loads kFIn - 1 chunks ahead and waits on exact
+// beta_raw into a kFIn-slot ring with global-to-LDS loads and waits on exact
 // counts of its own loads; a ring slot is refilled one tick after its chunk's
 // stage-A tick, since the consumers and stage B role 1 read it during that tick.
 //
@@ -42,11 +45,11 @@ namespace kda {
 
 constexpr int kFCons = 4;                             // consumer waves (32 value channels each)
 constexpr int kFPrep = 4;                             // stage-A waves
-constexpr int kFSolve = 2;                            // stage-B waves
-constexpr int kFThreads = 64 * (kFCons + kFPrep + kFSolve);  // 640
-constexpr int kFThreadsSeg = kFThreads + 64 * kFCons;         // 896: + the transfer-run consumers
-constexpr int kFIn = 4;                               // input chunks in flight per prep wave
-constexpr int kFSlots = 3;                            // prepared-chunk slots (stage A steps through them unrolled)
+constexpr int kFSolve = 3;                            // stage-B waves: even- and odd-chunk inverse, A^qk
+constexpr int kFThreads = 64 * (kFCons + kFPrep + kFSolve);  // 704
+constexpr int kFThreadsSeg = kFThreads + 64 * kFCons;         // 960: + the transfer-run consumers
+constexpr int kFIn = 3;                               // input-ring slots per prep wave (two chunks in flight)
+constexpr int kFSlots = 4;                            // prepared-chunk slots (stage A steps through them unrolled)
 constexpr int kFDma = 5;                              // global-to-LDS loads per chunk per prep wave
 // a ring slot is refilled one tick after its chunk's stage-A tick (stage B role 1 reads the
 // raw q, k and beta_raw of chunk c from the rings during tick c), so kFIn - 1 chunks are in
@@ -145,36 +148,61 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
         tb = tok_off[n];
     }
     const int te = tok_off[n + 1];
-    const int ticks = nch > 0 ? nch + 2 : 0;
+    const int ticks = nch > 0 ? nch + 3 : 0;
 
-    if (w >= kFCons + kFPrep && w < kFCons + kFPrep + kFSolve) {
+    // stage-B waves: 8 (inverse of even chunks), 9 (A^qk and beta), and the inverse of odd
+    // chunks after the transfer-run waves in the segmented form, on the SIMD of waves 2 and 6
+    const int w_inv_odd = kFCons + kFPrep + 2 + (SEG ? kFCons : 0);
+    const bool stage_b = w == kFCons + kFPrep || w == kFCons + kFPrep + 1 || w == w_inv_odd;
+    if (stage_b) {
         // ================================================================ stage-B waves
         if (nch == 0) return;  // uniform over the workgroup: no barrier is entered
-        const int role = w - kFCons - kFPrep;
+        const int role = w == kFCons + kFPrep + 1 ? 1 : 0;
+        const int parity = w == w_inv_odd ? 1 : 0;  // inverse waves: chunks of this parity
+        const int tok = lane & 15, g = lane >> 4;  // D layout: rows 4g+r, column tok
+        // carried from an inverse's first half (tick c+1) to its second (tick c+2)
+        f32x4 M2 = {0.f, 0.f, 0.f, 0.f}, M2T = M2, P1 = M2, beta_a = M2;
+        float rkb = 0.f;
         bar_sync();  // start: the stage-A waves have waited for chunk 0 in their rings
 #pragma unroll 1
         for (int tau = 0; tau < ticks; ++tau) {
-            if (tau >= 1 && tau - 1 < nch) {
-                const int c = tau - 1;
-                const char *X = parts + (c & 1) * kXBytes;
-                char *P = slots + (c % kFSlots) * kPBytes;
-                const int tok = lane & 15, g = lane >> 4;  // D layout: rows 4g+r, column tok
-                // A B^T over the 128 key channels: the four waves' 32-channel operand slices,
-                // one chained 16x16x32 product each (fp32 accumulation)
-                auto contract = [&](int offa, int offb) {
-                    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            // A B^T over the 128 key channels: the four waves' 32-channel operand slices of
+            // chunk c, one chained 16x16x32 product each (fp32 accumulation)
+            auto contract = [&](const char *X, int offa, int offb) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int mm = 0; mm < kFPrep; ++mm)
-                        a = mma32(reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offa)[lane],
-                                  reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offb)[lane], a);
-                    return a;
-                };
-                if (role == 0) {
-                    const f32x4 Rs = contract(kXKR, kXKI), RTs = contract(kXKI, kXKR);
-                    const f32x4 beta_a = *reinterpret_cast<const f32x4 *>(X + kXBeta + 16 * g);
+                for (int mm = 0; mm < kFPrep; ++mm)
+                    acc = mma32(reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offa)[lane],
+                                reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offb)[lane], acc);
+                return acc;
+            };
+            if (role == 0) {
+                // (A^kk)^T = (I + R^T)^-1 = (I-M)(I+M^2)(I+M^4)(I+M^8), M = R^T, with fp16
+                // operands and fp32 accumulation: the inverse's entries are bounded by 1
+                // in magnitude (FlashKDA deep-dive, section 3), so fp16's range suffices.
+                // Each chunk's inverse takes two ticks on one of the two inverse waves.
+                const int c2 = tau - 2;  // second half: M^4, M^8, the product, the store
+                if (c2 >= 0 && c2 < nch && (c2 & 1) == parity) {
+                    char *P = slots + (c2 % kFSlots) * kPBytes;
+                    const f32x4 M4 = mm16_h(M2T, M2);
+                    const f32x4 M4T = mm16_h(M2, M2T);
+                    const f32x4 M8T = mm16_h(M4, M4T);
+                    const f32x4 P2 = mm16_h(eye_plus(M4T, 1.f, g, tok), P1);
+                    const f32x4 AT = mm16_h(eye_plus(M8T, 1.f, g, tok), P2);
+                    f32x4 ABT;  // rk_b beta_a A^kk[b][a]: E' = Diag(rk) A^kk Diag(beta) Ebar
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ABT[r] = rkb * beta_a[r] * AT[r];
+                    reinterpret_cast<bf16x8 *>(P + kPAB)[lane] = split8(ABT);
+                }
+                const int c1 = tau - 1;  // first half: R, R^T, M^2 and (I - M)(I + M^2)
+                if (c1 >= 0 && c1 < nch && (c1 & 1) == parity) {
+                    const char *X = parts + (c1 & 1) * kXBytes;
+                    const char *P = slots + (c1 % kFSlots) * kPBytes;
+                    const f32x4 Rs = contract(X, kXKR, kXKI), RTs = contract(X, kXKI, kXKR);
+                    beta_a = *reinterpret_cast<const f32x4 *>(X + kXBeta + 16 * g);
                     const float beta_b = reinterpret_cast<const float *>(X + kXBeta)[tok];
                     // rk = 1 / |k| per token, formed by the consumers in the previous tick
-                    const float rkb = reinterpret_cast<const float *>(P + kPSC)[tok];
+                    rkb = reinterpret_cast<const float *>(P + kPSC)[tok];
                     const f32x4 rka = *reinterpret_cast<const f32x4 *>(P + kPSC + 16 * g);
                     f32x4 R, RT;
 #pragma unroll
@@ -183,29 +211,20 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                         R[r] = (tok < a) ? beta_a[r] * rka[r] * rkb * Rs[r] : 0.f;
                         RT[r] = (a < tok) ? beta_b * rkb * rka[r] * RTs[r] : 0.f;
                     }
-                    // (A^kk)^T = (I + R^T)^-1 = (I-M)(I+M^2)(I+M^4)(I+M^8), M = R^T, with fp16
-                    // operands and fp32 accumulation: the inverse's entries are bounded by 1
-                    // in magnitude (FlashKDA deep-dive, section 3), so fp16's range suffices
-                    const f32x4 M2 = mm16_h(R, RT);
-                    const f32x4 M2T = mm16_h(RT, R);
-                    const f32x4 M4 = mm16_h(M2T, M2);
-                    const f32x4 M4T = mm16_h(M2, M2T);
-                    const f32x4 M8T = mm16_h(M4, M4T);
-                    const f32x4 P1 = mm16_h(eye_plus(R, -1.f, g, tok), eye_plus(M2, 1.f, g, tok));
-                    const f32x4 P2 = mm16_h(eye_plus(M4T, 1.f, g, tok), P1);
-                    const f32x4 AT = mm16_h(eye_plus(M8T, 1.f, g, tok), P2);
-                    f32x4 ABT;  // rk_b beta_a A^kk[b][a]: E' = Diag(rk) A^kk Diag(beta) Ebar
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) ABT[r] = rkb * beta_a[r] * AT[r];
-                    reinterpret_cast<bf16x8 *>(P + kPAB)[lane] = split8(ABT);
-                } else {
-                    const f32x4 AQs = contract(kXKI, kXQR);
-                    const float rqb = reinterpret_cast<const float *>(P + kPSC + 64)[tok];  // s rq
-                    f32x4 AQT;  // chi_{b,a} / rk_a = s rq_b (q_b . k_a decayed), a <= b
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) AQT[r] = (4 * g + r <= tok) ? rqb * AQs[r] : 0.f;
-                    reinterpret_cast<bf16x8 *>(P + kPAQ)[lane] = split8(AQT);
+                    M2 = mm16_h(R, RT);
+                    M2T = mm16_h(RT, R);
+                    P1 = mm16_h(eye_plus(R, -1.f, g, tok), eye_plus(M2, 1.f, g, tok));
                 }
+            } else if (tau >= 1 && tau - 1 < nch) {
+                const int c = tau - 1;
+                const char *X = parts + (c & 1) * kXBytes;
+                char *P = slots + (c % kFSlots) * kPBytes;
+                const f32x4 AQs = contract(X, kXKI, kXQR);
+                const float rqb = reinterpret_cast<const float *>(P + kPSC + 64)[tok];  // s rq
+                f32x4 AQT;  // chi_{b,a} / rk_a = s rq_b (q_b . k_a decayed), a <= b
+#pragma unroll
+                for (int r = 0; r < 4; ++r) AQT[r] = (4 * g + r <= tok) ? rqb * AQs[r] : 0.f;
+                reinterpret_cast<bf16x8 *>(P + kPAQ)[lane] = split8(AQT);
             }
             if (role == 1 && tau < nch && lane < 16) {
                 // beta of chunk c = tau from the raw beta_raw in stage-A wave 0's ring (landed
@@ -415,6 +434,10 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 if (tau + 2 < nch) stage_a(tau + 2, std::integral_constant<int, 2>{});
                 tick_sync();
             }
+            if (tau + 3 < ticks) {
+                if (tau + 3 < nch) stage_a(tau + 3, std::integral_constant<int, 3>{});
+                tick_sync();
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // nothing still landing in LDS at exit
         return;
@@ -487,8 +510,8 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 sc[16 + tk] = scale * __builtin_amdgcn_rsqf(nq + kL2Eps);
             }
         }
-        if (tau >= 2) {
-            const int c = tau - 2;
+        if (tau >= 3) {
+            const int c = tau - 3;
             const char *L = slots + (c % kFSlots) * kPBytes;
             const int t0 = tb + c * kC, len = min(kC, te - t0);
             // K_b S^T and Q_b S^T for both column tiles (bf16 state operand)
@@ -591,7 +614,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
             consume(std::integral_constant<int, 1>{}, w);
         } else if (nch > 0) {  // transfer-run waves
             if (gseg > 0) {
-                consume(std::integral_constant<int, 2>{}, w - (kFCons + kFPrep + kFSolve));
+                consume(std::integral_constant<int, 2>{}, w - (kFCons + kFPrep + 2));
             } else {
 #pragma unroll 1
                 for (int tau = 0; tau <= ticks; ++tau) bar_sync();  // the start barrier and every tick's
