@@ -112,11 +112,17 @@ constexpr int kCorrWaves = 8;
 constexpr int kCorrTok = 32 * kCorrWaves;  // tokens per workgroup
 constexpr int kCorrLd = kD + 8;            // padded LDS row (bf16): rows 4 banks apart
 
+// LDS row of value channel r = 32p + 8g + 4u + i: row 16 (2p + u) + 4g + i. Result tiles
+// 2p and 2p + 1 then hold channels 32p + 8g + (0..3) and (4..7) in lane group g, so a
+// lane reads and writes eight consecutive output channels (16 bytes) at once.
+__device__ __forceinline__ int corr_row(int r) { return (r & ~31) + 16 * ((r >> 2) & 1) + 4 * ((r >> 3) & 3) + (r & 3); }
+
 // o_t += S_in y_t for every segment after the first. Workgroup (segment, head, j)
 // splits S_in once into bf16 hi and lo halves in LDS, then walks the segment's
 // token blocks j, j + gridDim.y, ... of 256 tokens: wave w takes 32 tokens and
-// forms (S_in y^T) for them as 16x16 tiles (rows: value channels, columns:
-// tokens), so each lane ends with four consecutive value channels of one token.
+// forms (S_in y^T) for them as 16x16 tiles (rows: value channels in the order
+// corr_row gives, columns: tokens), so each lane ends with eight consecutive value
+// channels of one token.
 __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__restrict__ out,
                                                                  const uint16_t *__restrict__ ybuf,
                                                                  const float *__restrict__ sin,
@@ -136,16 +142,23 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
     const float *Sg = sin + ((int64_t)seg * H + h) * kD * kD;
-    for (int i = tid; i < kD * kD / 4; i += 64 * kCorrWaves) {
-        const f32x4 x = reinterpret_cast<const f32x4 *>(Sg)[i];
+    constexpr int kSplitIt = kD * kD / 4 / (64 * kCorrWaves);
+    static_assert(kD * kD / 4 % (64 * kCorrWaves) == 0, "the split covers S_in in whole passes");
+    f32x4 sx[kSplitIt];  // every load of the split issued before the first LDS write
+#pragma unroll
+    for (int it = 0; it < kSplitIt; ++it) sx[it] = reinterpret_cast<const f32x4 *>(Sg)[tid + it * 64 * kCorrWaves];
+#pragma unroll
+    for (int it = 0; it < kSplitIt; ++it) {
+        const int i = tid + it * 64 * kCorrWaves;
+        const f32x4 x = sx[it];
         const int r = (4 * i) / kD, c = (4 * i) % kD;
         const u32x4 u = __builtin_bit_cast(u32x4, x);
         // hi truncated (x - hi is exact in fp32), lo the remainder rounded
         const u32x2 hi = {__builtin_amdgcn_perm(u[1], u[0], 0x07060302u), __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
         const f32x2 r01 = {x[0] - __uint_as_float(u[0] & 0xffff0000u), x[1] - __uint_as_float(u[1] & 0xffff0000u)};
         const f32x2 r23 = {x[2] - __uint_as_float(u[2] & 0xffff0000u), x[3] - __uint_as_float(u[3] & 0xffff0000u)};
-        *reinterpret_cast<u32x2 *>(&Shi[r][c]) = hi;
-        *reinterpret_cast<u32x2 *>(&Slo[r][c]) = u32x2{pk_bf16(r01), pk_bf16(r23)};
+        *reinterpret_cast<u32x2 *>(&Shi[corr_row(r)][c]) = hi;
+        *reinterpret_cast<u32x2 *>(&Slo[corr_row(r)][c]) = u32x2{pk_bf16(r01), pk_bf16(r23)};
     }
     __syncthreads();
 
@@ -155,7 +168,7 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
         // every load of the block's two token tiles is issued before any product, so
         // each wave keeps 2 x (512 B y + 256 B o) per lane-row in flight at once
         bf16x8 yb[2][kD / 32];
-        u32x2 ov[2][8];
+        u32x4 ov[2][kD / 32];
         bool live[2];
         uint16_t *orow[2];
 #pragma unroll
@@ -168,36 +181,47 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
 #pragma unroll
             for (int ks = 0; ks < kD / 32; ++ks) yb[tt][ks] = *reinterpret_cast<const bf16x8 *>(yrow + 32 * ks + 8 * g);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ov[tt][j] = *reinterpret_cast<const u32x2 *>(orow[tt] + 16 * j + 4 * g);
+            for (int p = 0; p < kD / 32; ++p) ov[tt][p] = *reinterpret_cast<const u32x4 *>(orow[tt] + 32 * p + 8 * g);
         }
-        f32x4 acc[2][8];
+        // two halves of the value channels, 64 each: 32 accumulator registers per lane
+        // rather than 64 keep the kernel under 128 VGPRs, so two workgroups share a CU
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int half = 0; half < 2; ++half) {
+            f32x4 acc[2][4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int ks = 0; ks < kD / 32; ++ks) {
+                for (int jj = 0; jj < 4; ++jj) acc[tt][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {  // each S_in fragment pair serves both token tiles
-                const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(&Shi[16 * j + col][32 * ks + 8 * g]);
-                const bf16x8 al = *reinterpret_cast<const bf16x8 *>(&Slo[16 * j + col][32 * ks + 8 * g]);
+            for (int ks = 0; ks < kD / 32; ++ks) {
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    acc[tt][j] = mma32(ah, yb[tt][ks], acc[tt][j]);
-                    acc[tt][j] = mma32(al, yb[tt][ks], acc[tt][j]);
+                for (int jj = 0; jj < 4; ++jj) {  // each S_in fragment pair serves both token tiles
+                    const int j = 4 * half + jj;
+                    const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(&Shi[16 * j + col][32 * ks + 8 * g]);
+                    const bf16x8 al = *reinterpret_cast<const bf16x8 *>(&Slo[16 * j + col][32 * ks + 8 * g]);
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        acc[tt][jj] = mma32(ah, yb[tt][ks], acc[tt][jj]);
+                        acc[tt][jj] = mma32(al, yb[tt][ks], acc[tt][jj]);
+                    }
                 }
+                __builtin_amdgcn_sched_barrier(0);  // keep one k-step's LDS fragments live at a time
             }
-            __builtin_amdgcn_sched_barrier(0);  // keep one k-step's LDS fragments live at a time
-        }
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            if (live[tt]) {
+            for (int tt = 0; tt < 2; ++tt) {
+                if (live[tt]) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const u32x2 o = ov[tt][j];
-                    const f32x2 lo = {bf_lo(o[0]) + acc[tt][j][0], bf_hi(o[0]) + acc[tt][j][1]};
-                    const f32x2 hi = {bf_lo(o[1]) + acc[tt][j][2], bf_hi(o[1]) + acc[tt][j][3]};
-                    *reinterpret_cast<u32x2 *>(orow[tt] + 16 * j + 4 * g) = u32x2{pk_bf16(lo), pk_bf16(hi)};
+                    for (int pp = 0; pp < 2; ++pp) {
+                        const int p = 2 * half + pp;
+                        const u32x4 o = ov[tt][p];
+                        const f32x4 a0 = acc[tt][2 * pp], a1 = acc[tt][2 * pp + 1];
+                        const f32x2 c0 = {bf_lo(o[0]) + a0[0], bf_hi(o[0]) + a0[1]};
+                        const f32x2 c1 = {bf_lo(o[1]) + a0[2], bf_hi(o[1]) + a0[3]};
+                        const f32x2 c2 = {bf_lo(o[2]) + a1[0], bf_hi(o[2]) + a1[1]};
+                        const f32x2 c3 = {bf_lo(o[3]) + a1[2], bf_hi(o[3]) + a1[3]};
+                        *reinterpret_cast<u32x4 *>(orow[tt] + 32 * p + 8 * g) =
+                            u32x4{pk_bf16(c0), pk_bf16(c1), pk_bf16(c2), pk_bf16(c3)};
+                    }
                 }
             }
         }
