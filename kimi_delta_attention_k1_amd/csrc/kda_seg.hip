@@ -25,15 +25,27 @@ __device__ __forceinline__ f32x4 mma4f(float a, float b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// One workgroup (4 waves) per (sequence, head, 16 value rows). The state rows stay
-// in LDS; each step forms S Phi_g + S0_g: wave w owns key columns [32w, 32w+32) as
-// two 16x16 tiles and contracts over the 128 rows of Phi_g in 16x16x4 fp32 steps.
+constexpr int kScanWaves = 8;  // one 16-column tile of the state rows each
+constexpr int kScanDepth = 2;  // segments whose Phi and S0 are in flight ahead of the chain
+
+// LDS column of state column k: the 32 columns 4i + g (i = 0..31) that one lane group g
+// of the 16x16x4 A operand reads are contiguous, so a lane fetches them 16 bytes at a time
+__device__ __forceinline__ int scan_col(int k) { return 32 * (k & 3) + (k >> 2); }
+
+// One workgroup (8 waves) per (sequence, head, 16 value rows). The state rows stay
+// in LDS; each step forms S Phi_g + S0_g: wave w owns key columns [16w, 16w+16) and
+// contracts over the 128 rows of Phi_g in 16x16x4 fp32 steps. The loads of Phi and
+// S0 run kScanDepth segments ahead of the chain, into register buffers that the
+// unrolled loop addresses statically (at most 63 loads per lane stay trackable by the
+// wait counter), so no step waits on a memory round trip.
 template <typename TSt>
-__global__ __launch_bounds__(256) void kseg_scan(const TSt *s0, TSt *s1, const int32_t *__restrict__ seg_off, int H,
-                                                 const float *__restrict__ sfin, const float *__restrict__ phi,
-                                                 float *__restrict__ sin)
+__global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt *s1,
+                                                             const int32_t *__restrict__ seg_off, int H,
+                                                             const float *__restrict__ sfin,
+                                                             const float *__restrict__ phi, float *__restrict__ sin)
 {
-    __shared__ float S[kScanRows][kScanLd];
+    constexpr int kThreads = 64 * kScanWaves;
+    __shared__ __attribute__((aligned(16))) float S[kScanRows][kScanLd];  // columns in scan_col order
     const int n = blockIdx.x / H, h = blockIdx.x % H, r0 = blockIdx.y * kScanRows;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
     const int first = seg_off[n], G = seg_off[n + 1] - first;
@@ -41,70 +53,59 @@ __global__ __launch_bounds__(256) void kseg_scan(const TSt *s0, TSt *s1, const i
     auto seg_off_of = [&](int sg) { return ((int64_t)sg * H + h) * mat; };
 
     // state entering segment 1: segment 0's run started from the initial state
-    for (int i = tid; i < kScanRows * kD; i += 256) {
+    for (int i = tid; i < kScanRows * kD; i += kThreads) {
         const int r = i / kD, c = i % kD;
         float x;
         if (G > 0)
             x = sfin[seg_off_of(first) + (int64_t)(r0 + r) * kD + c];
         else
             x = s0 ? ld_elem(s0, ((int64_t)n * H + h) * mat + (int64_t)(r0 + r) * kD + c) : 0.f;
-        S[r][c] = x;
+        S[r][scan_col(c)] = x;
     }
     __syncthreads();
-    // the loads of step gi + 1 (Phi and S0 of the next segment) are issued before the
-    // products of step gi, so the chain over segments waits on no memory round trip
-    float pb[kD / 4][2];
-    f32x4 z[2];
-    auto load_step = [&](int gi) {
-        const float *P = phi + seg_off_of(first + gi);
-        const float *Z = sfin + seg_off_of(first + gi);
+    float pb[kScanDepth][kD / 4];
+    f32x4 z[kScanDepth];
+    auto load_step = [&](int gi, float(&pp)[kD / 4], f32x4 &zz) {
+        const float *P = phi + seg_off_of(first + gi) + 16 * w + col;
+        const float *Z = sfin + seg_off_of(first + gi) + (int64_t)(r0 + 4 * g) * kD + 16 * w + col;
 #pragma unroll
-        for (int ks = 0; ks < kD / 4; ++ks)
+        for (int ks = 0; ks < kD / 4; ++ks) pp[ks] = P[(int64_t)(4 * ks + g) * kD];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) pb[ks][j] = P[(int64_t)(4 * ks + g) * kD + 32 * w + 16 * j + col];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) z[j][r] = Z[(int64_t)(r0 + 4 * g + r) * kD + 32 * w + 16 * j + col];
+        for (int r = 0; r < 4; ++r) zz[r] = Z[(int64_t)r * kD];
     };
-    if (G > 1) load_step(1);
-#pragma unroll 1
-    for (int gi = 1; gi < G; ++gi) {
+#pragma unroll
+    for (int d = 0; d < kScanDepth; ++d)
+        if (1 + d < G) load_step(1 + d, pb[d], z[d]);
+    auto step = [&](int gi, float(&pp)[kD / 4], f32x4 &zz) {
         float *Sin = sin + seg_off_of(first + gi);
-        for (int i = tid; i < kScanRows * kD; i += 256) Sin[(int64_t)(r0 + i / kD) * kD + i % kD] = S[i / kD][i % kD];
-        float pc[kD / 4][2];
-        f32x4 zc[2];
+        for (int i = tid; i < kScanRows * kD; i += kThreads)
+            Sin[(int64_t)(r0 + i / kD) * kD + i % kD] = S[i / kD][scan_col(i % kD)];
+        f32x4 a[kD / 16];  // A[row col][k = 4 ks + g] for ks = 0..31
 #pragma unroll
-        for (int ks = 0; ks < kD / 4; ++ks)
+        for (int q = 0; q < kD / 16; ++q) a[q] = *reinterpret_cast<const f32x4 *>(&S[col][32 * g + 4 * q]);
+        // four independent accumulation chains (k steps 4i + c go to chain c)
+        f32x4 acc[4];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) pc[ks][j] = pb[ks][j];
+        for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 2; ++j) zc[j] = z[j];
-        if (gi + 1 < G) load_step(gi + 1);
-        // four independent accumulation chains per tile (k steps 4i + c go to chain c)
-        f32x4 acc[2][4];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < kD / 4; ++ks) {
-            const float a = S[col][4 * ks + g];  // A[m = row][k]
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[j][ks & 3] = mma4f(a, pc[ks][j], acc[j][ks & 3]);
-        }
+        for (int ks = 0; ks < kD / 4; ++ks) acc[ks & 3] = mma4f(a[ks / 4][ks % 4], pp[ks], acc[ks & 3]);
+        const f32x4 zc = zz;
+        if (gi + kScanDepth < G) load_step(gi + kScanDepth, pp, zz);  // the buffer is free once read
         __syncthreads();  // every wave has read S
+        const f32x4 sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + zc;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const f32x4 sum = ((acc[j][0] + acc[j][1]) + (acc[j][2] + acc[j][3])) + zc[j];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[4 * g + r][32 * w + 16 * j + col] = sum[r];
-        }
+        for (int r = 0; r < 4; ++r) S[4 * g + r][scan_col(16 * w + col)] = sum[r];
         __syncthreads();
+    };
+    static_assert(kScanDepth == 2, "the loop below is unrolled over the buffers");
+#pragma unroll 1
+    for (int gi = 1; gi < G; gi += kScanDepth) {
+        step(gi, pb[0], z[0]);
+        if (gi + 1 < G) step(gi + 1, pb[1], z[1]);
     }
     if (s1) {
-        for (int i = tid; i < kScanRows * kD; i += 256)
-            st_elem(s1, ((int64_t)n * H + h) * mat + (int64_t)(r0 + i / kD) * kD + i % kD, S[i / kD][i % kD]);
+        for (int i = tid; i < kScanRows * kD; i += kThreads)
+            st_elem(s1, ((int64_t)n * H + h) * mat + (int64_t)(r0 + i / kD) * kD + i % kD, S[i / kD][scan_col(i % kD)]);
     }
 }
 
@@ -236,7 +237,7 @@ static hipError_t launch_seg_finish_t(const Problem &p, hipStream_t s)
     const float *sfin = reinterpret_cast<const float *>(p.ws + p.lay.sfin);
     const float *phi = reinterpret_cast<const float *>(p.ws + p.lay.phi);
     float *sin = reinterpret_cast<float *>(p.ws + p.lay.sin);
-    hipLaunchKernelGGL(kseg_scan<TSt>, dim3((unsigned)(p.N * p.H), kD / kScanRows), dim3(256), 0, s,
+    hipLaunchKernelGGL(kseg_scan<TSt>, dim3((unsigned)(p.N * p.H), kD / kScanRows), dim3(64 * kScanWaves), 0, s,
                        (const TSt *)p.s0, (TSt *)p.s1, seg, p.H, sfin, phi, sin);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     // token blocks of a segment spread over enough workgroups to fill the GPU about twice
