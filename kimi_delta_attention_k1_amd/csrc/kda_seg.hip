@@ -25,8 +25,10 @@ __device__ __forceinline__ f32x4 mma4f(float a, float b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-constexpr int kScanWaves = 8;  // one 16-column tile of the state rows each
-constexpr int kScanDepth = 2;  // segments whose Phi and S0 are in flight ahead of the chain
+constexpr int kScanWaves = 8;    // one 16-column tile of the state rows each
+constexpr int kScanDepth = 3;    // segments whose Phi and S0 are in flight ahead of the chain
+constexpr int kScanPhiLd = kD + 16;  // padded LDS row of Phi (floats): the four k rows a
+                                     // B-operand read touches fall 16 banks apart
 
 // LDS column of state column k: the 32 columns 4i + g (i = 0..31) that one lane group g
 // of the 16x16x4 A operand reads are contiguous, so a lane fetches them 16 bytes at a time
@@ -34,10 +36,10 @@ __device__ __forceinline__ int scan_col(int k) { return 32 * (k & 3) + (k >> 2);
 
 // One workgroup (8 waves) per (sequence, head, 16 value rows). The state rows stay
 // in LDS; each step forms S Phi_g + S0_g: wave w owns key columns [16w, 16w+16) and
-// contracts over the 128 rows of Phi_g in 16x16x4 fp32 steps. The loads of Phi and
-// S0 run kScanDepth segments ahead of the chain, into register buffers that the
-// unrolled loop addresses statically (at most 63 loads per lane stay trackable by the
-// wait counter), so no step waits on a memory round trip.
+// contracts over the 128 rows of Phi_g in 16x16x4 fp32 steps, with Phi_g and the S0_g
+// rows staged through LDS. Their 16-byte loads run kScanDepth segments ahead of the
+// chain (ten memory operations per lane and step, well within what the wait counter
+// tracks), into register buffers that the unrolled loop addresses statically.
 template <typename TSt>
 __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt *s1,
                                                              const int32_t *__restrict__ seg_off, int H,
@@ -45,12 +47,19 @@ __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt 
                                                              const float *__restrict__ phi, float *__restrict__ sin)
 {
     constexpr int kThreads = 64 * kScanWaves;
+    constexpr int kPhiLoads = kD * kD / 4 / kThreads;  // float4 loads of Phi per lane
+    static_assert(kPhiLoads * kThreads * 4 == kD * kD && kScanRows * kD == 4 * kThreads,
+                  "Phi in whole passes of float4 loads, the S0 rows in one");
     __shared__ __attribute__((aligned(16))) float S[kScanRows][kScanLd];  // columns in scan_col order
+    __shared__ __attribute__((aligned(16))) float Ph[kD][kScanPhiLd];
+    __shared__ __attribute__((aligned(16))) float Zs[kScanRows][kScanLd];
     const int n = blockIdx.x / H, h = blockIdx.x % H, r0 = blockIdx.y * kScanRows;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
     const int first = seg_off[n], G = seg_off[n + 1] - first;
     const int64_t mat = (int64_t)kD * kD;
     auto seg_off_of = [&](int sg) { return ((int64_t)sg * H + h) * mat; };
+    // this lane's 16-byte pieces: Phi element 4 (tid + it kThreads) and S0 row r0 + zr, columns zc..zc+3
+    const int zr = tid / (kD / 4), zc = 4 * (tid % (kD / 4));
 
     // state entering segment 1: segment 0's run started from the initial state
     for (int i = tid; i < kScanRows * kD; i += kThreads) {
@@ -62,47 +71,68 @@ __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt 
             x = s0 ? ld_elem(s0, ((int64_t)n * H + h) * mat + (int64_t)(r0 + r) * kD + c) : 0.f;
         S[r][scan_col(c)] = x;
     }
-    __syncthreads();
-    float pb[kScanDepth][kD / 4];
+    f32x4 pb[kScanDepth][kPhiLoads];
     f32x4 z[kScanDepth];
-    auto load_step = [&](int gi, float(&pp)[kD / 4], f32x4 &zz) {
-        const float *P = phi + seg_off_of(first + gi) + 16 * w + col;
-        const float *Z = sfin + seg_off_of(first + gi) + (int64_t)(r0 + 4 * g) * kD + 16 * w + col;
+    auto load_step = [&](int gi, f32x4(&pp)[kPhiLoads], f32x4 &zz) {
+        const f32x4 *P = reinterpret_cast<const f32x4 *>(phi + seg_off_of(first + gi));
 #pragma unroll
-        for (int ks = 0; ks < kD / 4; ++ks) pp[ks] = P[(int64_t)(4 * ks + g) * kD];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) zz[r] = Z[(int64_t)r * kD];
+        for (int it = 0; it < kPhiLoads; ++it) pp[it] = P[tid + it * kThreads];
+        zz = *reinterpret_cast<const f32x4 *>(sfin + seg_off_of(first + gi) + (int64_t)(r0 + zr) * kD + zc);
     };
+    // loads past the last segment re-read it (clamped), so every loop iteration issues
+    // the same memory operations and the waits before a buffer's use stay exact
+    if (G > 1) {
 #pragma unroll
-    for (int d = 0; d < kScanDepth; ++d)
-        if (1 + d < G) load_step(1 + d, pb[d], z[d]);
-    auto step = [&](int gi, float(&pp)[kD / 4], f32x4 &zz) {
-        float *Sin = sin + seg_off_of(first + gi);
-        for (int i = tid; i < kScanRows * kD; i += kThreads)
-            Sin[(int64_t)(r0 + i / kD) * kD + i % kD] = S[i / kD][scan_col(i % kD)];
+        for (int d = 0; d < kScanDepth; ++d) load_step(min(1 + d, G - 1), pb[d], z[d]);
+    }
+    __syncthreads();
+    auto step = [&](int gi, f32x4(&pp)[kPhiLoads], f32x4 &zz) {
+        // the previous step's reads of Ph and Zs ended at its barrier
+#pragma unroll
+        for (int it = 0; it < kPhiLoads; ++it) {
+            const int e = 4 * (tid + it * kThreads);
+            *reinterpret_cast<f32x4 *>(&Ph[e / kD][e % kD]) = pp[it];
+        }
+        *reinterpret_cast<f32x4 *>(&Zs[zr][zc]) = zz;
+        load_step(min(gi + kScanDepth, G - 1), pp, zz);  // the buffers are free once stored
+        __syncthreads();  // Ph, Zs and the previous step's S rows are in place
+        {
+            f32x4 x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = S[zr][scan_col(zc + j)];
+            *reinterpret_cast<f32x4 *>(sin + seg_off_of(first + gi) + (int64_t)(r0 + zr) * kD + zc) = x;
+        }
         f32x4 a[kD / 16];  // A[row col][k = 4 ks + g] for ks = 0..31
 #pragma unroll
         for (int q = 0; q < kD / 16; ++q) a[q] = *reinterpret_cast<const f32x4 *>(&S[col][32 * g + 4 * q]);
+        float b[kD / 4];  // B[k = 4 ks + g][column 16 w + col]
+#pragma unroll
+        for (int ks = 0; ks < kD / 4; ++ks) b[ks] = Ph[4 * ks + g][16 * w + col];
         // four independent accumulation chains (k steps 4i + c go to chain c)
         f32x4 acc[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < kD / 4; ++ks) acc[ks & 3] = mma4f(a[ks / 4][ks % 4], pp[ks], acc[ks & 3]);
-        const f32x4 zc = zz;
-        if (gi + kScanDepth < G) load_step(gi + kScanDepth, pp, zz);  // the buffer is free once read
-        __syncthreads();  // every wave has read S
-        const f32x4 sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + zc;
+        for (int ks = 0; ks < kD / 4; ++ks) acc[ks & 3] = mma4f(a[ks / 4][ks % 4], b[ks], acc[ks & 3]);
+        f32x4 zv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zv[r] = Zs[4 * g + r][16 * w + col];
+        __syncthreads();  // every wave has read S, Ph and Zs
+        const f32x4 sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + zv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[4 * g + r][scan_col(16 * w + col)] = sum[r];
-        __syncthreads();
     };
-    static_assert(kScanDepth == 2, "the loop below is unrolled over the buffers");
+    static_assert(kScanDepth == 3, "the loop below is unrolled over the buffers");
+    int gi = 1;
 #pragma unroll 1
-    for (int gi = 1; gi < G; gi += kScanDepth) {
+    for (; gi + 2 < G; gi += kScanDepth) {
         step(gi, pb[0], z[0]);
-        if (gi + 1 < G) step(gi + 1, pb[1], z[1]);
+        step(gi + 1, pb[1], z[1]);
+        step(gi + 2, pb[2], z[2]);
     }
+    if (gi < G) step(gi, pb[0], z[0]);
+    if (gi + 1 < G) step(gi + 1, pb[1], z[1]);
+    __syncthreads();  // the last step's S rows are in place
     if (s1) {
         for (int i = tid; i < kScanRows * kD; i += kThreads)
             st_elem(s1, ((int64_t)n * H + h) * mat + (int64_t)(r0 + i / kD) * kD + i % kD, S[i / kD][scan_col(i % kD)]);
