@@ -62,6 +62,18 @@ def test_ragged_segments_and_empty_sequences(gpu, lb):
         assert torch.equal(s[n].cpu(), w.initial_state[n])
 
 
+def test_segment_counts_five_six_seven(gpu):
+    # 3 sequences x 2 heads: segments of L = 16 chunks after a first one of 20, so
+    # 84, 100 and 116 chunks make 5, 6 and 7 segments. The scan walks segments 1..G-1
+    # three at a time and then the one or two left over: 4, 5 and 6 steps cover a
+    # whole group plus a tail of one, plus a tail of two, and two whole groups.
+    _banner("segment counts 5, 6 and 7 (scan groups and tails), H=2, initial state")
+    w = workloads.make([1344, 1600, 1856], 2, seed=13, init_std=0.02, beta_mean=0.5)
+    ref = run_oracle(w)
+    o, s = run_gpu(w, gpu, path="segmented")
+    compare(w, o, s, ref, bf16_tol, "segmented, 5/6/7 segments")
+
+
 def test_batch_mode_no_initial_state_no_final(gpu):
     _banner("batch mode B=2 T=1000 H=4, no initial state, no final state")
     w = workloads.make([1000, 1000], 4, seed=12, packed=False)
