@@ -476,38 +476,30 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
     if (ticks > 0) bar_sync();  // start: the stage-A waves have waited for chunk 0 in their rings
 #pragma unroll 1
     for (int tau = 0; tau < ticks; ++tau) {
-        if (MODE != 2 && tau < nch) {
+        if (MODE != 2 && tau < nch && (cw & 1)) {
             // per-token scales of chunk tau from the raw inputs in the stage-A rings
-            // (landed before the last barrier, refilled only next tick): wave cw takes
-            // tokens 4cw..4cw+3, lane (token, cg) channels [8cg, 8cg+8), summed over the
-            // 16-lane row; rk = 1/|k| and s rq = s/|q| go to the chunk's slot for stage B
-            // (next tick) and for the consumers' own step two ticks later
-            const int tk = 4 * cw + g, cg = col;
-            const char *I = inring + ((cg >> 2) * kFIn + tau % kFIn) * kIBytes + tk * 64 + (cg & 3) * 16;
-            const u32x4 qv = *reinterpret_cast<const u32x4 *>(I + kIQ);
-            const u32x4 kv = *reinterpret_cast<const u32x4 *>(I + kIK);
-            float nq = 0.f, nk = 0.f;
+            // (landed before the last barrier, refilled only next tick). The squared
+            // norms of the 16 k rows (wave 3) or q rows (wave 1) are the diagonal of their
+            // Gram matrix: four 16x16x32 bf16 products over the 128 channels, exact
+            // products accumulated in fp32, with the same registers as both operands.
+            // Lane (token i, group i/4) holds |x_i|^2. rk = 1/|k| and s rq = s/|q| go to
+            // the chunk's slot for stage B (next tick) and for the consumers' own step
+            // two ticks later. Waves 1 and 3 share their SIMDs with the lighter stage-B
+            // roles.
+            static_assert(kFCons == 4, "consumer waves 1 and 3 form the norms");
+            const bool isk = cw == 3;
+            const char *I = inring + (tau % kFIn) * kIBytes + col * 64 + g * 16 + (isk ? kIK : kIQ);
+            f32x4 gram = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float q0 = bf_lo(qv[e]), q1 = bf_hi(qv[e]), k0 = bf_lo(kv[e]), k1 = bf_hi(kv[e]);
-                nq += q0 * q0;
-                nq += q1 * q1;
-                nk += k0 * k0;
-                nk += k1 * k1;
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(I + ks * kFIn * kIBytes);
+                gram = mma32(x, x, gram);
             }
-            asm("" : "+v"(nq), "+v"(nk));
-            nq += row_shr<1>(nq);
-            nk += row_shr<1>(nk);
-            nq += row_shr<2>(nq);
-            nk += row_shr<2>(nk);
-            nq += row_shr<4>(nq);
-            nk += row_shr<4>(nk);
-            nq += row_shr<8>(nq);
-            nk += row_shr<8>(nk);
-            if (col == 15) {  // the row's total
+            if ((col >> 2) == g) {
+                const float n2 = (col & 2) ? ((col & 1) ? gram[3] : gram[2]) : ((col & 1) ? gram[1] : gram[0]);
                 float *sc = reinterpret_cast<float *>(slots + (tau % kFSlots) * kPBytes + kPSC);
-                sc[tk] = __builtin_amdgcn_rsqf(nk + kL2Eps);
-                sc[16 + tk] = scale * __builtin_amdgcn_rsqf(nq + kL2Eps);
+                const float r = __builtin_amdgcn_rsqf(n2 + kL2Eps);
+                sc[isk ? col : 16 + col] = isk ? r : scale * r;
             }
         }
         if (tau >= 3) {
