@@ -160,62 +160,68 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
         const int role = w == kFCons + kFPrep + 1 ? 1 : 0;
         const int parity = w == w_inv_odd ? 1 : 0;  // inverse waves: chunks of this parity
         const int tok = lane & 15, g = lane >> 4;  // D layout: rows 4g+r, column tok
-        // carried from an inverse's first half (tick c+1) to its second (tick c+2)
-        f32x4 M2 = {0.f, 0.f, 0.f, 0.f}, M2T = M2, P1 = M2, beta_a = M2;
-        float rkb = 0.f;
+        // A B^T over the 128 key channels: the four waves' 32-channel operand slices of
+        // chunk c, one chained 16x16x32 product each (fp32 accumulation)
+        auto contract = [&](const char *X, int offa, int offb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mm = 0; mm < kFPrep; ++mm)
+                acc = mma32(reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offa)[lane],
+                            reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offb)[lane], acc);
+            return acc;
+        };
         bar_sync();  // start: the stage-A waves have waited for chunk 0 in their rings
+        if (role == 0) {
+            // (A^kk)^T = (I + R^T)^-1 = (I-M)(I+M^2)(I+M^4)(I+M^8), M = R^T, with fp16
+            // operands and fp32 accumulation: the inverse's entries are bounded by 1 in
+            // magnitude (FlashKDA deep-dive, section 3), so fp16's range suffices. Each
+            // chunk c of this wave's parity takes two ticks: the first half at tick c+1,
+            // the second at tick c+2. One loop iteration covers both, so the values
+            // carried between them stay in the same registers.
+            int tau = 0;
+#pragma unroll 1
+            for (; tau <= parity; ++tau) tick_sync();  // ticks before chunk parity's first half
+#pragma unroll 1
+            for (int c = parity; c < nch; c += 2, tau += 2) {
+                const char *X = parts + (c & 1) * kXBytes;
+                char *P = slots + (c % kFSlots) * kPBytes;
+                // first half: R, R^T, M^2 and (I - M)(I + M^2)
+                const f32x4 Rs = contract(X, kXKR, kXKI), RTs = contract(X, kXKI, kXKR);
+                const f32x4 beta_a = *reinterpret_cast<const f32x4 *>(X + kXBeta + 16 * g);
+                const float beta_b = reinterpret_cast<const float *>(X + kXBeta)[tok];
+                // rk = 1 / |k| per token, formed by the consumers in the previous tick
+                const float rkb = reinterpret_cast<const float *>(P + kPSC)[tok];
+                const f32x4 rka = *reinterpret_cast<const f32x4 *>(P + kPSC + 16 * g);
+                f32x4 R, RT;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int a = 4 * g + r;
+                    R[r] = (tok < a) ? beta_a[r] * rka[r] * rkb * Rs[r] : 0.f;
+                    RT[r] = (a < tok) ? beta_b * rkb * rka[r] * RTs[r] : 0.f;
+                }
+                const f32x4 M2 = mm16_h(R, RT);
+                const f32x4 M2T = mm16_h(RT, R);
+                const f32x4 P1 = mm16_h(eye_plus(R, -1.f, g, tok), eye_plus(M2, 1.f, g, tok));
+                tick_sync();
+                // second half: M^4, M^8, the product, the store
+                const f32x4 M4 = mm16_h(M2T, M2);
+                const f32x4 M4T = mm16_h(M2, M2T);
+                const f32x4 M8T = mm16_h(M4, M4T);
+                const f32x4 P2 = mm16_h(eye_plus(M4T, 1.f, g, tok), P1);
+                const f32x4 AT = mm16_h(eye_plus(M8T, 1.f, g, tok), P2);
+                f32x4 ABT;  // rk_b beta_a A^kk[b][a]: E' = Diag(rk) A^kk Diag(beta) Ebar
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ABT[r] = rkb * beta_a[r] * AT[r];
+                reinterpret_cast<bf16x8 *>(P + kPAB)[lane] = split8(ABT);
+                tick_sync();
+            }
+#pragma unroll 1
+            for (; tau < ticks; ++tau) tick_sync();  // the rest only keep the barrier count
+            return;
+        }
 #pragma unroll 1
         for (int tau = 0; tau < ticks; ++tau) {
-            // A B^T over the 128 key channels: the four waves' 32-channel operand slices of
-            // chunk c, one chained 16x16x32 product each (fp32 accumulation)
-            auto contract = [&](const char *X, int offa, int offb) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int mm = 0; mm < kFPrep; ++mm)
-                    acc = mma32(reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offa)[lane],
-                                reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offb)[lane], acc);
-                return acc;
-            };
-            if (role == 0) {
-                // (A^kk)^T = (I + R^T)^-1 = (I-M)(I+M^2)(I+M^4)(I+M^8), M = R^T, with fp16
-                // operands and fp32 accumulation: the inverse's entries are bounded by 1
-                // in magnitude (FlashKDA deep-dive, section 3), so fp16's range suffices.
-                // Each chunk's inverse takes two ticks on one of the two inverse waves.
-                const int c2 = tau - 2;  // second half: M^4, M^8, the product, the store
-                if (c2 >= 0 && c2 < nch && (c2 & 1) == parity) {
-                    char *P = slots + (c2 % kFSlots) * kPBytes;
-                    const f32x4 M4 = mm16_h(M2T, M2);
-                    const f32x4 M4T = mm16_h(M2, M2T);
-                    const f32x4 M8T = mm16_h(M4, M4T);
-                    const f32x4 P2 = mm16_h(eye_plus(M4T, 1.f, g, tok), P1);
-                    const f32x4 AT = mm16_h(eye_plus(M8T, 1.f, g, tok), P2);
-                    f32x4 ABT;  // rk_b beta_a A^kk[b][a]: E' = Diag(rk) A^kk Diag(beta) Ebar
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) ABT[r] = rkb * beta_a[r] * AT[r];
-                    reinterpret_cast<bf16x8 *>(P + kPAB)[lane] = split8(ABT);
-                }
-                const int c1 = tau - 1;  // first half: R, R^T, M^2 and (I - M)(I + M^2)
-                if (c1 >= 0 && c1 < nch && (c1 & 1) == parity) {
-                    const char *X = parts + (c1 & 1) * kXBytes;
-                    const char *P = slots + (c1 % kFSlots) * kPBytes;
-                    const f32x4 Rs = contract(X, kXKR, kXKI), RTs = contract(X, kXKI, kXKR);
-                    beta_a = *reinterpret_cast<const f32x4 *>(X + kXBeta + 16 * g);
-                    const float beta_b = reinterpret_cast<const float *>(X + kXBeta)[tok];
-                    // rk = 1 / |k| per token, formed by the consumers in the previous tick
-                    rkb = reinterpret_cast<const float *>(P + kPSC)[tok];
-                    const f32x4 rka = *reinterpret_cast<const f32x4 *>(P + kPSC + 16 * g);
-                    f32x4 R, RT;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int a = 4 * g + r;
-                        R[r] = (tok < a) ? beta_a[r] * rka[r] * rkb * Rs[r] : 0.f;
-                        RT[r] = (a < tok) ? beta_b * rkb * rka[r] * RTs[r] : 0.f;
-                    }
-                    M2 = mm16_h(R, RT);
-                    M2T = mm16_h(RT, R);
-                    P1 = mm16_h(eye_plus(R, -1.f, g, tok), eye_plus(M2, 1.f, g, tok));
-                }
-            } else if (tau >= 1 && tau - 1 < nch) {
+            if (tau >= 1 && tau - 1 < nch) {
                 const int c = tau - 1;
                 const char *X = parts + (c & 1) * kXBytes;
                 char *P = slots + (c % kFSlots) * kPBytes;
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 for (int r = 0; r < 4; ++r) AQT[r] = (4 * g + r <= tok) ? rqb * AQs[r] : 0.f;
                 reinterpret_cast<bf16x8 *>(P + kPAQ)[lane] = split8(AQT);
             }
-            if (role == 1 && tau < nch && lane < 16) {
+            if (tau < nch && lane < 16) {
                 // beta of chunk c = tau from the raw beta_raw in stage-A wave 0's ring (landed
                 // before the last barrier, refilled only next tick): the low or high half of
                 // the aligned dword; rows past the end of the sequence get beta = 0 (absent)
