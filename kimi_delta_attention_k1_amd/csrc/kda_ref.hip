@@ -22,21 +22,35 @@ namespace kda {
 // ---------------------------------------------------------------------------
 constexpr int kMapThreads = 1024;
 
+constexpr int kMapWaves = kMapThreads / 64;
+
+// inclusive scan (sum, or running max) over the workgroup: lane shuffles within each
+// wave, then one wave scans the wave totals; sh[kMapThreads] receives the total
 __device__ __forceinline__ int block_scan_incl(int x, int *sh, bool is_max)
 {
-    const int t = threadIdx.x;
-    sh[t] = x;
-    __syncthreads();
-    for (int off = 1; off < kMapThreads; off <<= 1) {
-        int y = (t >= off) ? sh[t - off] : (is_max ? INT32_MIN : 0);
-        __syncthreads();
-        x = is_max ? max(x, y) : x + y;
-        sh[t] = x;
-        __syncthreads();
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int ident = is_max ? INT32_MIN : 0;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x = is_max ? max(x, y) : x + y;
     }
-    int total = sh[kMapThreads - 1];
+    if (lane == 63) sh[w] = x;  // wave totals
     __syncthreads();
-    sh[kMapThreads] = total;  // broadcast slot
+    if (w == 0) {
+        int v = lane < kMapWaves ? sh[lane] : ident;
+        for (int off = 1; off < kMapWaves; off <<= 1) {
+            const int y = __shfl_up(v, off, 64);
+            if (lane >= off) v = is_max ? max(v, y) : v + y;
+        }
+        if (lane < kMapWaves) sh[kMapWaves + lane] = v;  // inclusive over waves
+        if (lane == kMapWaves - 1) sh[kMapThreads] = v;  // broadcast slot
+    }
+    __syncthreads();
+    if (w > 0) {
+        const int y = sh[kMapWaves + w - 1];
+        x = is_max ? max(x, y) : x + y;
+    }
+    __syncthreads();  // the caller reads sh[kMapThreads]; the next scan rewrites sh
     return x;
 }
 
@@ -48,6 +62,10 @@ __global__ __launch_bounds__(kMapThreads) void k0_chunk_map(const int32_t *__res
                                                              int32_t *__restrict__ order)
 {
     __shared__ int sh[kMapThreads + 1];
+    // with N <= kMapThreads every offset is also kept here, so later passes read LDS
+    // rather than global memory just written by other threads
+    __shared__ int ltok[kMapThreads + 1], lchk[kMapThreads + 1];
+    const bool small = N <= kMapThreads;
     const int t = threadIdx.x;
     __shared__ int bad;
     if (t == 0) bad = 0;
@@ -72,6 +90,7 @@ __global__ __launch_bounds__(kMapThreads) void k0_chunk_map(const int32_t *__res
         }
         int s = block_scan_incl(x, sh, true);
         if (n <= N) tok_off[n] = s;
+        if (small && n <= N) ltok[n] = s;
         carry = sh[kMapThreads];
         __syncthreads();
     }
@@ -82,9 +101,10 @@ __global__ __launch_bounds__(kMapThreads) void k0_chunk_map(const int32_t *__res
     for (int base = 0; base <= N; base += kMapThreads) {
         const int n = base + t;
         int cnt = 0;
-        if (n < N) cnt = (tok_off[n + 1] - tok_off[n] + kC - 1) / kC;
+        if (n < N) cnt = small ? (ltok[n + 1] - ltok[n] + kC - 1) / kC : (tok_off[n + 1] - tok_off[n] + kC - 1) / kC;
         int s = block_scan_incl(cnt, sh, false);
         if (n <= N) chunk_off[n] = carry + s - cnt;  // exclusive
+        if (small && n <= N) lchk[n] = carry + s - cnt;
         carry += sh[kMapThreads];
         __syncthreads();
     }
@@ -96,7 +116,7 @@ __global__ __launch_bounds__(kMapThreads) void k0_chunk_map(const int32_t *__res
         for (int base = 0; base <= N; base += kMapThreads) {
             const int n = base + t;
             int cnt = 0;
-            if (n < N) cnt = seg_count(chunk_off[n + 1] - chunk_off[n], seg_len, seg_first);
+            if (n < N) cnt = seg_count(small ? lchk[n + 1] - lchk[n] : chunk_off[n + 1] - chunk_off[n], seg_len, seg_first);
             int s = block_scan_incl(cnt, sh, false);
             if (n <= N) seg_off[n] = carry + s - cnt;
             carry += sh[kMapThreads];
@@ -110,10 +130,10 @@ __global__ __launch_bounds__(kMapThreads) void k0_chunk_map(const int32_t *__res
         __syncthreads();
         if (N <= kMapThreads) {
             if (t < N) {
-                const int ct = chunk_off[t + 1] - chunk_off[t];
+                const int ct = lchk[t + 1] - lchk[t];
                 int rank = 0;
                 for (int m = 0; m < N; ++m) {
-                    const int cm = chunk_off[m + 1] - chunk_off[m];
+                    const int cm = lchk[m + 1] - lchk[m];
                     rank += (cm > ct || (cm == ct && m < t)) ? 1 : 0;
                 }
                 order[rank] = t;
