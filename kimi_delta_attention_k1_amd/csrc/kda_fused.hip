@@ -17,9 +17,9 @@
 // separated by one workgroup barrier; chunk c is handled at
 //   tick c    : stage A -- gate, prefix sums, decays; the wave's 32-channel
 //               slices of the in-chunk operands, and K_b / Q_b / K_end / gamma / v
-//               into prepared slot c % 4; the consumers -- the per-token scales
-//               rk = 1/|k|, s rq = s/|q| of chunk c from the raw inputs; stage B
-//               wave 9 -- its beta
+//               into prepared slot c % 4; consumer waves 3 and 1 -- the per-token
+//               scales rk = 1/|k|, s rq = s/|q| of chunk c from the raw inputs (the
+//               diagonals of the raw rows' Gram matrices); stage B wave 9 -- its beta
 //   tick c+1  : stage B -- contracts the operands over the 128 channels; wave 9
 //               forms (A^qk)^T; the chunk's inverse wave forms R, R^T, M^2 and
 //               (I - M)(I + M^2)
@@ -51,8 +51,8 @@ constexpr int kFThreadsSeg = kFThreads + 64 * kFCons;         // 960: + the tran
 constexpr int kFIn = 3;                               // input-ring slots per prep wave (two chunks in flight)
 constexpr int kFSlots = 4;                            // prepared-chunk slots (stage A steps through them unrolled)
 constexpr int kFDma = 5;                              // global-to-LDS loads per chunk per prep wave
-// a ring slot is refilled one tick after its chunk's stage-A tick (stage B role 1 reads the
-// raw q, k and beta_raw of chunk c from the rings during tick c), so kFIn - 1 chunks are in
+// a ring slot is refilled one tick after its chunk's stage-A tick (the consumers read the raw
+// q and k, stage B role 1 the beta_raw, of chunk c from the rings during tick c), so kFIn - 1 chunks are in
 // flight: waiting for chunk c + 1 at the end of tick c leaves two chunks' loads outstanding
 constexpr int kFPending = (kFIn - 2) * kFDma;         // loads allowed in flight when chunk c+1 must have landed
 static_assert(kFPending <= 63, "vmcnt holds at most 63 outstanding loads");
