@@ -74,6 +74,16 @@ def test_segment_counts_five_six_seven(gpu):
     compare(w, o, s, ref, bf16_tol, "segmented, 5/6/7 segments")
 
 
+def test_one_pair_many_segments(gpu):
+    # one pair of 4096 chunks: G = 256 segments wanted, L = 16 chunks after a first one
+    # of 20, so 256 segments: a long scan and 255 corrected segments
+    _banner("one sequence of 65536 tokens, H=1: 256 segments")
+    w = workloads.make([65536], 1, seed=14, init_std=0.02, beta_mean=0.5)
+    ref = run_oracle(w)
+    o, s = run_gpu(w, gpu, path="segmented")
+    compare(w, o, s, ref, bf16_tol, "segmented, 256 segments")
+
+
 def test_batch_mode_no_initial_state_no_final(gpu):
     _banner("batch mode B=2 T=1000 H=4, no initial state, no final state")
     w = workloads.make([1000, 1000], 4, seed=12, packed=False)
