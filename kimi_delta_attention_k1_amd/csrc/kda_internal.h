@@ -60,8 +60,8 @@ inline bool use_lookahead(int64_t N, int64_t H, bool f32_path, bool bf16_residen
 // is cut into G = max(2, kSegTargetGroups / pairs) segments (from the average
 // sequence), so that at most about kSegTargetGroups (segment, head) workgroups, one
 // per compute unit, run at once. Every segment after the first is L chunks long;
-// the first is L0 = L + L/4 long, because its workgroups skip the transfer run and
-// take about a quarter less time per chunk. Workspace after the chunk map:
+// the first is L0 = L + L/2 long, because its workgroups skip the transfer run and
+// take about a third less time per chunk. Workspace after the chunk map:
 //   seg_off [N+1] int32             exclusive scan of segments per sequence
 //   sfin    [seg_max][H][128][128]  fp32, segment's final state from S = 0 (seg 0: S_0)
 //   phi     [seg_max][H][128][128]  fp32, segment's key-space transfer
@@ -69,15 +69,15 @@ inline bool use_lookahead(int64_t N, int64_t H, bool f32_path, bool bf16_residen
 //   ybuf    [T_tot][H][128]         bf16, y_t = Phi_t (s qhat_t) within the segment
 constexpr int64_t kSegTargetGroups = 256;
 constexpr int64_t kSegMinChunks = 16;
-inline int64_t seg_first_for(int64_t seg_len) { return seg_len + (seg_len + 3) / 4; }
+inline int64_t seg_first_for(int64_t seg_len) { return seg_len + (seg_len + 1) / 2; }
 inline int64_t seg_len_for(int64_t N, int64_t H, int64_t n_c_max)
 {
     const int64_t pairs = N * H;
     int64_t G = kSegTargetGroups / pairs;
     if (G < 2) G = 2;
     const int64_t avg = (n_c_max + N - 1) / N;
-    // L0 + (G - 1) L = avg with L0 = 5 L / 4
-    const int64_t l = (4 * avg + 4 * G) / (4 * G + 1);
+    // L0 + (G - 1) L = avg with L0 = 3 L / 2
+    const int64_t l = (2 * avg + 2 * G) / (2 * G + 1);
     return l > kSegMinChunks ? l : kSegMinChunks;
 }
 // upper bound of the segment count given sum_n chunks_n <= n_c_max: every segment

@@ -201,11 +201,11 @@ def test_path_flags_and_workspace(lib):
 def _seg_layout(N, H, T_tot, n_c):
     """Chunk map, segment offsets, three fp32 [128][128] matrices per (segment, head)
     and a bf16 [T_tot][H][128] buffer. G = max(2, 256 // (N H)) segments per average
-    sequence of A = ceil(n_c / N) chunks, the first 5/4 as long as the others:
-    L = max(16, (4 A + 4 G) // (4 G + 1)), at most n_c // L + N segments."""
+    sequence of A = ceil(n_c / N) chunks, the first 3/2 as long as the others:
+    L = max(16, (2 A + 2 G) // (2 G + 1)), at most n_c // L + N segments."""
     G = max(2, 256 // (N * H))
     A = -(-n_c // N)
-    L = max(16, (4 * A + 4 * G) // (4 * G + 1))
+    L = max(16, (2 * A + 2 * G) // (2 * G + 1))
     smax = n_c // L + N
     seg = _layout(N, H, 0, 0)
     sfin = (seg + 4 * (N + 1) + 127) // 128 * 128
@@ -213,7 +213,7 @@ def _seg_layout(N, H, T_tot, n_c):
 
 
 def test_segmented_path_workspace(lib):
-    # C4: one sequence of 131072 tokens, H=32 -> 8192 chunks: segments of 1242 chunks, then 993
+    # C4: one sequence of 131072 tokens, H=32 -> 8192 chunks: segments of 1446 chunks, then 964
     assert kda.workspace_size(1, 131072, 1, 32, path="segmented") == _seg_layout(1, 32, 131072, 8192)
     # the automatic rule picks the segmented pass there; the size covers it and the split path
     split = _layout(1, 32, 8192, 14848, look=True)

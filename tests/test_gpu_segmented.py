@@ -63,7 +63,7 @@ def test_ragged_segments_and_empty_sequences(gpu, lb):
 
 
 def test_segment_counts_five_six_seven(gpu):
-    # 3 sequences x 2 heads: segments of L = 16 chunks after a first one of 20, so
+    # 3 sequences x 2 heads: segments of L = 16 chunks after a first one of 24, so
     # 84, 100 and 116 chunks make 5, 6 and 7 segments. The scan walks segments 1..G-1
     # three at a time and then the one or two left over: 4, 5 and 6 steps cover a
     # whole group plus a tail of one, plus a tail of two, and two whole groups.
@@ -76,7 +76,7 @@ def test_segment_counts_five_six_seven(gpu):
 
 def test_one_pair_many_segments(gpu):
     # one pair of 4096 chunks: G = 256 segments wanted, L = 16 chunks after a first one
-    # of 20, so 256 segments: a long scan and 255 corrected segments
+    # of 24, so 256 segments: a long scan and 255 corrected segments
     _banner("one sequence of 65536 tokens, H=1: 256 segments")
     w = workloads.make([65536], 1, seed=14, init_std=0.02, beta_mean=0.5)
     ref = run_oracle(w)
