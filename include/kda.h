@@ -53,12 +53,17 @@ extern "C" {
  * the pages use -5, FlashKDA review section 2.1). */
 #define KDA_LOWER_BOUND_MIN (-10.0f)
 #define KDA_LOWER_BOUND_MAX (0.0f)
+/* Largest lower_bound accepted with KDA_FLAG_BF16_RESIDENT_STATE. */
+#define KDA_BF16_RESIDENT_MAX_LOWER_BOUND (-0.2f)
 
 typedef enum kda_status {
     KDA_OK = 0,
     KDA_ERR_NULL_ARG = 1,    /* a required pointer is NULL                          */
     KDA_ERR_BAD_SHAPE = 2,   /* head_dim != 128, H outside [1, 65535], B/T/N out of
-                                range                                              */
+                                range, or a launch of the chosen path would exceed
+                                the device's grid limits (2^32 work-items along x;
+                                e.g. the token-by-token path from 2^22 (sequence,
+                                head) pairs, the single pass from about 6.1 M)     */
     KDA_ERR_BAD_DTYPE = 3,   /* unknown dtype code                                  */
     KDA_ERR_BAD_SEQLENS = 4, /* cu_seqlens given with batch != 1, or N < 1           */
     KDA_ERR_BAD_ARG = 5,     /* lower_bound / scale out of range or non-finite,
@@ -111,12 +116,16 @@ enum {
      * chunk's fp32 update, as a kernel that keeps the on-chip state in bf16
      * between updates does (FlashKDA deep-dive, section 3), instead of
      * carrying it in fp32. For measuring that choice; implies the two-kernel
-     * path and is not valid with fp32 compute or another path flag. */
+     * path and is not valid with fp32 compute or another path flag. Its
+     * roundings accumulate when the state barely decays: with lower_bound
+     * above KDA_BF16_RESIDENT_MAX_LOWER_BOUND the call is rejected with
+     * KDA_ERR_BAD_ARG (at lower_bound 0 the final state measured 1.04 times
+     * the bf16 tolerance, at -0.2 0.36 times). */
     KDA_FLAG_BF16_RESIDENT_STATE = 32u,
     /* bf16-compute kda_fwd: run the segmented single pass, for few (sequence,
      * head) pairs over long sequences. Every sequence is cut into
      * max(2, 256 / (num_seqs * num_heads)) segments (from the average
-     * sequence; at least 16 chunks each, the first a quarter longer than the
+     * sequence; at least 16 chunks each, the first half again as long as the
      * others), so that about 256 (segment, head) workgroups, one per compute
      * unit, run at once. Each segment runs the single-pass kernel twice over the
      * same prepared chunks: from a zero state (the first segment: the initial

@@ -155,6 +155,8 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     if (!isfinite(lower_bound) || lower_bound < KDA_LOWER_BOUND_MIN || lower_bound > KDA_LOWER_BOUND_MAX)
         return KDA_ERR_BAD_ARG;
     if (!isfinite(desc->scale) || !(desc->scale > 0.f)) return KDA_ERR_BAD_ARG;
+    if ((desc->flags & KDA_FLAG_BF16_RESIDENT_STATE) && lower_bound > KDA_BF16_RESIDENT_MAX_LOWER_BOUND)
+        return KDA_ERR_BAD_ARG;
 
     const int64_t H = desc->num_heads, N = desc->num_seqs;
     const size_t esz = desc->io_dtype == KDA_DTYPE_BF16 ? 2 : 4;
@@ -205,6 +207,15 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     p.bf16_resident = (desc->flags & KDA_FLAG_BF16_RESIDENT_STATE) != 0;
     p.ws = static_cast<char *>(workspace);
     p.lay = lay;
+
+    // every launch of the path (both stages, whichever the call runs) within the
+    // grid limits, or nothing is enqueued
+    const bool fits = path == kSeg     ? kda::fits_fused(p, true) && kda::fits_seg_finish(p)
+                      : path == kFused ? kda::fits_fused(p, false)
+                      : path == kRecurrent ? kda::fits_recurrent(p)
+                      : p.f32_path         ? kda::fits_ref(p)
+                                           : kda::fits_split(p);
+    if (!fits) return KDA_ERR_BAD_SHAPE;
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (path == kSeg) {

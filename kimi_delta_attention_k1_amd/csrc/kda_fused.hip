@@ -21,8 +21,8 @@
 //               scales rk = 1/|k|, s rq = s/|q| of chunk c from the raw inputs (the
 //               diagonals of the raw rows' Gram matrices); stage B wave 9 -- its beta
 //   tick c+1  : stage B -- contracts the operands over the 128 channels; wave 9
-//               forms (A^qk)^T; the chunk's inverse wave forms R, R^T, M^2 and
-//               (I - M)(I + M^2)
+//               forms (A^qk)^T; the chunk's inverse wave forms R, R^T and the
+//               first levels of the block inversion of I + R
 //   tick c+2  : the inverse wave completes (A^kk Diag(beta))^T into slot c % 4
 //   tick c+3  : consumers run the recurrence step on slot c % 4.
 // Each stage-A wave streams its 32-channel slices of q, k, g_raw, v and
@@ -172,12 +172,19 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
         };
         bar_sync();  // start: the stage-A waves have waited for chunk 0 in their rings
         if (role == 0) {
-            // (A^kk)^T = (I + R^T)^-1 = (I-M)(I+M^2)(I+M^4)(I+M^8), M = R^T, with fp16
-            // operands and fp32 accumulation: the inverse's entries are bounded by 1 in
-            // magnitude (FlashKDA deep-dive, section 3), so fp16's range suffices. Each
-            // chunk c of this wave's parity takes two ticks: the first half at tick c+1,
-            // the second at tick c+2. One loop iteration covers both, so the values
-            // carried between them stay in the same registers.
+            // (A^kk)^T = (I + M)^-1 with M = R^T (strictly upper triangular), by block
+            // inversion over four levels of diagonal blocks (2, 4, 8, 16 rows): with X
+            // the inverse of the diagonal blocks of one level and C the part of M in the
+            // off-diagonal blocks of the next, X - X C X inverts the next level's blocks
+            // ([[A, B], [0, D]]^-1 = [[A^-1, -A^-1 B D^-1], [0, D^-1]]). Every value formed
+            // is a block of the inverse or a sum of eight bounded products, so the fp16
+            // operands (fp32 accumulation) lose nothing to cancellation. The doubling
+            // product (I - M)(I + M^2)(I + M^4)(I + M^8) takes as many products but forms
+            // M^8, whose entries reach the thousands when the keys of a chunk are
+            // correlated and barely decay; they then cancel, and fp16 operands leave
+            // errors of order one. Each chunk c of this wave's parity takes two ticks: the
+            // first half at tick c+1, the second at tick c+2. One loop iteration covers
+            // both, so the values carried between them stay in the same registers.
             int tau = 0;
 #pragma unroll 1
             for (; tau <= parity; ++tau) tick_sync();  // ticks before chunk parity's first half
@@ -192,6 +199,9 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 // rk = 1 / |k| per token, formed by the consumers in the previous tick
                 const float rkb = reinterpret_cast<const float *>(P + kPSC)[tok];
                 const f32x4 rka = *reinterpret_cast<const f32x4 *>(P + kPSC + 16 * g);
+                // D layout: element r is row a = 4g + r, column tok. R holds R (lower), RT
+                // holds R^T = M; blk(L, x) keeps the part of x in level L's off-diagonal
+                // blocks (same block of 2^L rows and columns, different half)
                 f32x4 R, RT;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -199,16 +209,32 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                     R[r] = (tok < a) ? beta_a[r] * rka[r] * rkb * Rs[r] : 0.f;
                     RT[r] = (a < tok) ? beta_b * rkb * rka[r] * RTs[r] : 0.f;
                 }
-                const f32x4 M2 = mm16_h(R, RT);
-                const f32x4 M2T = mm16_h(RT, R);
-                const f32x4 P1 = mm16_h(eye_plus(R, -1.f, g, tok), eye_plus(M2, 1.f, g, tok));
+                auto blk = [&](int L, f32x4 x) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int a = 4 * g + r;
+                        x[r] = ((a >> L) == (tok >> L) && (a >> (L - 1)) != (tok >> (L - 1))) ? x[r] : 0.f;
+                    }
+                    return x;
+                };
+                // level 1: Xi = I - C_1 (2 x 2 blocks), XiT = Xi^T = I - C_1^T
+                f32x4 Xi = eye_plus(blk(1, RT), -1.f, g, tok), XiT = eye_plus(blk(1, R), -1.f, g, tok);
+                // level 2: Y = C_2 Xi; Xi <- Xi - Xi Y, XiT <- XiT - Y^T XiT
+                {
+                    const f32x4 Y = mm16_h(blk(2, R), Xi);
+                    const f32x4 Z = mm16_h(XiT, Y), ZT = mm16_h(Y, XiT);
+                    Xi -= Z;
+                    XiT -= ZT;
+                }
+                const f32x4 Y3 = mm16_h(blk(3, R), Xi);  // level 3's Y (its update of Xi next tick)
                 tick_sync();
-                // second half: M^4, M^8, the product, the store
-                const f32x4 M4 = mm16_h(M2T, M2);
-                const f32x4 M4T = mm16_h(M2, M2T);
-                const f32x4 M8T = mm16_h(M4, M4T);
-                const f32x4 P2 = mm16_h(eye_plus(M4T, 1.f, g, tok), P1);
-                const f32x4 AT = mm16_h(eye_plus(M8T, 1.f, g, tok), P2);
+                // second half: level 3's update, level 4 (Xi only), the store
+                {
+                    const f32x4 Z = mm16_h(XiT, Y3), ZT = mm16_h(Y3, XiT);
+                    Xi -= Z;
+                    XiT -= ZT;
+                }
+                const f32x4 AT = Xi - mm16_h(XiT, mm16_h(blk(4, R), Xi));  // (A^kk)^T in D layout
                 f32x4 ABT;  // rk_b beta_a A^kk[b][a]: E' = Diag(rk) A^kk Diag(beta) Ebar
 #pragma unroll
                 for (int r = 0; r < 4; ++r) ABT[r] = rkb * beta_a[r] * AT[r];
@@ -588,8 +614,9 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 }
             }
         }
-        // consumers write no LDS and use every value they read before this point
-        bar_sync();
+        // waves 1 and 3 stored the chunk's per-token scales above, which stage B reads
+        // next tick: complete them before the barrier (every value read is used already)
+        tick_sync();
     }
     if constexpr (MODE == 0) {
         if (s1) {
@@ -647,6 +674,11 @@ static hipError_t launch_fused_any(const Problem &p, hipStream_t s)
     if (p.scalar_gate)
         return p.st_bf16 ? launch_fused_t<uint16_t, true, SEG>(p, s) : launch_fused_t<float, true, SEG>(p, s);
     return p.st_bf16 ? launch_fused_t<uint16_t, false, SEG>(p, s) : launch_fused_t<float, false, SEG>(p, s);
+}
+
+bool fits_fused(const Problem &p, bool seg)
+{
+    return seg ? grid_fits(p.lay.seg_max * p.H, 1, kFThreadsSeg) : grid_fits(p.N * p.H, 1, kFThreads);
 }
 
 hipError_t launch_fused(const Problem &p, hipStream_t s) { return launch_fused_any<false>(p, s); }

@@ -161,6 +161,19 @@ struct Problem {
     WsLayout lay;
 };
 
+// Launch extents: a launch keeps its work-items along x below 2^32 and its grid's y
+// extent within 65535. fits_* check every launch of a path on the host, with the
+// same grid arithmetic as the launches, before anything is enqueued.
+inline bool grid_fits(int64_t gx, int64_t gy, int64_t threads)
+{
+    return gx * threads < ((int64_t)1 << 32) && gy <= 65535;
+}
+bool fits_split(const Problem &p);       // k1_mfma, then k2_mfma or k2_look
+bool fits_ref(const Problem &p);         // k1_ref, k2_ref (and the chunk map)
+bool fits_fused(const Problem &p, bool seg);
+bool fits_recurrent(const Problem &p);
+bool fits_seg_finish(const Problem &p);  // kseg_scan, kseg_correct
+
 hipError_t launch_chunk_map(const Problem &p, hipStream_t s);   // K0
 hipError_t launch_prep_ref(const Problem &p, hipStream_t s);    // fp32 K1
 hipError_t launch_recur_ref(const Problem &p, hipStream_t s);   // fp32 K2

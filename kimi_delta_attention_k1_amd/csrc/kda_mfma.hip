@@ -833,12 +833,23 @@ __global__ __launch_bounds__(KLShape<CONS>::threads) void k2_look(
     out_step(nch - 1);
 }
 
+// chunk kernel: waves (one per (chunk, head) unit) per workgroup, a divisor of H
+static int k1_waves(int H) { return (H % 4 == 0) ? 4 : (H % 2 == 0 ? 2 : 1); }
+
+// recurrence workgroups: 8 / CONS per (sequence, head) pair, the pair count padded
+// to a multiple of 8 when a pair takes several
+template <int CONS> static int64_t k2_grid(int64_t pairs)
+{
+    constexpr int groups = 8 / CONS;
+    return groups == 1 ? pairs : (pairs + 7) / 8 * 8 * groups;
+}
+
 hipError_t launch_prep_mfma(const Problem &p, hipStream_t s)
 {
     if (p.n_c_max == 0) return hipSuccess;
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
-    const int wpb = (p.H % 4 == 0) ? 4 : (p.H % 2 == 0 ? 2 : 1);  // waves per block divide H
+    const int wpb = k1_waves(p.H);
     const bool look = use_lookahead(p.N, p.H, false, p.bf16_resident);
     auto kern = p.scalar_gate ? (look ? k1_mfma<true, true> : k1_mfma<true, false>)
                               : (look ? k1_mfma<false, true> : k1_mfma<false, false>);
@@ -854,8 +865,7 @@ static hipError_t launch_k2(const Problem &p, hipStream_t s)
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
     const int pairs = (int)(p.N * p.H);
-    constexpr int groups = 8 / CONS;
-    const unsigned grid = groups == 1 ? (unsigned)pairs : (unsigned)((pairs + 7) / 8 * 8 * groups);
+    const unsigned grid = (unsigned)k2_grid<CONS>(pairs);
     hipLaunchKernelGGL((k2_mfma<TSt, CONS, RS>), dim3(grid), dim3(K2Shape<CONS>::threads), 0, s, (const uint16_t *)p.v,
                        (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H, pairs, p.n_c_max,
                        (const char *)(p.ws + p.lay.units));
@@ -870,8 +880,7 @@ static hipError_t launch_look(const Problem &p, hipStream_t s)
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
     const int pairs = (int)(p.N * p.H);
-    constexpr int groups = 8 / CONS;
-    const unsigned grid = (unsigned)((pairs + 7) / 8 * 8 * groups);
+    const unsigned grid = (unsigned)((pairs + 7) / 8 * 8 * (8 / CONS));
     hipLaunchKernelGGL((k2_look<TSt, CONS>), dim3(grid), dim3(KLShape<CONS>::threads), 0, s, (const uint16_t *)p.v,
                        (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H, pairs, p.n_c_max,
                        (const char *)(p.ws + p.lay.units), (const char *)(p.ws + p.lay.ket));
@@ -889,6 +898,19 @@ static hipError_t launch_recur_mfma_t(const Problem &p, hipStream_t s)
     if (pairs >= 96) return launch_k2<TSt, 4, RS>(p, s);
     if (pairs >= 48) return launch_k2<TSt, 2, RS>(p, s);
     return launch_k2<TSt, 1, RS>(p, s);
+}
+
+bool fits_split(const Problem &p)
+{
+    const int wpb = k1_waves(p.H);
+    if (!grid_fits(p.n_c_max, p.H / wpb, 64 * wpb)) return false;
+    const int64_t pairs = p.N * p.H, padded = (pairs + 7) / 8 * 8;
+    if (!p.bf16_resident && use_lookahead(p.N, p.H, false, false))
+        return pairs >= 48 ? grid_fits(padded * 4, 1, KLShape<2>::threads) : grid_fits(padded * 8, 1, KLShape<1>::threads);
+    if (pairs >= 192) return grid_fits(k2_grid<8>(pairs), 1, K2Shape<8>::threads);
+    if (pairs >= 96) return grid_fits(k2_grid<4>(pairs), 1, K2Shape<4>::threads);
+    if (pairs >= 48) return grid_fits(k2_grid<2>(pairs), 1, K2Shape<2>::threads);
+    return grid_fits(k2_grid<1>(pairs), 1, K2Shape<1>::threads);
 }
 
 hipError_t launch_recur_mfma(const Problem &p, hipStream_t s)

@@ -212,6 +212,8 @@ static hipError_t launch_recurrent_t(const Problem &p, hipStream_t st)
     return hipGetLastError();
 }
 
+bool fits_recurrent(const Problem &p) { return grid_fits(p.N * p.H * (kD / kRRows), 1, kRThreads); }
+
 hipError_t launch_recurrent(const Problem &p, hipStream_t st)
 {
     if (p.io_bf16)

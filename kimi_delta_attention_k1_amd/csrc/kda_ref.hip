@@ -366,6 +366,8 @@ static hipError_t launch_recur_ref_t(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
+bool fits_ref(const Problem &p) { return grid_fits(p.n_c_max, p.H, 256) && grid_fits(p.N, p.H, 128); }
+
 hipError_t launch_prep_ref(const Problem &p, hipStream_t s)
 {
     return p.io_bf16 ? launch_prep_ref_t<uint16_t>(p, s) : launch_prep_ref_t<float>(p, s);

@@ -259,6 +259,20 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
     }
 }
 
+// token blocks of a segment spread over enough workgroups to fill the GPU about twice
+static int64_t corr_blocks(const Problem &p)
+{
+    const int64_t per_seg = (p.lay.seg_len * kC + kCorrTok - 1) / kCorrTok;
+    const int64_t want = (2 * kSegTargetGroups + p.lay.seg_max * p.H - 1) / (p.lay.seg_max * p.H);
+    return want < per_seg ? want : per_seg;
+}
+
+bool fits_seg_finish(const Problem &p)
+{
+    return grid_fits(p.N * p.H, kD / kScanRows, 64 * kScanWaves) &&
+           grid_fits(p.lay.seg_max * p.H, corr_blocks(p), 64 * kCorrWaves);
+}
+
 template <typename TSt>
 static hipError_t launch_seg_finish_t(const Problem &p, hipStream_t s)
 {
@@ -270,10 +284,7 @@ static hipError_t launch_seg_finish_t(const Problem &p, hipStream_t s)
     hipLaunchKernelGGL(kseg_scan<TSt>, dim3((unsigned)(p.N * p.H), kD / kScanRows), dim3(64 * kScanWaves), 0, s,
                        (const TSt *)p.s0, (TSt *)p.s1, seg, p.H, sfin, phi, sin);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    // token blocks of a segment spread over enough workgroups to fill the GPU about twice
-    const int64_t per_seg = (p.lay.seg_len * kC + kCorrTok - 1) / kCorrTok;
-    const int64_t want = (2 * kSegTargetGroups + p.lay.seg_max * p.H - 1) / (p.lay.seg_max * p.H);
-    const int64_t blocks = want < per_seg ? want : per_seg;
+    const int64_t blocks = corr_blocks(p);
     hipLaunchKernelGGL(kseg_correct, dim3((unsigned)(p.lay.seg_max * p.H), (unsigned)blocks), dim3(64 * kCorrWaves),
                        0, s, (uint16_t *)p.out, (const uint16_t *)(p.ws + p.lay.ybuf), (const float *)sin, tok, seg,
                        (int)p.N, p.H, (int)p.lay.seg_len, (int)p.lay.seg_first);

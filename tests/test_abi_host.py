@@ -250,3 +250,26 @@ def test_segmented_stage_entry_points_reject_other_paths(lib, desc_kw):
         rc = fn(a, a, a, a, a, None, None, a, None, ctypes.c_float(-5.0), ctypes.byref(desc), a,
                 ctypes.c_size_t(1 << 30), None)
         assert rc == BAD_ARG, kda.status_str(rc)
+
+
+def test_bf16_resident_state_needs_a_decaying_gate(lib):
+    """The bf16-resident recurrence accumulates its roundings when the state barely
+    decays: lower_bound above -0.2 is rejected; at -0.2 validation goes on (here to the
+    missing workspace)."""
+    desc = _desc(flags=kda.FLAG_BF16_RESIDENT_STATE)
+    assert _call(lib, desc, lb=0.0) == BAD_ARG
+    assert _call(lib, desc, lb=-0.19) == BAD_ARG
+    assert _call(lib, desc, lb=-0.2, drop=("ws",)) == WORKSPACE
+    assert _call(lib, _desc(flags=kda.FLAG_SPLIT), lb=0.0, drop=("ws",)) == WORKSPACE  # fp32 state: any bound
+
+
+@pytest.mark.parametrize("flags,N,H", [
+    (kda.FLAG_RECURRENT, 65536, 64),  # 2^22 pairs x 8 workgroups of 128 threads = 2^32 work-items
+    (kda.FLAG_FUSED, 95327, 64),      # 6,100,928 pairs x 704 threads >= 2^32
+])
+def test_grid_limits_rejected_before_launch(lib, flags, N, H):
+    """A launch whose work-items along x reach 2^32 is refused with BAD_SHAPE before
+    anything is enqueued (batch mode, one token or one chunk per sequence)."""
+    T = 1 if flags == kda.FLAG_RECURRENT else 16
+    desc = _desc(batch=N, seqlen=T, num_seqs=N, num_heads=H, flags=flags)
+    assert _call(lib, desc) == BAD_SHAPE

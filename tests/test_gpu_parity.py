@@ -3,8 +3,8 @@
 Tolerances (global max over the compared tensor):
   bf16 I/O : max|x_gpu - x_ref| <= 1e-2 max|x_ref| + 1e-3, for o and the final state
   fp32 path: max|x_gpu - x_ref| <= 1e-5 max|x_ref|
-Full-size workloads are compared on sampled (sequence, head) pairs, which the
-oracle computes whole; everything else is compared on every pair.
+Every case, the full-size workloads on the automatic path included, is
+compared with the oracle on every (sequence, head) pair.
 """
 import numpy as np
 import pytest
@@ -54,36 +54,32 @@ def test_c2_fp32_compute_flag(gpu):
     assert worst < 1e-4
 
 
-def test_c3_full_size_sampled(gpu):
-    _banner("c3 packed 8 x 8192, H=32 (sampled pairs)")
+def _all_pairs(w):
+    return [(n, h) for n in range(w.N) for h in range(w.H)]
+
+
+def test_c3_all_pairs(gpu):
+    _banner("c3 packed 8 x 8192, H=32, automatic path (single pass), all 256 pairs")
     w = workloads.c3()
-    pairs = [(0, 0), (3, 17), (7, 31), (5, 8)]
-    ref = run_oracle(w, pairs=pairs)
     o, s = run_gpu(w, gpu)
     assert torch.isfinite(o).all() and torch.isfinite(s).all()
-    compare(w, o, s, ref, bf16_tol, "c3 bf16 sampled")
+    compare(w, o, s, run_oracle(w, pairs=_all_pairs(w)), bf16_tol, "c3 bf16 all pairs")
 
 
-def test_c4_full_size_sampled(gpu):
-    _banner("c4 long context T=131072, H=32 (sampled heads)")
+def test_c4_all_heads(gpu):
+    _banner("c4 long context T=131072, H=32, automatic path (segmented), all 32 heads")
     w = workloads.c4()
-    ref = run_oracle(w, pairs=[(0, 5), (0, 30)])
     o, s = run_gpu(w, gpu)
     assert torch.isfinite(o).all() and torch.isfinite(s).all()
-    compare(w, o, s, ref, bf16_tol, "c4 bf16 sampled")
+    compare(w, o, s, run_oracle(w, pairs=_all_pairs(w)), bf16_tol, "c4 bf16 all heads")
 
 
-def test_c5_full_size_sampled(gpu):
-    _banner("c5 ragged 64 sequences, H=32 (sampled pairs incl. shortest/longest)")
+def test_c5_all_pairs(gpu):
+    _banner("c5 ragged 64 sequences, H=32, automatic path (single pass), all 2048 pairs")
     w = workloads.c5()
-    lens = w.seq_lens
-    nmin, nmax = int(np.argmin(lens)), int(np.argmax(lens))
-    odd = next(i for i, L in enumerate(lens) if L % 16 != 0)
-    pairs = [(nmin, 0), (nmax, 31), (odd, 13), (63, 7)]
-    ref = run_oracle(w, pairs=pairs)
     o, s = run_gpu(w, gpu)
     assert torch.isfinite(o).all() and torch.isfinite(s).all()
-    compare(w, o, s, ref, bf16_tol, "c5 bf16 sampled")
+    compare(w, o, s, run_oracle(w, pairs=_all_pairs(w)), bf16_tol, "c5 bf16 all pairs")
 
 
 # ------------------------------------------------------------------ edge cases (all pairs)

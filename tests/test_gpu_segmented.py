@@ -50,7 +50,7 @@ def test_c4_long_context_sampled_and_against_split(gpu):
         assert err <= tol
 
 
-@pytest.mark.parametrize("lb", [-5.0, -1.0, 0.0])
+@pytest.mark.parametrize("lb", [-10.0, -5.0, -1.0, 0.0])
 def test_ragged_segments_and_empty_sequences(gpu, lb):
     _banner(f"ragged lengths around the 256-token segment, empty sequences, lb={lb}")
     lens = [0, 1, 255, 256, 257, 700, 1000, 33, 0, 513]
@@ -172,9 +172,12 @@ def test_stage_entry_points_compose_to_kda_fwd(gpu):
 ])
 def test_automatic_rule_boundaries(gpu, N, H, T, expect):
     """Without a path flag, kda_fwd runs exactly the path the rule names (bitwise
-    equal to the forced call) on either side of each threshold."""
+    equal to the forced call) on either side of each threshold, and meets the oracle
+    on the first, a middle and the last (sequence, head) pair."""
     _banner(f"automatic rule: {N} x {T} tokens, H={H} ({N * H} pairs) -> {expect}")
     w = workloads.make([T] * N, H, seed=17, packed=False)
     oa, sa = run_gpu(w, gpu)
     oe, se = run_gpu(w, gpu, path=expect)
     assert torch.equal(oa, oe) and torch.equal(sa, se)
+    ref = run_oracle(w, pairs=[(0, 0), (N // 2, H // 2), (N - 1, H - 1)])
+    compare(w, oa, sa, ref, bf16_tol, f"automatic rule {N * H} pairs ({expect})")
