@@ -92,6 +92,11 @@ def run_oracle(w, pairs=None, threads=0):
     return res
 
 
+# (what, pairs compared, worst output err/tol, worst state err/tol) of every comparison in
+# this session, printed at the end of the run (tests/conftest.py)
+RESULTS = []
+
+
 def compare(w, o_gpu, s_gpu, ref, tol_fn, what=""):
     """Check every pair in ref; returns (worst o ratio, worst state ratio) of err/tol."""
     offs = w.offsets()
@@ -110,6 +115,7 @@ def compare(w, o_gpu, s_gpu, ref, tol_fn, what=""):
             worst_s = max(worst_s, es / tol_s if tol_s > 0 else es)
     print(f"{what}: err/tol o {worst_o:.3f} state {worst_s:.3f} (tol o {tol_o:.3e}, state {tol_s:.3e})",
           flush=True)
+    RESULTS.append((what, len(ref), worst_o, worst_s if sg is not None else None))
     assert worst_o <= 1.0, f"{what}: output error {worst_o:.3f} x tolerance"
     assert worst_s <= 1.0, f"{what}: state error {worst_s:.3f} x tolerance"
     return worst_o, worst_s
