@@ -71,7 +71,10 @@ typedef enum kda_status {
                                 an input                                           */
     KDA_ERR_WORKSPACE = 6,   /* workspace NULL, too small, or not 128-B aligned     */
     KDA_ERR_MISALIGNED = 7,  /* a tensor base address is not 16-B aligned           */
-    KDA_ERR_HIP = 8          /* a kernel launch failed (HIP runtime error)          */
+    KDA_ERR_HIP = 8,         /* a kernel launch failed (HIP runtime error)          */
+    KDA_ERR_TOO_LARGE = 9    /* kda_fwd_noalloc: the call needs more scratch than
+                                the library's static buffer holds (more than
+                                KDA_NOALLOC_MAX_SEQS sequences)                    */
 } kda_status_t;
 
 /* Element types. */
@@ -302,6 +305,38 @@ kda_status_t kda_fwd_seg_finish(const void *q, const void *k, const void *v,
                                 const kda_desc_t *desc,
                                 void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/*
+ * kda_fwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). It takes kda_fwd's other arguments with the same meaning
+ * and checks, and runs only the paths whose scratch is small: the single-pass
+ * kernel (KDA_FLAG_FUSED, and without a path flag for bf16 compute) or the
+ * token-by-token kernel (KDA_FLAG_RECURRENT, and without a path flag for
+ * sequences averaging at most KDA_RECURRENT_MAX_AVG_TOKENS tokens or for fp32
+ * compute). Their scratch -- the chunk map and the order of the sequences --
+ * lives in a static device buffer of KDA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends; its address is looked
+ * up once per device, on the first call with that device current. The call
+ * allocates and frees nothing.
+ *  - KDA_FLAG_SPLIT, KDA_FLAG_SEGMENTED and KDA_FLAG_BF16_RESIDENT_STATE give
+ *    KDA_ERR_BAD_ARG; more than KDA_NOALLOC_MAX_SEQS sequences give
+ *    KDA_ERR_TOO_LARGE; both before anything is enqueued.
+ *  - Every call on one GPU uses that GPU's one buffer: calls that overlap in
+ *    time on one GPU (different streams, or host threads) race and must be
+ *    serialised by the caller. Nothing in the buffer needs clearing between
+ *    calls: each call rewrites what it reads.
+ */
+#define KDA_NOALLOC_MAX_SEQS 65536
+#define KDA_NOALLOC_SCRATCH_BYTES (800u * 1024u)
+kda_status_t kda_fwd_noalloc(const void *q, const void *k, const void *v,
+                             const void *g_raw, const void *beta_raw,
+                             const int32_t *cu_seqlens,
+                             const void *initial_state,
+                             void *out, void *final_state,
+                             float lower_bound,
+                             const kda_desc_t *desc,
+                             void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_str(kda_status_t status);

@@ -31,7 +31,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "prepare_call", "Call", "workspace_size", "KdaError", "load_library", "library_path", "seqlens_flag",
+__all__ = ["fwd", "fwd_noalloc", "prepare_call", "Call", "workspace_size", "KdaError", "load_library", "library_path", "seqlens_flag",
            "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE", "FLAG_SPLIT", "FLAG_FUSED", "FLAG_RECURRENT", "FLAG_SCALAR_GATE",
            "FLAG_BF16_RESIDENT_STATE", "FLAG_SEGMENTED",
            "FUSED_MIN_PAIRS", "SEGMENTED_MAX_PAIRS", "SEGMENTED_MIN_AVG_CHUNKS", "RECURRENT_MAX_AVG_TOKENS"]
@@ -93,6 +93,8 @@ def load_library():
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.POINTER(KdaDesc),
                        vp, ctypes.c_size_t, vp]
+    lib.kda_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.POINTER(KdaDesc), vp]
     lib.kda_status_str.restype = ctypes.c_char_p
     lib.kda_status_str.argtypes = [ctypes.c_int]
     lib.kda_version.restype = ctypes.c_int
@@ -169,6 +171,13 @@ class Call:
     def seg_finish(self):
         self._go(self._lib.kda_fwd_seg_finish)
 
+    def run_noalloc(self):
+        """The same call through kda_fwd_noalloc (the library's static scratch
+        instead of the workspace)."""
+        st = self._lib.kda_fwd_noalloc(*self._args[:11], self._args[13])
+        if st != 0:
+            raise KdaError(st, self._lib.kda_status_str(st).decode())
+
 
 def fwd(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | None = None,
         initial_state=None, output_final_state: bool = True, cu_seqlens=None, out=None, final_state=None,
@@ -190,12 +199,29 @@ def fwd(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | N
     return c.out, c.final_state
 
 
+def fwd_noalloc(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | None = None,
+                initial_state=None, output_final_state: bool = True, cu_seqlens=None, out=None, final_state=None,
+                fp32_compute: bool = False, path: str = "auto", stream=None):
+    """KDA forward through kda_fwd_noalloc: no workspace; the library's static
+    scratch on the device serves as one. `path` is "auto", "fused" or
+    "recurrent" (the paths with a small workspace). out and final_state are
+    allocated here when not given; pass them to keep the call free of
+    allocations."""
+    c = prepare_call(q, k, v, g_raw, beta_raw, lower_bound=lower_bound, scale=scale, initial_state=initial_state,
+                     output_final_state=output_final_state, cu_seqlens=cu_seqlens, out=out,
+                     final_state=final_state, fp32_compute=fp32_compute, path=path, stream=stream,
+                     no_workspace=True)
+    c.run_noalloc()
+    return c.out, c.final_state
+
+
 def prepare_call(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: float | None = None,
                  initial_state=None, output_final_state: bool = True, cu_seqlens=None, out=None,
                  final_state=None, workspace=None, fp32_compute: bool = False, path: str = "auto",
-                 bf16_resident_state: bool = False, stream=None) -> Call:
+                 bf16_resident_state: bool = False, stream=None, no_workspace: bool = False) -> Call:
     """Check and marshal fwd's arguments once (allocating out, final_state and
-    the workspace when not given) without launching anything."""
+    the workspace when not given) without launching anything. no_workspace: for
+    kda_fwd_noalloc, which takes none (the call then passes NULL and 0)."""
     import torch
     lib = load_library()
     tensors = (q, k, v, g_raw, beta_raw)
@@ -247,8 +273,11 @@ def prepare_call(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: 
     flags = _flags(fp32_compute, path) | (FLAG_SCALAR_GATE if scalar_gate else 0) | \
         (FLAG_BF16_RESIDENT_STATE if bf16_resident_state else 0)
     desc = make_desc(B, seqlen, N, H, io, st_code, scale, flags, head_dim=D)
-    need = int(lib.kda_fwd_workspace_size(ctypes.byref(desc)))
-    if workspace is None:
+    need = 0 if no_workspace else int(lib.kda_fwd_workspace_size(ctypes.byref(desc)))
+    if no_workspace:
+        if workspace is not None:
+            raise ValueError("no_workspace excludes a workspace")
+    elif workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     elif workspace.numel() < need:
         raise ValueError(f"workspace too small: {workspace.numel()} < {need} bytes")
@@ -256,7 +285,7 @@ def prepare_call(q, k, v, g_raw, beta_raw, *, lower_bound: float = -5.0, scale: 
         stream = torch.cuda.current_stream(q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(cu_seqlens), _ptr(initial_state),
             _ptr(out), _ptr(final_state), ctypes.c_float(lower_bound), ctypes.byref(desc), _ptr(workspace),
-            ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream.cuda_stream))
+            ctypes.c_size_t(0 if workspace is None else workspace.numel()), ctypes.c_void_p(stream.cuda_stream))
     keep = (q, k, v, g_raw, beta_raw, cu_seqlens, initial_state, out, final_state, workspace, desc, stream)
     return Call(lib, args, keep, out, final_state)
 

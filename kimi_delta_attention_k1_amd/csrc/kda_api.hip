@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "kda_internal.h"
 
@@ -260,6 +262,63 @@ extern "C" kda_status_t kda_fwd_recur(KDA_ARGS) { return run(KDA_PASS, kRecur); 
 extern "C" kda_status_t kda_fwd_seg_pass(KDA_ARGS) { return run(KDA_PASS, kSegStage | kPrepare); }
 extern "C" kda_status_t kda_fwd_seg_finish(KDA_ARGS) { return run(KDA_PASS, kSegStage | kRecur); }
 
+// Scratch of kda_fwd_noalloc: the single pass's and the token-by-token path's
+// workspace (chunk map and sequence order), one copy per GPU. Host code never
+// passes this name to a kernel (on the host it stands for no device address);
+// it uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+
+// address of the current device's scratch, looked up on the first call with that
+// device current and kept
+hipError_t scratch_for_current_device(void **ptr)
+{
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" kda_status_t kda_fwd_noalloc(const void *q, const void *k, const void *v, const void *g_raw,
+                                        const void *beta_raw, const int32_t *cu_seqlens,
+                                        const void *initial_state, void *out, void *final_state,
+                                        float lower_bound, const kda_desc_t *desc, void *stream)
+{
+    Shape s;
+    const kda_status_t st = check_desc(desc, cu_seqlens != nullptr, &s);
+    if (st != KDA_OK) return st;
+    if (desc->flags & (KDA_FLAG_SPLIT | KDA_FLAG_SEGMENTED | KDA_FLAG_BF16_RESIDENT_STATE)) return KDA_ERR_BAD_ARG;
+    // the paths with a small workspace: token by token where kda_fwd would take it or
+    // for fp32 compute, the single pass otherwise
+    kda_desc_t d = *desc;
+    if (!(d.flags & (KDA_FLAG_FUSED | KDA_FLAG_RECURRENT)))
+        d.flags |= (s.path == kRecurrent || s.f32_path) ? KDA_FLAG_RECURRENT : KDA_FLAG_FUSED;
+    if (d.num_seqs > KDA_NOALLOC_MAX_SEQS) return KDA_ERR_TOO_LARGE;
+    const size_t need = (d.flags & KDA_FLAG_FUSED) ? kda::ws_layout_fused(d.num_seqs, d.num_heads).total
+                                                   : kda::ws_layout(d.num_seqs, d.num_heads, 0, s.f32_path, false).total;
+    if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_TOO_LARGE;
+    void *ws = nullptr;
+    if (scratch_for_current_device(&ws) != hipSuccess) return KDA_ERR_HIP;
+    return run(q, k, v, g_raw, beta_raw, cu_seqlens, initial_state, out, final_state, lower_bound, &d, ws,
+               KDA_NOALLOC_SCRATCH_BYTES, stream, kPrepare | kRecur);
+}
+
 extern "C" const char *kda_status_str(kda_status_t status)
 {
     switch (status) {
@@ -272,6 +331,7 @@ extern "C" const char *kda_status_str(kda_status_t status)
     case KDA_ERR_WORKSPACE: return "workspace missing, too small or not 128-byte aligned";
     case KDA_ERR_MISALIGNED: return "a tensor base address is not 16-byte aligned";
     case KDA_ERR_HIP: return "HIP kernel launch failed";
+    case KDA_ERR_TOO_LARGE: return "too many sequences for the static scratch of kda_fwd_noalloc";
     }
     return "unknown status";
 }

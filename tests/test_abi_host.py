@@ -14,7 +14,7 @@ import kimi_delta_attention_k1_amd as kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_SEQLENS, BAD_ARG, WORKSPACE, MISALIGNED, HIP = range(9)
+OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_SEQLENS, BAD_ARG, WORKSPACE, MISALIGNED, HIP, TOO_LARGE = range(10)
 
 
 @pytest.fixture(scope="module")
@@ -40,7 +40,7 @@ def test_header_symbols_are_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.kda_version() >= 200
-    for code in range(9):
+    for code in range(10):
         assert kda.status_str(code) and kda.status_str(code) != "unknown status"
     assert kda.status_str(99) == "unknown status"
 
@@ -273,3 +273,22 @@ def test_grid_limits_rejected_before_launch(lib, flags, N, H):
     T = 1 if flags == kda.FLAG_RECURRENT else 16
     desc = _desc(batch=N, seqlen=T, num_seqs=N, num_heads=H, flags=flags)
     assert _call(lib, desc) == BAD_SHAPE
+
+
+def _noalloc(lib, desc, N, H, T_tot):
+    f = Fake(dict(q=T_tot * H * 256, k=T_tot * H * 256, v=T_tot * H * 256, g=T_tot * H * 256, b=T_tot * H * 2,
+                  cu=4 * (N + 1), out=T_tot * H * 256, s1=N * H * 65536))
+    a = {k_: ctypes.c_void_p(v_) for k_, v_ in f.addr.items()}
+    return lib.kda_fwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["b"], a["cu"], None, a["out"], a["s1"],
+                               ctypes.c_float(-5.0), ctypes.byref(desc), None)
+
+
+def test_noalloc_rejects_before_any_gpu_call(lib):
+    """Too many sequences for the static scratch, and the paths with a large workspace,
+    are refused before the library looks up its scratch or enqueues anything."""
+    N = 65537
+    assert _noalloc(lib, _desc(seqlen=16 * N, num_seqs=N), N, 2, 16 * N) == TOO_LARGE
+    for flags in (kda.FLAG_SPLIT, kda.FLAG_SEGMENTED, kda.FLAG_BF16_RESIDENT_STATE):
+        assert _noalloc(lib, _desc(seqlen=64, num_seqs=2, flags=flags), 2, 2, 64) == BAD_ARG
+    assert lib.kda_fwd_noalloc(None, None, None, None, None, None, None, None, None, ctypes.c_float(-5.0), None,
+                               None) == NULL_ARG
