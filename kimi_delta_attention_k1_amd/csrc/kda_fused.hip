@@ -8,32 +8,32 @@
 // A^kk = (I + R)^-1, then E = A^kk Diag(beta)(V - K_b S^T), O = Q_b S^T + A^qk E
 // and S^T <- Diag(gamma) S^T + K_end^T E (6.4).
 //
-// Workgroup: 4 consumer waves (the recurrence; wave w owns value channels
-// [32w, 32w+32) as two 16-wide column tiles, so every operand read from LDS
-// serves two tiles), 4 stage-A waves (wave m owns key channels [32m, 32m+32))
-// and 3 stage-B waves: 8 and 10 (14 in the segmented form) invert the even and
-// the odd chunks, 9 forms A^qk and beta. Waves w, w+4, w+8 (and w+12) share a
-// SIMD, so the two inverse waves sit on different SIMDs. Time advances in ticks
+// Workgroup: 4 consumer waves (the recurrence; wave w owns value channels [32w,
+// 32w+32) as two 16-wide column tiles, so every operand read from LDS serves two
+// tiles), 4 stage-A waves (wave m owns key channels [32m, 32m+32)) and 3 stage-B waves:
+// 8 and 10 (14 in the segmented form, after its 4 transfer-run waves) invert the even
+// and the odd chunks, 9 ("role 1") forms A^qk and beta. Waves w, w+4, w+8 (and w+12)
+// share a SIMD, so the two inverse waves sit on different SIMDs. Time advances in ticks
 // separated by one workgroup barrier; chunk c is handled at
-//   tick c    : stage A -- gate, prefix sums, decays; the wave's 32-channel
-//               slices of the in-chunk operands, and K_b / Q_b / K_end / gamma / v
-//               into prepared slot c % 4; consumer waves 3 and 1 -- the per-token
-//               scales rk = 1/|k|, s rq = s/|q| of chunk c from the raw inputs (the
-//               diagonals of the raw rows' Gram matrices); stage B wave 9 -- its beta
-//   tick c+1  : stage B -- contracts the operands over the 128 channels; wave 9
+//   tick c    : stage A -- gate, prefix sums, decays; the wave's channel slices of
+//               K_b / Q_b / K_inv / K_end (hi, lo), gamma and v into prepared slot
+//               c % 4; consumer waves 3 and 1 -- the per-token scales rk = 1/|k| and
+//               s rq = s/|q| of chunk c from the raw inputs (the diagonals of the raw
+//               rows' Gram matrices); role 1 -- its beta
+//   tick c+1  : stage B -- contracts the operands over the 128 channels; role 1
 //               forms (A^qk)^T; the chunk's inverse wave forms R, R^T and the
 //               first levels of the block inversion of I + R
 //   tick c+2  : the inverse wave completes (A^kk Diag(beta))^T into slot c % 4
 //   tick c+3  : consumers run the recurrence step on slot c % 4.
-// Each stage-A wave streams its 32-channel slices of q, k, g_raw, v and
-// beta_raw into a kFIn-slot ring with global-to-LDS loads and waits on exact
-// counts of its own loads; a ring slot is refilled one tick after its chunk's
-// stage-A tick, since the consumers and stage B role 1 read it during that tick.
+// Each stage-A wave streams its channel slices of q, k, g_raw, v and beta_raw into a
+// kFIn-slot ring with global-to-LDS loads and waits on exact counts of its own loads;
+// a ring slot is refilled one tick after its chunk's stage-A tick, since the consumers
+// and stage B read it during that tick.
 //
-// L2 normalisation is deferred: stage A works on raw q, k; the consumers form
-// rk and s rq (the read scale s folded in) a tick ahead of stage B, which folds
-// them into R, (A^kk Diag(beta))^T and (A^qk)^T; the consumers scale K_b S^T by
-// rk and Q_b S^T by rq per row. The recurrence then runs on
+// L2 normalisation is deferred: stage A works on raw q, k; consumer waves 3 and 1 form
+// rk and s rq (the read scale s folded in) a tick ahead of stage B, which folds them into R,
+// (A^kk Diag(beta))^T and (A^qk)^T; the consumers scale K_b S^T by rk and Q_b S^T by
+// rq per row. The recurrence then runs on
 // E' = Diag(rk) E, which is exactly what the state update needs with the raw
 // K_end (K_end^T E = K_end_raw^T E'), and A^qk / Diag(rk) applied to E' gives
 // the same outputs.
@@ -43,41 +43,61 @@
 
 namespace kda {
 
-constexpr int kFCons = 4;                             // consumer waves (32 value channels each)
-constexpr int kFPrep = 4;                             // stage-A waves
-constexpr int kFSolve = 3;                            // stage-B waves: even- and odd-chunk inverse, A^qk
-constexpr int kFThreads = 64 * (kFCons + kFPrep + kFSolve);  // 704
-constexpr int kFThreadsSeg = kFThreads + 64 * kFCons;         // 960: + the transfer-run consumers
-constexpr int kFIn = 3;                               // input-ring slots per prep wave (two chunks in flight)
-constexpr int kFSlots = 4;                            // prepared-chunk slots (stage A steps through them unrolled)
-constexpr int kFDma = 5;                              // global-to-LDS loads per chunk per prep wave
-// a ring slot is refilled one tick after its chunk's stage-A tick (the consumers read the raw
-// q and k, stage B role 1 the beta_raw, of chunk c from the rings during tick c), so kFIn - 1 chunks are in
-// flight: waiting for chunk c + 1 at the end of tick c leaves two chunks' loads outstanding
-constexpr int kFPending = (kFIn - 2) * kFDma;         // loads allowed in flight when chunk c+1 must have landed
+constexpr int kFCons = 4;  // consumer waves (32 value channels each)
+constexpr int kFPrep = 4;  // stage-A waves (32 key channels each)
+constexpr int kAW = 32;    // key channels per stage-A wave
+constexpr int kNE = 8;     // key channels per stage-A lane
+// 4 consumer, 4 stage-A and 3 stage-B waves; the segmented form adds 4 transfer-run waves
+template <bool SEG> constexpr int f_threads() { return 64 * (kFCons + kFPrep + 3 + (SEG ? kFCons : 0)); }
+constexpr int kFIn = 3;     // input-ring slots per stage-A wave (two chunks in flight)
+constexpr int kFSlots = 4;  // prepared-chunk slots (stage A steps through them unrolled)
+constexpr int kFDma = 5;    // global-to-LDS loads per chunk per stage-A wave: q, k, g_raw, v, beta
+// a ring slot is refilled one tick after its chunk's stage-A tick (consumer waves 1 and 3
+// read the raw q and k, stage B role 1 the beta_raw, of chunk c from the rings during tick c),
+// so kFIn - 1 chunks are in flight: waiting for chunk c + 1 at the end of tick c leaves
+// (kFIn - 2) chunks' loads outstanding
+constexpr int kFPending = (kFIn - 2) * kFDma;
 static_assert(kFPending <= 63, "vmcnt holds at most 63 outstanding loads");
 
-// prepared slot
-constexpr int kPKB = 0, kPQB = 4096, kPKE = 8192, kPAB = 12288, kPAQ = 13312, kPGM = 14336;
-constexpr int kPSC = 14848;  // rk[16], s*rq[16]
-constexpr int kPV = 14976;   // v tile [16][128] bf16, rows kVRow bytes apart
-constexpr int kVRow = 272;   // 256 + 16: row r starts 4 r banks further, so row-wise
-                             // 16-byte writes and column-wise reads spread over the banks
-constexpr int kPBytes = kPV + kC * kVRow;
-// per-prep-wave input slot: q, k, g_raw, v as [16 rows][32 channels] bf16, then
-// beta_raw as one aligned dword per lane (the token's element in its low or high half);
-// a scalar g_raw takes the same dword form at the start of its block
-constexpr int kIQ = 0, kIK = 1024, kIG = 2048, kIV = 3072, kIB = 4096, kIBytes = 4352;
-// in-chunk operand buffer (two, alternating by chunk parity): per stage-A wave, its
-// 32-channel slices of K_r = k e^{G - Gref}, K_inv = k e^{Gref - G} and Q_r = q e^{G - Gref}
-// as bf16 16x16x32 operands (lane = token, 8 channels), which stage B contracts over
-// all 128 channels for R, R^T and A^qk
-constexpr int kXKR = 0, kXKI = 1024, kXQR = 2048, kXWave = 3072;
-constexpr int kXBeta = kFPrep * kXWave;
-constexpr int kXBytes = kXBeta + 64;
-constexpr int kFLds = kFSlots * kPBytes + kFPrep * kFIn * kIBytes + 2 * kXBytes;
-static_assert(kFLds <= 160 * 1024, "LDS budget of one gfx950 workgroup");
-static_assert(kPBytes % 128 == 0 && kIBytes % 64 == 0 && kXBytes % 64 == 0, "16-byte aligned LDS blocks");
+// prepared slot: the chunk's operands in the consumers' matrix-core lane order (1 KB
+// per 16 x 32 or 32 x 16 block, swizzled), which stage B also contracts:
+//   KB  K_b = k e^{G - r}   (16x16x32 A order, k step m = key channels [32m, 32m+32))
+//   QB  Q_b = q e^{G - r}   (same order)
+//   KE  K_end = k e^{G_last - G} as a bf16 hi/lo pair (about 16 bits), 2 KB per tile
+//       pair m: lane L's 32 bytes hold, for tiles 2m and 2m+1, four tokens' hi values
+//       then the same tokens' lo values (16x16x16 A order for each half, so one 16-byte
+//       read is a 16x16x32 operand [hi | lo]). The update K_end^T E' adds into the
+//       state every chunk, so a one-bf16 K_end would leave a 2^-9 relative error per
+//       chunk in state directions that later keys never overwrite: with correlated
+//       keys and gates that barely decay that grew past the bf16 bound
+//   AB  (Diag(rk) A^kk Diag(beta))^T, AQ (A^qk)^T as bf16 hi/lo pairs; GM gamma = e^{G_last}
+//   SC  rk[16], s*rq[16]
+//   KI  K_inv = k e^{r - G}  (KB's order)
+//   V   the v tile [16][128] bf16, rows kVRow bytes apart
+//   ER  e^{r} per key channel (token-7 reference only; the consumers scale their bf16
+//       state operand by it)
+// with r = 0 (decays from the chunk start, CSR) or r = G of the chunk's token 7.
+constexpr int kPKB = 0, kPQB = 4096, kPKE = 8192, kPAB = 16384, kPAQ = 17408, kPGM = 18432;
+constexpr int kPSC = 18944;
+constexpr int kPKI = 19072;
+constexpr int kPV = kPKI + 4096;
+constexpr int kVRow = 272;  // 256 + 16: row r starts 4 r banks further, so row-wise
+                            // 16-byte writes and column-wise reads spread over the banks
+constexpr int kPER = kPV + kC * kVRow;
+template <bool CSR> constexpr int slot_bytes() { return kPER + (CSR ? 0 : 512); }
+// per-stage-A-wave input slot: q, k, g_raw, v as [16 rows][32 channels] bf16, then
+// beta_raw as one aligned dword per token (lanes 0-15; the token's element in its low or
+// high half); a scalar g_raw takes the same dword form at the start of its block
+constexpr int kIQ = 0, kIK = 1024, kIG = 2048, kIV = 3072, kIB = 4096, kIBytes = 4160;
+constexpr int kXBeta = 0, kXBytes = 64;  // per-parity buffer: the chunk's beta, formed a tick ahead
+template <bool CSR> constexpr int lds_bytes()
+{
+    return kFSlots * slot_bytes<CSR>() + kFPrep * kFIn * kIBytes + 2 * kXBytes;
+}
+static_assert(lds_bytes<false>() <= 160 * 1024 && lds_bytes<true>() <= 160 * 1024, "LDS budget of one workgroup");
+static_assert(slot_bytes<false>() % 128 == 0 && slot_bytes<true>() % 128 == 0 && kIBytes % 64 == 0 &&
+                  kPKI % 16 == 0 && kPV % 16 == 0,
+              "16-byte aligned LDS blocks");
 
 // 16-byte slot of lane L in a 1 KB operand block: L with its low three bits XORed with
 // bits 3-5. The consumers' 16-byte reads still cover all banks in every group of eight
@@ -86,16 +106,6 @@ __device__ __forceinline__ int swz(int L) { return L ^ ((L >> 3) & 7); }
 
 // barrier that first completes this wave's own LDS traffic (not its global loads)
 __device__ __forceinline__ void tick_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// sum over the four lanes l with equal l % 16: two cross-row swaps (rows of 16 lanes),
-// no LDS round trip
-__device__ __forceinline__ float sum_rows4(float x)
-{
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 // SG: scalar gate, g_raw is [T][H] and its one value per token and head applies to
 // every key channel (Gated DeltaNet, Doubleword section 3)
@@ -115,8 +125,18 @@ __device__ __forceinline__ float sum_rows4(float x)
 // o_t = o0_t + S_in y_t; the scan and correction kernels (kda_seg.hip) finish it.
 // Segment 0 starts from the known initial state, so its waves 10-13 only keep
 // the barrier count.
-template <typename TSt, bool SG, bool SEG>
-__global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
+//
+// CSR: in-chunk decays referenced to the chunk start (lower_bound >= -5). Then
+// |G| <= 16 |lb| <= 80 in natural-log units, so e^G and e^-G, and the bf16 operands
+// k e^G, q e^G and k e^-G, stay inside fp32's and bf16's normal range (factors down
+// to about 1e-35 and up to 6e34): two exponentials and four products per element.
+// Otherwise (down to lower_bound -10) the operands are referenced to the chunk's token
+// 7, which keeps every factor within e^{8 |lb|}: K_b = k e^{G - Gref}, Q_b likewise, and
+// the consumers scale their bf16 copy of the state by e^{Gref} per key channel. Either
+// way K_b, Q_b and K_inv = k e^{r - G} are both the consumers' operands and stage B's
+// for R and A^qk.
+template <typename TSt, bool SG, bool SEG, bool CSR>
+__global__ __launch_bounds__(f_threads<SEG>()) void kf_fused(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const uint16_t *__restrict__ graw, const uint16_t *__restrict__ braw, const TSt *s0, TSt *s1,
     uint16_t *__restrict__ out, const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off, int H,
@@ -124,10 +144,12 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
     float *__restrict__ sfin,
     float *__restrict__ phi, uint16_t *__restrict__ ybuf, const int32_t *__restrict__ order)
 {
-    __shared__ __attribute__((aligned(1024))) char lds[kFLds];
+    constexpr int kPBytes = slot_bytes<CSR>();
+    constexpr int NP = kFPrep, AW = kAW, NE = kNE;
+    __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<CSR>()];
     char *const slots = lds;
     char *const inring = lds + kFSlots * kPBytes;
-    char *const parts = inring + kFPrep * kFIn * kIBytes;
+    char *const parts = inring + NP * kFIn * kIBytes;
 
     // the wave index is uniform over the wave: keep it scalar so role branches and
     // the address arithmetic built on it stay in scalar registers
@@ -150,24 +172,28 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
     const int te = tok_off[n + 1];
     const int ticks = nch > 0 ? nch + 3 : 0;
 
-    // stage-B waves: 8 (inverse of even chunks), 9 (A^qk and beta), and the inverse of odd
-    // chunks after the transfer-run waves in the segmented form, on the SIMD of waves 2 and 6
-    const int w_inv_odd = kFCons + kFPrep + 2 + (SEG ? kFCons : 0);
-    const bool stage_b = w == kFCons + kFPrep || w == kFCons + kFPrep + 1 || w == w_inv_odd;
+    // stage-B waves after the stage-A waves: the inverse of even chunks, role 1 (A^qk and
+    // beta), and the inverse of odd chunks (the last wave, after the transfer-run waves in
+    // the segmented form), on SIMDs 0, 1 and 2
+    constexpr int w_inv_odd = kFCons + NP + 2 + (SEG ? kFCons : 0);
+    const bool stage_b = w == kFCons + NP || w == kFCons + NP + 1 || w == w_inv_odd;
     if (stage_b) {
         // ================================================================ stage-B waves
         if (nch == 0) return;  // uniform over the workgroup: no barrier is entered
-        const int role = w == kFCons + kFPrep + 1 ? 1 : 0;
+        const int role = w == kFCons + NP + 1 ? 1 : 0;
         const int parity = w == w_inv_odd ? 1 : 0;  // inverse waves: chunks of this parity
         const int tok = lane & 15, g = lane >> 4;  // D layout: rows 4g+r, column tok
-        // A B^T over the 128 key channels: the four waves' 32-channel operand slices of
-        // chunk c, one chained 16x16x32 product each (fp32 accumulation)
-        auto contract = [&](const char *X, int offa, int offb) {
+        // A B^T over the 128 key channels of the slot's K_b, Q_b and K_inv blocks (32-channel
+        // slices in the consumers' lane order): one chained 16x16x32 product per slice (fp32
+        // accumulation). Both operands carry the same channel permutation, so the sum runs
+        // over the key channels as such.
+        const int ls = swz(lane);
+        auto contract = [&](const char *P, int offa, int offb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int mm = 0; mm < kFPrep; ++mm)
-                acc = mma32(reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offa)[lane],
-                            reinterpret_cast<const bf16x8 *>(X + mm * kXWave + offb)[lane], acc);
+            for (int mm = 0; mm < 4; ++mm)
+                acc = mma32(reinterpret_cast<const bf16x8 *>(P + mm * 1024 + offa)[ls],
+                            reinterpret_cast<const bf16x8 *>(P + mm * 1024 + offb)[ls], acc);
             return acc;
         };
         bar_sync();  // start: the stage-A waves have waited for chunk 0 in their rings
@@ -192,11 +218,11 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
             for (int c = parity; c < nch; c += 2, tau += 2) {
                 const char *X = parts + (c & 1) * kXBytes;
                 char *P = slots + (c % kFSlots) * kPBytes;
-                // first half: R, R^T, M^2 and (I - M)(I + M^2)
-                const f32x4 Rs = contract(X, kXKR, kXKI), RTs = contract(X, kXKI, kXKR);
+                // first half (tick c + 1): R, R^T and the first levels of the inverse
+                const f32x4 Rs = contract(P, kPKB, kPKI), RTs = contract(P, kPKI, kPKB);
                 const f32x4 beta_a = *reinterpret_cast<const f32x4 *>(X + kXBeta + 16 * g);
                 const float beta_b = reinterpret_cast<const float *>(X + kXBeta)[tok];
-                // rk = 1 / |k| per token, formed by the consumers in the previous tick
+                // rk = 1 / |k| per token, formed by consumer wave 3 in tick c
                 const float rkb = reinterpret_cast<const float *>(P + kPSC)[tok];
                 const f32x4 rka = *reinterpret_cast<const f32x4 *>(P + kPSC + 16 * g);
                 // D layout: element r is row a = 4g + r, column tok. R holds R (lower), RT
@@ -228,7 +254,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 }
                 const f32x4 Y3 = mm16_h(blk(3, R), Xi);  // level 3's Y (its update of Xi next tick)
                 tick_sync();
-                // second half: level 3's update, level 4 (Xi only), the store
+                // second half (tick c + 2): level 3's update, level 4 (Xi only), the store
                 {
                     const f32x4 Z = mm16_h(XiT, Y3), ZT = mm16_h(Y3, XiT);
                     Xi -= Z;
@@ -249,9 +275,8 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
         for (int tau = 0; tau < ticks; ++tau) {
             if (tau >= 1 && tau - 1 < nch) {
                 const int c = tau - 1;
-                const char *X = parts + (c & 1) * kXBytes;
                 char *P = slots + (c % kFSlots) * kPBytes;
-                const f32x4 AQs = contract(X, kXKI, kXQR);
+                const f32x4 AQs = contract(P, kPKI, kPQB);
                 const float rqb = reinterpret_cast<const float *>(P + kPSC + 64)[tok];  // s rq
                 f32x4 AQT;  // chi_{b,a} / rk_a = s rq_b (q_b . k_a decayed), a <= b
 #pragma unroll
@@ -275,11 +300,12 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
         }
         return;
     }
-    if (w >= kFCons && w < kFCons + kFPrep) {
+    if (w >= kFCons && w < kFCons + NP) {
         // ================================================================ stage-A waves
         if (nch == 0) return;  // uniform over the workgroup: no barrier is entered
         const int m = w - kFCons;
-        const int t = lane & 15, sg = lane >> 4;  // token; channel subgroup of 8
+        const int t = lane & 15, sg = lane >> 4;  // token; channel subgroup of NE
+        const int cl0 = AW * m + NE * sg;         // the lane's first key channel
         char *const myin = inring + m * kFIn * kIBytes;
         const char *const qb8 = reinterpret_cast<const char *>(q);
         const char *const kb8 = reinterpret_cast<const char *>(k);
@@ -287,50 +313,54 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
         const char *const vb8 = reinterpret_cast<const char *>(v);
         const char *const bb8 = reinterpret_cast<const char *>(braw);
 
-        // this wave's 32-channel slices of chunk c into input slot `slot`
+        // this wave's 32-channel slices of chunk c into input slot `slot` (a load's lane l
+        // writes LDS bytes 16 l on from its base)
         auto dma_chunk = [&](int c, int slot) {
             c = min(c, nch - 1);  // past the end: re-read the last chunk (never consumed)
-            const int row = min(tb + c * kC + (lane >> 2), te - 1);
-            const int64_t off = (((int64_t)row * H + h) * kD + 32 * m) * 2 + (lane & 3) * 16;
             char *dst = myin + slot * kIBytes;
-            __builtin_amdgcn_global_load_lds(qb8 + off, (lds_void *)(dst + kIQ), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(kb8 + off, (lds_void *)(dst + kIK), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vb8 + off, (lds_void *)(dst + kIV), 16, 0, 0);
             // the dword holding beta_raw[brow][h] (and a scalar g_raw[brow][h]): rounding
             // the address down to 4 bytes stays inside the 4-byte word, hence inside the
             // page, that holds the element
             const int brow = min(tb + c * kC + (lane & 15), te - 1);
             const int64_t eo = ((int64_t)brow * H + h) * 2;
-            if constexpr (SG) {
-                const uintptr_t ga = reinterpret_cast<uintptr_t>(gb8 + eo);
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(ga & ~(uintptr_t)3),
-                                                 (lds_void *)(dst + kIG), 4, 0, 0);
-            } else {
-                __builtin_amdgcn_global_load_lds(gb8 + off, (lds_void *)(dst + kIG), 16, 0, 0);
+            // one load per array: lane = (row l/4, 16-byte piece l%4)
+            const int row = min(tb + c * kC + (lane >> 2), te - 1);
+            const int64_t off = (((int64_t)row * H + h) * kD + AW * m) * 2 + (lane & 3) * 16;
+            __builtin_amdgcn_global_load_lds(qb8 + off, (lds_void *)(dst + kIQ), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(kb8 + off, (lds_void *)(dst + kIK), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vb8 + off, (lds_void *)(dst + kIV), 16, 0, 0);
+            if constexpr (!SG) __builtin_amdgcn_global_load_lds(gb8 + off, (lds_void *)(dst + kIG), 16, 0, 0);
+            if (lane < kC) {  // one dword per token, lanes 0-15 (64 bytes of the slot)
+                if constexpr (SG) {
+                    const uintptr_t ga = reinterpret_cast<uintptr_t>(gb8 + eo);
+                    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(ga & ~(uintptr_t)3),
+                                                     (lds_void *)(dst + kIG), 4, 0, 0);
+                }
+                const uintptr_t ba = reinterpret_cast<uintptr_t>(bb8 + eo);
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(ba & ~(uintptr_t)3),
+                                                 (lds_void *)(dst + kIB), 4, 0, 0);
             }
-            const uintptr_t ba = reinterpret_cast<uintptr_t>(bb8 + eo);
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(ba & ~(uintptr_t)3),
-                                             (lds_void *)(dst + kIB), 4, 0, 0);
         };
 #pragma unroll
         for (int i = 0; i < kFIn - 1; ++i) dma_chunk(i, i);
         // The inputs of chunk c are read from LDS into registers at the end of tick
         // c - 1 (chunk 0: here), so their LDS latency overlaps the other waves' work.
-        u32x4 qa, ka, ga, va;
+        typedef uint32_t uNE __attribute__((ext_vector_type(NE / 2)));
+        uNE qa, ka, ga, va;
         auto read_inputs = [&](int c) {
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kFPending) : "memory");  // chunk c landed
-            const char *I = myin + (c % kFIn) * kIBytes;
-            qa = *reinterpret_cast<const u32x4 *>(I + kIQ + t * 64 + sg * 16);
-            ka = *reinterpret_cast<const u32x4 *>(I + kIK + t * 64 + sg * 16);
+            const char *I = myin + (c % kFIn) * kIBytes + t * (2 * AW) + sg * (2 * NE);
+            qa = *reinterpret_cast<const uNE *>(I + kIQ);
+            ka = *reinterpret_cast<const uNE *>(I + kIK);
             if constexpr (SG) {
-                ga[0] = *reinterpret_cast<const uint32_t *>(I + kIG + t * 4);
+                ga[0] = *reinterpret_cast<const uint32_t *>(myin + (c % kFIn) * kIBytes + kIG + t * 4);
             } else {
-                ga = *reinterpret_cast<const u32x4 *>(I + kIG + t * 64 + sg * 16);
+                ga = *reinterpret_cast<const uNE *>(I + kIG);
             }
-            va = *reinterpret_cast<const u32x4 *>(I + kIV + t * 64 + sg * 16);
+            va = *reinterpret_cast<const uNE *>(I + kIV);
         };
         read_inputs(0);
-        tick_sync();  // start: chunk 0 has landed in this wave's ring (role 1 reads every ring)
+        tick_sync();  // start: chunk 0 has landed in this wave's ring (stage B reads every ring)
 
         const float lb2 = lb * kLog2e;
         // one tick of stage A on chunk c. The prepared slot c % kFSlots is a compile-time
@@ -339,7 +369,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
         auto stage_a = [&](const int c, auto slot_tag) {
             constexpr int slot = decltype(slot_tag)::value;
             // chunk c - 1's slot is free (its inputs were read before the last barrier,
-            // by this wave and by stage B role 1): refill it with chunk c + kFIn - 1
+            // by this wave and by stage B): refill it with chunk c + kFIn - 1
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             dma_chunk(c + kFIn - 1, (c + kFIn - 1) % kFIn);
             const int t0 = tb + c * kC, len = min(kC, te - t0);
@@ -349,10 +379,17 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
             // that are never stored
             const bool valid = t < len;
 
-            const float vmask = valid ? 1.f : 0.f;
-            float qf[8], kf[8], gf[8];
+            // gate in log2 units: lb2 sigma(x) = 1 / ((1 + e^-x) / lb2), one fma and one
+            // reciprocal after the exponential. Rows past the end (and lower_bound 0) take
+            // -FLT_MAX for 1/lb2: their gate is -0 or a denormal, which decays by nothing
+            // (a finite stand-in, so e^-x = 0 from x = +inf meets no 0 * inf)
+            const float ilb = (valid && lb2 != 0.f) ? 1.f / lb2 : -3.402823466e38f;
+            auto gate2 = [&](float x) {
+                return __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(-x * kLog2e), ilb, ilb));
+            };
+            float qf[NE], kf[NE], gf[NE];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < NE / 2; ++e) {
                 qf[2 * e] = bf_lo(qa[e]);
                 qf[2 * e + 1] = bf_hi(qa[e]);
                 kf[2 * e] = bf_lo(ka[e]);
@@ -362,7 +399,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 const int grow = min(t0 + t, te - 1);
                 const int64_t eo = ((int64_t)grow * H + h) * 2;  // byte offset of [grow][h]
                 const bool ghi = (reinterpret_cast<uintptr_t>(gb8 + eo) & 2) != 0;
-                float x = vmask * lb2 * sigmoid_fast(ghi ? bf_hi(ga[0]) : bf_lo(ga[0]));
+                float x = gate2(ghi ? bf_hi(ga[0]) : bf_lo(ga[0]));
                 // rounded exactly as the per-channel gate below, step by step
                 asm("" : "+v"(x));
                 x += row_shr<1>(x);
@@ -371,86 +408,100 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 x += row_shr<8>(x);
                 asm("" : "+v"(x));
 #pragma unroll
-                for (int i = 0; i < 8; ++i) gf[i] = x;
+                for (int i = 0; i < NE; ++i) gf[i] = x;
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < NE / 2; ++e) {
                     gf[2 * e] = bf_lo(ga[e]);
                     gf[2 * e + 1] = bf_hi(ga[e]);
                 }
+                // gate (log2 units) and prefix sum over tokens, one shift step at a time over
+                // all channels, so consecutive DPP adds touch different registers; the empty
+                // asm statements keep each value as computed, so each shifted add stays a
+                // single DPP add
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {  // gate (log2 units) and prefix sum over tokens
-                    float x = vmask * lb2 * sigmoid_fast(gf[i]);
-                    // the empty asm statements keep x as computed, so each shifted add
-                    // below becomes a single DPP add
-                    asm("" : "+v"(x));
-                    x += row_shr<1>(x);
-                    x += row_shr<2>(x);
-                    x += row_shr<4>(x);
-                    x += row_shr<8>(x);
-                    asm("" : "+v"(x));
-                    gf[i] = x;
+                for (int i = 0; i < NE; ++i) {
+                    gf[i] = gate2(gf[i]);
+                    asm("" : "+v"(gf[i]));
+                }
+#pragma unroll
+                for (int i = 0; i < NE; ++i) gf[i] += row_shr<1>(gf[i]);
+#pragma unroll
+                for (int i = 0; i < NE; ++i) gf[i] += row_shr<2>(gf[i]);
+#pragma unroll
+                for (int i = 0; i < NE; ++i) gf[i] += row_shr<4>(gf[i]);
+#pragma unroll
+                for (int i = 0; i < NE; ++i) {
+                    gf[i] += row_shr<8>(gf[i]);
+                    asm("" : "+v"(gf[i]));
                 }
             }
-            char *X = parts + (c & 1) * kXBytes;
             char *P = slots + slot * kPBytes;
-            // decays relative to token 7 (each factor within e^{8|lb|}); K_end via token 15
-            bf16x8 kr_h, ki_h, qr_h;
-            float ke[8];
+            // per element: K_b = k e^{G - r}, Q_b = q e^{G - r}, K_inv = k e^{r - G} and
+            // K_end = K_inv e^{G_last - r} (the factor from token 15's lane of the row);
+            // gamma = e^{G_last}, and e^{r} for the consumers when r is token 7's G
+            float ke[NE], gam[NE], er[NE];
+            bf16x4 kb4[NE / 4], qb4[NE / 4], ki4[NE / 4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float gref = row_bcast<7>(gf[i]);
-                const float up = __builtin_amdgcn_exp2f(gf[i] - gref);
-                const float dn = __builtin_amdgcn_exp2f(gref - gf[i]);
-                const float cl = row_bcast<15>(up);  // e^{G_last - Gref}
-                const float kr = kf[i] * up, ki = kf[i] * dn, qr = qf[i] * up;
-                kr_h[i] = (__bf16)kr;
-                ki_h[i] = (__bf16)ki;
-                qr_h[i] = (__bf16)qr;
+            for (int i = 0; i < NE; ++i) {
+                float up, dn, cl;
+                if constexpr (CSR) {  // r = 0
+                    up = __builtin_amdgcn_exp2f(gf[i]);
+                    dn = __builtin_amdgcn_exp2f(-gf[i]);
+                    cl = row_bcast<15>(up);
+                    gam[i] = up;
+                } else {  // r = G of token 7: every factor within e^{8 |lb|}
+                    const float gref = row_bcast<7>(gf[i]), d = gf[i] - gref;
+                    up = __builtin_amdgcn_exp2f(d);
+                    dn = __builtin_amdgcn_exp2f(-d);
+                    cl = row_bcast<15>(up);
+                    er[i] = __builtin_amdgcn_exp2f(gref);
+                    gam[i] = cl * er[i];
+                }
+                const float ki = kf[i] * dn;
+                kb4[i >> 2][i & 3] = (__bf16)(kf[i] * up);
+                qb4[i >> 2][i & 3] = (__bf16)(qf[i] * up);
+                ki4[i >> 2][i & 3] = (__bf16)ki;
                 ke[i] = ki * cl;
             }
-            // raw K_end = k e^{G_last - G}: consumer fragment (tile pair m), lane
-            // (kc + 16 (t/4)), element (t%4) + 4 hi, channel 32m + 16 hi + kc; rounded
-            // in pairs, stored as halves
+            // raw K_end as a bf16 hi/lo pair: channel cr = AW m + NE sg + i sits in tile pair
+            // cr / 32, consumer lane (cr % 16) + 16 (t / 4), tile half (cr / 16) % 2, element
+            // t % 4 (hi part; lo 8 bytes on); rounded in pairs, stored as halves
 #pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                const uint32_t pk = pk_bf16(f32x2{ke[i], ke[i + 1]});
+            for (int i = 0; i < NE; i += 2) {
+                const uint32_t ph = pk_bf16(f32x2{ke[i], ke[i + 1]});
+                const uint32_t pl = pk_bf16(f32x2{ke[i] - bf_lo(ph), ke[i + 1] - bf_hi(ph)});
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const int cr = 8 * sg + i + j, kc = cr & 15, hi = cr >> 4;
-                    *reinterpret_cast<uint16_t *>(P + kPKE + m * 1024 + swz(kc + 16 * (t >> 2)) * 16 +
-                                                  ((t & 3) + 4 * hi) * 2) = (uint16_t)(pk >> (16 * j));
+                    const int cr = cl0 + i + j, kc = cr & 15, hf = (cr >> 4) & 1;
+                    char *d = P + kPKE + (cr >> 5) * 2048 + swz(kc + 16 * (t >> 2)) * 32 + hf * 16 + (t & 3) * 2;
+                    *reinterpret_cast<uint16_t *>(d) = (uint16_t)(ph >> (16 * j));
+                    *reinterpret_cast<uint16_t *>(d + 8) = (uint16_t)(pl >> (16 * j));
                 }
             }
-            reinterpret_cast<bf16x8 *>(X + m * kXWave + kXKR)[lane] = kr_h;
-            reinterpret_cast<bf16x8 *>(X + m * kXWave + kXKI)[lane] = ki_h;
-            reinterpret_cast<bf16x8 *>(X + m * kXWave + kXQR)[lane] = qr_h;
-
-            // raw K_b = k e^{G}, Q_b = q e^{G} in the consumer's 16x16x32 A order
-            // (k step m); gamma = e^{G_last} from token 15; the v tile
-            bf16x4 kb4[2], qb4[2];
-            float dec[8];
+            // K_b, Q_b and K_inv in the consumer's 16x16x32 A order: the 4 channels from cb
+            // sit in tile pair cb / 32, consumer lane t + 16 gd, elements e0 .. e0 + 3
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                dec[i] = __builtin_amdgcn_exp2f(gf[i]);
-                kb4[i >> 2][i & 3] = (__bf16)(kf[i] * dec[i]);
-                qb4[i >> 2][i & 3] = (__bf16)(qf[i] * dec[i]);
+            for (int j = 0; j < NE / 4; ++j) {
+                const int cb = cl0 + 4 * j, q4 = (cb & 31) >> 2;
+                const int gd = q4 & 3, e0 = (q4 >> 2) * 4;
+                const int o = (cb >> 5) * 1024 + swz(t + 16 * gd) * 16 + e0 * 2;
+                *reinterpret_cast<bf16x4 *>(P + kPKB + o) = kb4[j];
+                *reinterpret_cast<bf16x4 *>(P + kPQB + o) = qb4[j];
+                *reinterpret_cast<bf16x4 *>(P + kPKI + o) = ki4[j];
             }
+            if (t == 15) {  // gamma (and e^{r}) per key channel
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int q4 = 2 * sg + hf;                 // which 4 channels of the 32
-                const int gd = q4 & 3, e0 = (q4 >> 2) * 4;  // consumer lane group, element
-                const int o = m * 1024 + swz(t + 16 * gd) * 16 + e0 * 2;
-                *reinterpret_cast<bf16x4 *>(P + kPKB + o) = kb4[hf];
-                *reinterpret_cast<bf16x4 *>(P + kPQB + o) = qb4[hf];
+                for (int j = 0; j < NE / 4; ++j) {
+                    float *gm = reinterpret_cast<float *>(P + kPGM) + cl0 + 4 * j;
+                    *reinterpret_cast<f32x4 *>(gm) = f32x4{gam[4 * j], gam[4 * j + 1], gam[4 * j + 2], gam[4 * j + 3]};
+                    if constexpr (!CSR) {
+                        float *e = reinterpret_cast<float *>(P + kPER) + cl0 + 4 * j;
+                        *reinterpret_cast<f32x4 *>(e) = f32x4{er[4 * j], er[4 * j + 1], er[4 * j + 2], er[4 * j + 3]};
+                    }
+                }
             }
-            if (t == 15) {
-                float *gm = reinterpret_cast<float *>(P + kPGM) + 32 * m + 8 * sg;
-                *reinterpret_cast<f32x4 *>(gm) = f32x4{dec[0], dec[1], dec[2], dec[3]};
-                *reinterpret_cast<f32x4 *>(gm + 4) = f32x4{dec[4], dec[5], dec[6], dec[7]};
-            }
-            *reinterpret_cast<u32x4 *>(P + kPV + t * kVRow + (32 * m + 8 * sg) * 2) =
-                valid ? va : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<uNE *>(P + kPV + t * kVRow + cl0 * 2) = valid ? va : uNE{};
             if (c + 1 < nch) read_inputs(c + 1);
         };
         // ticks past the last chunk only keep the barrier count
@@ -516,7 +567,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
             // products accumulated in fp32, with the same registers as both operands.
             // Lane (token i, group i/4) holds |x_i|^2. rk = 1/|k| and s rq = s/|q| go to
             // the chunk's slot for stage B (next tick) and for the consumers' own step
-            // two ticks later. Waves 1 and 3 share their SIMDs with the lighter stage-B
+            // three ticks later. Waves 1 and 3 share their SIMDs with the lighter stage-B
             // roles.
             static_assert(kFCons == 4, "consumer waves 1 and 3 form the norms");
             const bool isk = cw == 3;
@@ -538,7 +589,8 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
             const int c = tau - 3;
             const char *L = slots + (c % kFSlots) * kPBytes;
             const int t0 = tb + c * kC, len = min(kC, te - t0);
-            // K_b S^T and Q_b S^T for both column tiles (bf16 state operand)
+            // K_b S^T and Q_b S^T for both column tiles (bf16 state operand; with token 7's
+            // reference r, the state scaled by e^{r} per key channel: K_b e^{r} = k e^G)
             f32x4 xk[2], xq[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) xk[u] = xq[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -546,13 +598,18 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
             for (int p = 0; p < 4; ++p) {
                 const bf16x8 kb = *reinterpret_cast<const bf16x8 *>(L + kPKB + p * 1024 + sl * 16);
                 const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(L + kPQB + p * 1024 + sl * 16);
+                f32x4 er0 = {1.f, 1.f, 1.f, 1.f}, er1 = er0;
+                if constexpr (!CSR) {
+                    er0 = *reinterpret_cast<const f32x4 *>(L + kPER + (32 * p + 4 * g) * 4);
+                    er1 = *reinterpret_cast<const f32x4 *>(L + kPER + (32 * p + 16 + 4 * g) * 4);
+                }
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     bf16x8 sb;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        sb[r] = (__bf16)st[u][2 * p][r];
-                        sb[4 + r] = (__bf16)st[u][2 * p + 1][r];
+                        sb[r] = (__bf16)(CSR ? st[u][2 * p][r] : st[u][2 * p][r] * er0[r]);
+                        sb[4 + r] = (__bf16)(CSR ? st[u][2 * p + 1][r] : st[u][2 * p + 1][r] * er1[r]);
                     }
                     xk[u] = mma32(kb, sb, xk[u]);
                     // operands swapped: (Q_b S^T)^T, lane (token, g) holds value channels 4g..4g+3
@@ -583,9 +640,12 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                     }
                     xq[u][r] *= rq1;
                 }
+                // E' = Diag(rk) E with split-bf16 operands: A_h eb_h + A_l eb_h + A_h eb_l (an
+                // fp32 16x16x4 form measured slower: its four chained products sit on the
+                // recurrence's critical path)
                 bf16x4 eb_h, eb_l, e_h, e_l;
                 split4t_packed(eb, eb_h, eb_l);
-                f32x4 E = {0.f, 0.f, 0.f, 0.f};  // E' = Diag(rk) E: A_h eb_h + A_l eb_h + A_h eb_l
+                f32x4 E = {0.f, 0.f, 0.f, 0.f};
                 E = mma16(ab_h, eb_h, E);
                 E = mma16(ab_l, eb_h, E);
                 E = mma16(ab_h, eb_l, E);
@@ -600,18 +660,18 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
                 const u32x2 ob = {pk_bf16(f32x2{O[0], O[1]}), pk_bf16(f32x2{O[2], O[3]})};
                 if (col < len) *reinterpret_cast<u32x2 *>(orow + 16 * u) = ob;
             }
-            // S^T <- Diag(gamma) S^T + K_end^T E'
+            // S^T <- Diag(gamma) S^T + K_end^T E', K_end = hi + lo and E' = eh + el:
+            // [hi | lo] against [eh; eh] in one 16x16x32 product, then hi against el
+            bf16x8 ehh[2];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const u32x4 kq = *reinterpret_cast<const u32x4 *>(L + kPKE + p * 1024 + sl * 16);
+            for (int u = 0; u < 2; ++u) ehh[u] = cat8(eh[u], eh[u]);
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int t = 2 * p + hh;
-                    const bf16x4 kt = __builtin_bit_cast(bf16x4, hh ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]});
-                    const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kPGM + (16 * t + 4 * g) * 4);
+            for (int t = 0; t < 8; ++t) {
+                const bf16x8 k8 = *reinterpret_cast<const bf16x8 *>(L + kPKE + (t >> 1) * 2048 + sl * 32 + (t & 1) * 16);
+                const bf16x4 kt = {k8[0], k8[1], k8[2], k8[3]};
+                const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kPGM + (16 * t + 4 * g) * 4);
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) st[u][t] = mma16(kt, el[u], mma16(kt, eh[u], st[u][t] * gm));
-                }
+                for (int u = 0; u < 2; ++u) st[u][t] = mma16(kt, el[u], mma32(k8, ehh[u], st[u][t] * gm));
             }
         }
         // waves 1 and 3 stored the chunk's per-token scales above, which stage B reads
@@ -639,7 +699,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
             consume(std::integral_constant<int, 1>{}, w);
         } else if (nch > 0) {  // transfer-run waves
             if (gseg > 0) {
-                consume(std::integral_constant<int, 2>{}, w - (kFCons + kFPrep + 2));
+                consume(std::integral_constant<int, 2>{}, w - (kFCons + NP + 2));
             } else {
 #pragma unroll 1
                 for (int tau = 0; tau <= ticks; ++tau) bar_sync();  // the start barrier and every tick's
@@ -650,7 +710,7 @@ __global__ __launch_bounds__(SEG ? kFThreadsSeg : kFThreads) void kf_fused(
     }
 }
 
-template <typename TSt, bool SG, bool SEG>
+template <typename TSt, bool SG, bool SEG, bool CSR>
 static hipError_t launch_fused_t(const Problem &p, hipStream_t s)
 {
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
@@ -660,7 +720,7 @@ static hipError_t launch_fused_t(const Problem &p, hipStream_t s)
     float *phi = SEG ? reinterpret_cast<float *>(p.ws + p.lay.phi) : nullptr;
     uint16_t *ybuf = SEG ? reinterpret_cast<uint16_t *>(p.ws + p.lay.ybuf) : nullptr;
     const int64_t groups = (SEG ? p.lay.seg_max : p.N) * p.H;
-    hipLaunchKernelGGL((kf_fused<TSt, SG, SEG>), dim3((unsigned)groups), dim3(SEG ? kFThreadsSeg : kFThreads), 0, s,
+    hipLaunchKernelGGL((kf_fused<TSt, SG, SEG, CSR>), dim3((unsigned)groups), dim3(f_threads<SEG>()), 0, s,
                        (const uint16_t *)p.q, (const uint16_t *)p.k, (const uint16_t *)p.v, (const uint16_t *)p.g,
                        (const uint16_t *)p.beta, (const TSt *)p.s0, (TSt *)p.s1, (uint16_t *)p.out, tok, chk, p.H,
                        p.lb, p.scale, seg, (int)p.N, (int)p.lay.seg_len, (int)p.lay.seg_first, sfin, phi, ybuf,
@@ -668,17 +728,26 @@ static hipError_t launch_fused_t(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
+// decays referenced to the chunk start from lower_bound -5 up (see kf_fused)
+constexpr float kCsrMinLowerBound = -5.0f;
+
+template <bool SEG, bool CSR>
+static hipError_t launch_fused_ref(const Problem &p, hipStream_t s)
+{
+    if (p.scalar_gate)
+        return p.st_bf16 ? launch_fused_t<uint16_t, true, SEG, CSR>(p, s) : launch_fused_t<float, true, SEG, CSR>(p, s);
+    return p.st_bf16 ? launch_fused_t<uint16_t, false, SEG, CSR>(p, s) : launch_fused_t<float, false, SEG, CSR>(p, s);
+}
+
 template <bool SEG>
 static hipError_t launch_fused_any(const Problem &p, hipStream_t s)
 {
-    if (p.scalar_gate)
-        return p.st_bf16 ? launch_fused_t<uint16_t, true, SEG>(p, s) : launch_fused_t<float, true, SEG>(p, s);
-    return p.st_bf16 ? launch_fused_t<uint16_t, false, SEG>(p, s) : launch_fused_t<float, false, SEG>(p, s);
+    return p.lb >= kCsrMinLowerBound ? launch_fused_ref<SEG, true>(p, s) : launch_fused_ref<SEG, false>(p, s);
 }
 
 bool fits_fused(const Problem &p, bool seg)
 {
-    return seg ? grid_fits(p.lay.seg_max * p.H, 1, kFThreadsSeg) : grid_fits(p.N * p.H, 1, kFThreads);
+    return seg ? grid_fits(p.lay.seg_max * p.H, 1, f_threads<true>()) : grid_fits(p.N * p.H, 1, f_threads<false>());
 }
 
 hipError_t launch_fused(const Problem &p, hipStream_t s) { return launch_fused_any<false>(p, s); }

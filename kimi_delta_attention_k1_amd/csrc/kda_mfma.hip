@@ -187,15 +187,30 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
         AQT[r] = (a <= tok) ? dAQT[r] : 0.f;           // (A^qk)^T[a][tok] = chi_{tok,a}
     }
 
-    // ---- (A^kk)^T = (I + M)^-1 with M = R^T: (I-M)(I+M^2)(I+M^4)(I+M^8), exact since M^16 = 0
-    const f32x4 M2 = mm16_f32(R, RT);
-    const f32x4 M2T = mm16_f32(RT, R);
-    const f32x4 M4 = mm16_f32(M2T, M2);
-    const f32x4 M4T = mm16_f32(M2, M2T);
-    const f32x4 M8T = mm16_f32(M4, M4T);
-    const f32x4 P1 = mm16_f32(eye_plus(R, -1.f, g, tok), eye_plus(M2, 1.f, g, tok));
-    const f32x4 P2 = mm16_f32(eye_plus(M4T, 1.f, g, tok), P1);
-    const f32x4 AT = mm16_f32(eye_plus(M8T, 1.f, g, tok), P2);
+    // ---- (A^kk)^T = (I + M)^-1 with M = R^T (strictly upper triangular), by block
+    // inversion over levels of diagonal blocks of 2, 4, 8 and 16 rows: with X the inverse
+    // of one level's diagonal blocks and C the part of M in the next level's off-diagonal
+    // blocks, X - X C X inverts the next level's blocks. Every value formed is a block
+    // of the inverse or a sum of bounded products; the doubling product
+    // (I - M)(I + M^2)(I + M^4)(I + M^8) would form M^8, whose entries reach the
+    // thousands for correlated keys that barely decay, and then cancel.
+    auto blk = [&](int L, f32x4 x) {  // the part of x in level L's off-diagonal blocks
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int a = 4 * g + r;
+            x[r] = ((a >> L) == (tok >> L) && (a >> (L - 1)) != (tok >> (L - 1))) ? x[r] : 0.f;
+        }
+        return x;
+    };
+    f32x4 Xi = eye_plus(blk(1, RT), -1.f, g, tok), XiT = eye_plus(blk(1, R), -1.f, g, tok);
+#pragma unroll
+    for (int L = 2; L <= 3; ++L) {  // Y = C_L Xi; Xi <- Xi - Xi Y, XiT <- XiT - Y^T XiT
+        const f32x4 Y = mm16_f32(blk(L, R), Xi);
+        const f32x4 Z = mm16_f32(XiT, Y), ZT = mm16_f32(Y, XiT);
+        Xi -= Z;
+        XiT -= ZT;
+    }
+    const f32x4 AT = Xi - mm16_f32(XiT, mm16_f32(blk(4, R), Xi));
     f32x4 ABT;  // (A^kk Diag(beta))^T[a][tok] = beta_a A^kk[tok][a]
 #pragma unroll
     for (int r = 0; r < 4; ++r) ABT[r] = beta_row[r] * AT[r];

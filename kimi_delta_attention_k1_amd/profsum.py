@@ -56,9 +56,11 @@ def src_hash(kernel: str) -> str:
 
 
 def short_name(kernel_name: str) -> str:
-    # the segmented instantiations of the single pass end their template list with "true>"
-    if "kda::kf_fused<" in kernel_name and kernel_name.split("(")[0].endswith("true>"):
-        return "kf_fused_seg"
+    # the single pass's template arguments are <state type, scalar gate, segmented, chunk-start
+    # reference>: the segmented instantiations have "true" third
+    if "kda::kf_fused<" in kernel_name:
+        targs = kernel_name.split("(")[0].split("kda::kf_fused<", 1)[1].rstrip(">").split(",")
+        return "kf_fused_seg" if len(targs) > 2 and targs[2].strip() == "true" else "kf_fused"
     for short, keys in SHORT.items():
         if any(key in kernel_name for key in keys):
             return short
