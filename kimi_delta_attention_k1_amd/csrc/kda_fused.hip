@@ -590,7 +590,11 @@ __global__ __launch_bounds__(f_threads<SEG>()) void kf_fused(
             const char *L = slots + (c % kFSlots) * kPBytes;
             const int t0 = tb + c * kC, len = min(kC, te - t0);
             // K_b S^T and Q_b S^T for both column tiles (bf16 state operand; with token 7's
-            // reference r, the state scaled by e^{r} per key channel: K_b e^{r} = k e^G)
+            // reference r, the state scaled by e^{r} per key channel: K_b e^{r} = k e^G).
+            // K_b and Q_b are read here, in the tick that uses them. Loading them into
+            // registers before the previous barrier gave wrong outputs with ROCm 7.2.0's
+            // hipcc (AMD clang 22, roc-7.2.0): the code it generated wrote a VALU result
+            // into an accumulator operand of an MFMA still in flight.
             f32x4 xk[2], xq[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) xk[u] = xq[u] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -409,7 +409,12 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                 }
             }
         };
-        // S^T <- Diag(gamma) S^T + K_end^T (E_hi + E_lo): [K_end | K_end] x [E_hi ; E_lo]
+        // S^T <- Diag(gamma) S^T + K_end^T (E_hi + E_lo): [K_end | K_end] x [E_hi ; E_lo].
+        // One 16x16x32 product per tile, the last writer of the accumulator. Forms that
+        // chain a 16x16x16 product onto this accumulator (for a K_end hi/lo pair) gave
+        // wrong states or outputs in this kernel with ROCm 7.2.0's hipcc (AMD clang 22,
+        // roc-7.2.0), also with s_nop padding between the products; the same chain is
+        // correct in kf_fused.
         auto update = [&](const char *L, bf16x8 e_hl) {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
@@ -457,6 +462,9 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                 E = mma16(ab_h, eb_l, E);
                 split4(E, e_h, e_l);
                 const bf16x8 e_hl = cat8(e_h, e_l);
+                // the output wave gets E in fp32 and splits it itself: handing over the
+                // bf16 hi/lo registers instead gave wrong outputs (with correct states)
+                // with ROCm 7.2.0's hipcc
                 ebuf[j & 1][wc][lane] = E;
                 update(L, e_hl);
                 // the E tile is in LDS before the barrier publishes it
@@ -507,6 +515,9 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
 #pragma unroll 1
             for (int j = 0; j < nch; ++j) {
                 if (j > 0) out_step(j - 1, true);
+                // this wave's LDS reads (the E tile the recurrence wave rewrites two
+                // barriers on, the unit's slot) are complete before the barrier
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 bar_sync();
             }
             if (nch > 0) out_step(nch - 1, false);
@@ -585,6 +596,8 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                 if constexpr (RS) st[t] = round_bf16x4(st[t]);
             }
         }
+        // this wave's reads of the slot are complete before it may be refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         bar_sync();  // this chunk's slot may be refilled; chunk j+1 is published
     }
     if (s1) {
