@@ -665,7 +665,11 @@ __global__ __launch_bounds__(f_threads<SEG>()) void kf_fused(
                 if (col < len) *reinterpret_cast<u32x2 *>(orow + 16 * u) = ob;
             }
             // S^T <- Diag(gamma) S^T + K_end^T E', K_end = hi + lo and E' = eh + el:
-            // [hi | lo] against [eh; eh] in one 16x16x32 product, then hi against el
+            // [hi | lo] against [eh; eh] in one 16x16x32 product, then hi against el in a
+            // 16x16x16 one. Such a pair needs about five wait states between its products
+            // (see mma16); here the two column tiles' products interleave, which puts three
+            // or more independent products between them, and a host test checks the
+            // generated code for it. A second 16x16x32 product instead costs 3% at C3.
             bf16x8 ehh[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) ehh[u] = cat8(eh[u], eh[u]);

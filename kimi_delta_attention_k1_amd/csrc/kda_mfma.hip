@@ -410,11 +410,6 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
             }
         };
         // S^T <- Diag(gamma) S^T + K_end^T (E_hi + E_lo): [K_end | K_end] x [E_hi ; E_lo].
-        // One 16x16x32 product per tile, the last writer of the accumulator. Forms that
-        // chain a 16x16x16 product onto this accumulator (for a K_end hi/lo pair) gave
-        // wrong states or outputs in this kernel with ROCm 7.2.0's hipcc (AMD clang 22,
-        // roc-7.2.0), also with s_nop padding between the products; the same chain is
-        // correct in kf_fused.
         auto update = [&](const char *L, bf16x8 e_hl) {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
@@ -456,15 +451,14 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                 bf16x4 eb_h, eb_l, e_h, e_l;
                 split4(eb, eb_h, eb_l);
                 const bf16x8 ab = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.ab + lane * 16);
-                const bf16x4 ab_h = {ab[0], ab[1], ab[2], ab[3]};
                 f32x4 E = {0.f, 0.f, 0.f, 0.f};
                 E = mma32(ab, cat8(eb_h, eb_h), E);
-                E = mma16(ab_h, eb_l, E);
+                E = mma32(ab, cat8(eb_l, eb_l), E);
                 split4(E, e_h, e_l);
                 const bf16x8 e_hl = cat8(e_h, e_l);
-                // the output wave gets E in fp32 and splits it itself: handing over the
-                // bf16 hi/lo registers instead gave wrong outputs (with correct states)
-                // with ROCm 7.2.0's hipcc
+                // the output wave gets E in fp32 and splits it itself (a variant that handed
+                // over the bf16 hi/lo registers gave wrong outputs; it chained products of
+                // two shapes, which the note at mma16 explains)
                 ebuf[j & 1][wc][lane] = E;
                 update(L, e_hl);
                 // the E tile is in LDS before the barrier publishes it
@@ -497,9 +491,8 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                 const bf16x8 e_hl = cat8(e_h, e_l);
                 // O = Q_b S^T + A^qk E
                 const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.aq + lane * 16);
-                const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]};
                 f32x4 O = mma32(aq, cat8(e_h, e_h), xq);
-                O = mma16(aq_h, e_l, O);
+                O = mma32(aq, cat8(e_l, e_l), O);
                 uint16_t *orow = out + ((int64_t)(t0 + 4 * g) * H + h) * kD + vcol;
                 const int64_t rstride = (int64_t)H * kD;
                 if (len == kC) {
@@ -557,21 +550,19 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                 *reinterpret_cast<const uint16_t *>(L + kVOff + tr * (32 * CONS) + (vcol - 16 * wbase) * 2);
             eb[r] = (tr < len ? bf16_bits_to_f32(vr) : 0.f) - xk[r];
         }
-        // A operands arrive as {hi, lo}: [hi | lo] x [x_hi ; x_hi] + hi x x_lo is the
-        // split product hi*x_hi + lo*x_hi + hi*x_lo in two instructions.
+        // A operands arrive as {hi, lo}: [hi | lo] x [x_hi ; x_hi] + [hi | lo] x [x_lo ; x_lo]
+        // is the split product (hi + lo)(x_hi + x_lo) in two 16x16x32 instructions.
         bf16x4 eb_h, eb_l, e_h, e_l;
         split4(eb, eb_h, eb_l);
         const bf16x8 ab = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.ab + lane * 16);
-        const bf16x4 ab_h = {ab[0], ab[1], ab[2], ab[3]};
         f32x4 E = {0.f, 0.f, 0.f, 0.f};
         E = mma32(ab, cat8(eb_h, eb_h), E);
-        E = mma16(ab_h, eb_l, E);
+        E = mma32(ab, cat8(eb_l, eb_l), E);
         split4(E, e_h, e_l);
         // O = Q_b S^T + A^qk E
         const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.aq + lane * 16);
-        const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]};
         f32x4 O = mma32(aq, cat8(e_h, e_h), xq);
-        O = mma16(aq_h, e_l, O);
+        O = mma32(aq, cat8(e_l, e_l), O);
         uint16_t *orow = out + ((int64_t)(t0 + 4 * g) * H + h) * kD + vcol;
         const int64_t rstride = (int64_t)H * kD;
         if (len == kC) {
@@ -734,8 +725,9 @@ __global__ __launch_bounds__(KLShape<CONS>::threads) void k2_look(
             if (c > 0) {  // + M E_prev in split operands
                 bf16x4 m_h, m_l;
                 split4(mbuf[c & 1][wc][lane], m_h, m_l);
-                xk = mma32(cat8(m_h, m_l), cat8(ep_h, ep_h), xk);
-                xk = mma16(m_h, ep_l, xk);
+                const bf16x8 m_hl = cat8(m_h, m_l);
+                xk = mma32(m_hl, cat8(ep_h, ep_h), xk);
+                xk = mma32(m_hl, cat8(ep_l, ep_l), xk);
             }
             f32x4 eb;
 #pragma unroll
@@ -748,10 +740,9 @@ __global__ __launch_bounds__(KLShape<CONS>::threads) void k2_look(
             bf16x4 eb_h, eb_l;
             split4(eb, eb_h, eb_l);
             const bf16x8 ab = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.ab + lane * 16);
-            const bf16x4 ab_h = {ab[0], ab[1], ab[2], ab[3]};
             f32x4 E = {0.f, 0.f, 0.f, 0.f};
             E = mma32(ab, cat8(eb_h, eb_h), E);
-            E = mma16(ab_h, eb_l, E);
+            E = mma32(ab, cat8(eb_l, eb_l), E);
             ebuf[c & 1][wc][lane] = E;
             split4(E, ep_h, ep_l);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -832,9 +823,8 @@ __global__ __launch_bounds__(KLShape<CONS>::threads) void k2_look(
         bf16x4 e_h, e_l;
         split4(ebuf[c & 1][wc][lane], e_h, e_l);
         const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.aq + lane * 16);
-        const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]};
         f32x4 O = mma32(aq, cat8(e_h, e_h), xqbuf[c & 1][0][wc][lane] + xqbuf[c & 1][1][wc][lane]);
-        O = mma16(aq_h, e_l, O);
+        O = mma32(aq, cat8(e_l, e_l), O);
         uint16_t *orow = out + ((int64_t)(t0 + 4 * g) * H + h) * kD + vcol;
         const int64_t rstride = (int64_t)H * kD;
 #pragma unroll

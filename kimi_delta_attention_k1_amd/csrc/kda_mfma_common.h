@@ -24,6 +24,14 @@ __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// A product that accumulates onto the result of the product just before it must have
+// that product's shape (16x16x32 after 16x16x32, 16x16x16 after 16x16x16). Measured on
+// gfx950: when a 16x16x16 bf16 product takes as its accumulator the result of a 16x16x32
+// one (or the reverse) fewer than about five wait states later, half of its accumulator
+// elements are read before that result is written, so the earlier product is lost there.
+// ROCm 7.2.0's compiler (AMD clang 22, roc-7.2.0) inserts no wait states between the two.
+// Split-bf16 products therefore add their lo terms with a second 16x16x32 product,
+// [x_hi | x_lo] x [y_lo ; y_lo], never with a 16x16x16 one on the same accumulator.
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
@@ -129,20 +137,6 @@ __device__ __forceinline__ f32x4 mm16_f32(f32x4 xt, f32x4 y)
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = mma4(xt[s], y[s], acc);
     return acc;
-}
-
-// C = X Y for 16x16 tiles from split bf16 operands (X_hi Y_hi + X_lo Y_hi + X_hi Y_lo,
-// about 16 significant bits per product); xt holds X^T and y holds Y in D layout, which
-// is the 16x16x16 operand layout of both: lane (tok, g) holds X[tok][4g..4g+3] and
-// Y[4g..4g+3][tok]
-__device__ __forceinline__ f32x4 mm16_bf(f32x4 xt, f32x4 y)
-{
-    bf16x4 xh, xl, yh, yl;
-    split4(xt, xh, xl);
-    split4(y, yh, yl);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mma32(cat8(xh, xl), cat8(yh, yh), acc);
-    return mma16(xh, yl, acc);
 }
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
