@@ -93,7 +93,13 @@ enum {
      * kda_fwd_prepare + kda_fwd_recur run. With fewer than 96 (sequence, head)
      * pairs (and without KDA_FLAG_BF16_RESIDENT_STATE) the recurrence runs in
      * look-ahead form and the workspace also holds 4096 B per (chunk, head);
-     * kda_fwd_workspace_size accounts for it. */
+     * kda_fwd_workspace_size accounts for it. Accuracy limit: this path keeps
+     * the state-update key operand K_end = khat e^{G_last - G} in one bf16, so
+     * keys that stay strongly correlated over hundreds of tokens (cosine 0.96
+     * and above between all keys of a head) with little or no decay can exceed
+     * the bf16 bound on the final state (measured 2.1x at cosine 0.96 over 512
+     * tokens with lower_bound 0 and beta 1); the single-pass and segmented
+     * paths stay within it there (KDA_FLAG_FUSED, KDA_FLAG_SEGMENTED). */
     KDA_FLAG_SPLIT = 2u,
     /* bf16-compute kda_fwd: run the single-pass kernel (one workgroup per
      * (sequence, head) prepares each chunk in on-chip memory and runs the
@@ -145,13 +151,14 @@ enum {
 };
 /* Without a path flag, kda_fwd runs the token-by-token kernel when the
  * sequences average at most KDA_RECURRENT_MAX_AVG_TOKENS tokens (batch mode:
- * seqlen; packed: T_tot / num_seqs), else, for bf16 compute, the single-pass
- * segmented single pass when num_seqs * num_heads <= KDA_SEGMENTED_MAX_PAIRS
- * and the sequences average at least KDA_SEGMENTED_MIN_AVG_CHUNKS 16-token
- * chunks (chunk bound / num_seqs), else the single-pass kernel when
+ * seqlen; packed: T_tot / num_seqs), else, for bf16 compute, the segmented
+ * single pass when num_seqs * num_heads <= KDA_SEGMENTED_MAX_PAIRS and the
+ * sequences average at least KDA_SEGMENTED_MIN_AVG_CHUNKS 16-token chunks
+ * (chunk bound / num_seqs), else the single-pass kernel when
  * num_seqs * num_heads >= KDA_FUSED_MIN_PAIRS, and the two-kernel path
- * otherwise; fp32 compute uses the fp32 two-kernel path. The thresholds are
- * where each path measured fastest on MI355X. The two paths evaluate the same chunkwise equations and
+ * otherwise (see KDA_FLAG_SPLIT for its accuracy limit); fp32 compute uses
+ * the fp32 two-kernel path. The thresholds are where each path measured
+ * fastest on MI355X. The paths evaluate the same chunkwise equations and
  * agree to bf16 rounding; they are not bitwise identical (the single pass
  * applies the L2 normalisation after its in-chunk products instead of
  * before). */
