@@ -182,7 +182,9 @@ def pick_path(kda, w, path):
     n_c = sum((L + 15) // 16 for L in w.seq_lens) if not w.packed else (w.T_tot + 15 * w.N) // 16
     if w.N * w.H <= kda.SEGMENTED_MAX_PAIRS and n_c >= kda.SEGMENTED_MIN_AVG_CHUNKS * w.N:
         return "segmented"
-    return "fused" if w.N * w.H >= kda.FUSED_MIN_PAIRS else "split"
+    if w.N * w.H >= kda.FUSED_MIN_PAIRS or n_c <= kda.FUSED_MAX_AVG_CHUNKS * w.N:
+        return "fused"
+    return "split"
 
 
 def to_device(w, dev):

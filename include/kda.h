@@ -155,14 +155,16 @@ enum {
  * single pass when num_seqs * num_heads <= KDA_SEGMENTED_MAX_PAIRS and the
  * sequences average at least KDA_SEGMENTED_MIN_AVG_CHUNKS 16-token chunks
  * (chunk bound / num_seqs), else the single-pass kernel when
- * num_seqs * num_heads >= KDA_FUSED_MIN_PAIRS, and the two-kernel path
- * otherwise (see KDA_FLAG_SPLIT for its accuracy limit); fp32 compute uses
+ * num_seqs * num_heads >= KDA_FUSED_MIN_PAIRS or the sequences average at
+ * most KDA_FUSED_MAX_AVG_CHUNKS chunks, and the two-kernel path otherwise
+ * (see KDA_FLAG_SPLIT for its accuracy limit); fp32 compute uses
  * the fp32 two-kernel path. The thresholds are where each path measured
  * fastest on MI355X. The paths evaluate the same chunkwise equations and
  * agree to bf16 rounding; they are not bitwise identical (the single pass
  * applies the L2 normalisation after its in-chunk products instead of
  * before). */
 #define KDA_FUSED_MIN_PAIRS 96
+#define KDA_FUSED_MAX_AVG_CHUNKS 8
 #define KDA_SEGMENTED_MAX_PAIRS 128
 #define KDA_SEGMENTED_MIN_AVG_CHUNKS 128
 #define KDA_RECURRENT_MAX_AVG_TOKENS 4

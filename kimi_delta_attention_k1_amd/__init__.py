@@ -16,8 +16,8 @@ an output correction; bf16 compute only), "recurrent" (the recurrence token by
 token, for decode and short sequences) or "auto" (the library's rule: recurrent
 up to RECURRENT_MAX_AVG_TOKENS tokens per sequence on average, else segmented
 up to SEGMENTED_MAX_PAIRS (sequence, head) pairs when the sequences average at
-least SEGMENTED_MIN_AVG_CHUNKS chunks, else fused from FUSED_MIN_PAIRS pairs on,
-else split).
+least SEGMENTED_MIN_AVG_CHUNKS chunks, else fused from FUSED_MIN_PAIRS pairs on
+or when the sequences average at most FUSED_MAX_AVG_CHUNKS chunks, else split).
 
 Layouts follow the FlashKDA API (DocSearch FlashKDA digest, "flash_kda.fwd API
 reference"): q, k, v, g_raw are [B, T, H, 128] (or packed [T_tot, H, 128]),
@@ -34,7 +34,7 @@ import os
 __all__ = ["fwd", "fwd_noalloc", "prepare_call", "Call", "workspace_size", "KdaError", "load_library", "library_path", "seqlens_flag",
            "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE", "FLAG_SPLIT", "FLAG_FUSED", "FLAG_RECURRENT", "FLAG_SCALAR_GATE",
            "FLAG_BF16_RESIDENT_STATE", "FLAG_SEGMENTED",
-           "FUSED_MIN_PAIRS", "SEGMENTED_MAX_PAIRS", "SEGMENTED_MIN_AVG_CHUNKS", "RECURRENT_MAX_AVG_TOKENS"]
+           "FUSED_MIN_PAIRS", "FUSED_MAX_AVG_CHUNKS", "SEGMENTED_MAX_PAIRS", "SEGMENTED_MIN_AVG_CHUNKS", "RECURRENT_MAX_AVG_TOKENS"]
 
 HEAD_DIM = 128
 CHUNK = 16
@@ -46,6 +46,7 @@ FLAG_SCALAR_GATE = 16
 FLAG_BF16_RESIDENT_STATE = 32
 FLAG_SEGMENTED = 64
 FUSED_MIN_PAIRS = 96
+FUSED_MAX_AVG_CHUNKS = 8
 SEGMENTED_MAX_PAIRS = 128
 SEGMENTED_MIN_AVG_CHUNKS = 128
 RECURRENT_MAX_AVG_TOKENS = 4

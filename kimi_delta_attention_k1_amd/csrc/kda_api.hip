@@ -54,7 +54,9 @@ Path pick_path(const kda_desc_t *d, bool f32_path, int64_t T_tot, int64_t n_c_ma
     if (T_tot <= (int64_t)KDA_RECURRENT_MAX_AVG_TOKENS * d->num_seqs) return kRecurrent;
     if (f32_path) return kSplit;
     if (seg_worth(d, n_c_max)) return kSeg;
-    if (d->num_seqs * (int64_t)d->num_heads >= KDA_FUSED_MIN_PAIRS) return kFused;
+    if (d->num_seqs * (int64_t)d->num_heads >= KDA_FUSED_MIN_PAIRS ||
+        n_c_max <= (int64_t)KDA_FUSED_MAX_AVG_CHUNKS * d->num_seqs)
+        return kFused;
     return kSplit;
 }
 

@@ -162,7 +162,7 @@ def _desc(**kw):
     (dict(drop=("q",)), NULL_ARG),
     (dict(drop=("out",)), NULL_ARG),
     (dict(drop=("ws",)), WORKSPACE),
-    (dict(ws_bytes=1000), WORKSPACE),
+    (dict(ws_bytes=256), WORKSPACE),  # below every path's chunk map
     (dict(shift=dict(ws=64)), WORKSPACE),
     (dict(shift=dict(q=2)), MISALIGNED),
     (dict(shift=dict(g=2)), MISALIGNED),                     # [T][H][128] g_raw needs 16 bytes

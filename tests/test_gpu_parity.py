@@ -1,5 +1,9 @@
 """GPU parity: the HIP library through its C ABI against the fp64 oracle.
 
+The cases here run the two-kernel path (and its fp32 form) unless they name another
+path; the full-size workloads run the automatic rule. The automatic rule sends short
+sequences to the single pass, whose edge cases tests/test_gpu_fused.py covers.
+
 Tolerances (global max over the compared tensor):
   bf16 I/O : max|x_gpu - x_ref| <= 1e-2 max|x_ref| + 1e-3, for o and the final state
   fp32 path: max|x_gpu - x_ref| <= 1e-5 max|x_ref|
@@ -13,13 +17,19 @@ import torch
 import kimi_delta_attention_k1_amd as kda
 from kimi_delta_attention_k1_amd import workloads
 from oracle import chunked
-from tests.gpu_helpers import bf16_tol, compare, f32_tol, np64, run_gpu, run_oracle
+from tests.gpu_helpers import bf16_tol, compare, f32_tol, np64, run_oracle
+from tests.gpu_helpers import run_gpu as _run_gpu
 
 pytestmark = pytest.mark.gpu
 
 
 def _banner(name):
     print(f"\n[case] {name}", flush=True)
+
+
+def run_gpu(w, dev, **kw):
+    kw.setdefault("path", "split")
+    return _run_gpu(w, dev, **kw)
 
 
 # ------------------------------------------------------------------ named workloads
@@ -61,7 +71,7 @@ def _all_pairs(w):
 def test_c3_all_pairs(gpu):
     _banner("c3 packed 8 x 8192, H=32, automatic path (single pass), all 256 pairs")
     w = workloads.c3()
-    o, s = run_gpu(w, gpu)
+    o, s = run_gpu(w, gpu, path="auto")
     assert torch.isfinite(o).all() and torch.isfinite(s).all()
     compare(w, o, s, run_oracle(w, pairs=_all_pairs(w)), bf16_tol, "c3 bf16 all pairs")
 
@@ -69,7 +79,7 @@ def test_c3_all_pairs(gpu):
 def test_c4_all_heads(gpu):
     _banner("c4 long context T=131072, H=32, automatic path (segmented), all 32 heads")
     w = workloads.c4()
-    o, s = run_gpu(w, gpu)
+    o, s = run_gpu(w, gpu, path="auto")
     assert torch.isfinite(o).all() and torch.isfinite(s).all()
     compare(w, o, s, run_oracle(w, pairs=_all_pairs(w)), bf16_tol, "c4 bf16 all heads")
 
@@ -77,7 +87,7 @@ def test_c4_all_heads(gpu):
 def test_c5_all_pairs(gpu):
     _banner("c5 ragged 64 sequences, H=32, automatic path (single pass), all 2048 pairs")
     w = workloads.c5()
-    o, s = run_gpu(w, gpu)
+    o, s = run_gpu(w, gpu, path="auto")
     assert torch.isfinite(o).all() and torch.isfinite(s).all()
     compare(w, o, s, run_oracle(w, pairs=_all_pairs(w)), bf16_tol, "c5 bf16 all pairs")
 
@@ -143,7 +153,8 @@ def test_inplace_state_and_determinism(gpu):
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     buf = w.initial_state.to(gpu).contiguous()
     q, k, v, g, b = (t.to(gpu) for t in (w.q, w.k, w.v, w.g_raw, w.beta_raw))
-    o3, s3 = kda.fwd(q, k, v, g, b, initial_state=buf, final_state=buf, cu_seqlens=w.cu_seqlens().to(gpu))
+    o3, s3 = kda.fwd(q, k, v, g, b, initial_state=buf, final_state=buf, cu_seqlens=w.cu_seqlens().to(gpu),
+                     path="split")
     torch.cuda.synchronize()
     assert s3.data_ptr() == buf.data_ptr()
     assert torch.equal(o3, o1) and torch.equal(s3, s1)
@@ -251,7 +262,7 @@ def test_k1_intermediates_against_chunked_oracle(gpu):
     w = workloads.make([40, 16], 2, seed=37)
     T, H = w.T_tot, w.H
     ws = torch.zeros(kda.workspace_size(1, T, w.N, H), dtype=torch.uint8, device=gpu)
-    run_gpu(w, gpu, workspace=ws)
+    run_gpu(w, gpu, workspace=ws, path="split")  # the chunk kernel writes the units
     f = lambda t: t.float().numpy()  # noqa: E731
     _, _, inter = chunked.forward(f(w.q), f(w.k), f(w.v), f(w.g_raw), f(w.beta_raw), w.offsets(),
                                   lower_bound=w.lower_bound, keep=True)

@@ -169,6 +169,8 @@ def test_stage_entry_points_compose_to_kda_fwd(gpu):
     (43, 3, 2048, "fused"),      # 129 pairs: two segments per pair no longer fit one round
     (32, 3, 2032, "fused"),      # 96 pairs, 127 chunks per sequence: too short to segment
     (19, 5, 2032, "split"),      # 95 pairs, too short to segment
+    (8, 4, 128, "fused"),        # 32 pairs of 8 chunks: short sequences take the single pass
+    (8, 4, 144, "split"),        # 9 chunks per sequence
 ])
 def test_automatic_rule_boundaries(gpu, N, H, T, expect):
     """Without a path flag, kda_fwd runs exactly the path the rule names (bitwise
