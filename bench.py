@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA fwd tokens/sec at H=32, D=128 bf16; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E peak
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak
-UNIT_BYTES = 14848           # workspace bytes per (chunk, head) unit, bf16 path
+UNIT_BYTES = 18944           # workspace bytes per (chunk, head) unit, bf16 path
 KET_BYTES = 4096             # K_end in K_b order per unit, look-ahead recurrence only
 LOOK_MAX_PAIRS = 96          # fewer (sequence, head) pairs: look-ahead recurrence
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -48,7 +48,7 @@ def algorithmic_work(w, bf16_resident_state=False):
 
     Per (chunk, head) unit, 16 token rows of 128 channels:
       chunk-parallel kernel: reads q, k, g_raw (3 x 256 B per token-head) and
-        beta_raw (2 B per token-head), writes one 14848 B workspace unit;
+        beta_raw (2 B per token-head), writes one 18944 B workspace unit;
       recurrence kernel: reads the unit and v (256 B per token-head), writes o
         (256 B per token-head); per (sequence, head) it reads the 64 KiB fp32
         initial state (when given) and writes the 64 KiB final state;

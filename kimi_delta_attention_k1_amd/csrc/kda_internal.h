@@ -24,11 +24,14 @@ constexpr float kL2Eps = 1e-6f;  // L2-norm epsilon: x / sqrt(sum x^2 + eps)
 // the chunk-parallel kernel hands the recurrence kernel; the chunks of one
 // (sequence, head) are therefore contiguous.
 //
-// bf16 path unit (14848 B), every block in the lane order the recurrence
+// bf16 path unit (18944 B), every block in the lane order the recurrence
 // kernel's matrix-core instructions consume (64 lanes x 16 B per 1 KB slab):
 //   KB   4096  K_b  = khat * exp(G_i)           bf16, 16x16x32 A-operand order
 //   QB   4096  Q_b  = s qhat * exp(G_i)         bf16, same order
-//   KE   4096  K_end= khat * exp(G_last - G_i)  bf16, 16x16x16 A-operand order
+//   KE   8192  K_end= khat * exp(G_last - G_i)  as a bf16 hi/lo pair, 2 KB per tile pair
+//              p: lane L's 32 bytes are tile 2p's four tokens' hi values, then their lo
+//              values, then tile 2p+1's (16x16x16 A-operand order for each half, so 16
+//              bytes form a 16x16x32 operand [hi | lo])
 //   AB   1024  (A^kk Diag(beta))^T  split into bf16 hi/lo: lane-major {hi x4, lo x4}
 //   AQ   1024  (A^qk)^T             split into bf16 hi/lo: lane-major {hi x4, lo x4}
 //   GM    512  gamma = exp(G_last)              fp32 [128]
@@ -41,7 +44,7 @@ constexpr size_t kHeaderBytes = 128;
 struct UnitLayout {
     size_t kb, qb, ke, ab, aq, gm, bytes;
 };
-constexpr UnitLayout kUnitBf16 = {0, 4096, 8192, 12288, 13312, 14336, 14848};
+constexpr UnitLayout kUnitBf16 = {0, 4096, 8192, 16384, 17408, 18432, 18944};
 constexpr UnitLayout kUnitF32 = {0, 8192, 16384, 24576, 25600, 26624, 27136};
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
     const uint16_t *__restrict__ braw, const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off,
     int N, int H, int64_t n_c_max, float lb, float scale, char *__restrict__ units, char *__restrict__ ket)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t sKE[kK1MaxWaves][kD][kC];  // K_end as [channel][token]
+    __shared__ __attribute__((aligned(16))) uint16_t sKE[kK1MaxWaves][2][kD][kC];  // K_end hi, lo as [channel][token]
     // each lane's own K_end values in K_b order (4 destination lanes x 8 elements)
     __shared__ __attribute__((aligned(16))) uint16_t sKT[KET ? kK1MaxWaves : 1][64][32];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -158,8 +158,15 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
             const float dn = __builtin_amdgcn_exp2f(gref - gf[i]);
             const float cl = row_bcast<15>(up);  // e^{G_last - Gref} for this channel
             // K_end = khat e^{G_last - G} = khat e^{Gref - G} e^{G_last - Gref}, to LDS as [channel][token]
-            const uint16_t keb = __builtin_bit_cast(uint16_t, (__bf16)(kf[i] * dn * cl));
-            sKE[wv][32 * g + i][tok] = keb;
+            // as a bf16 hi/lo pair (about 16 bits): the update adds K_end^T E into the state
+            // every chunk, and one bf16 K_end leaves a 2^-9 relative error per chunk in state
+            // directions that later keys never overwrite when keys stay correlated and
+            // gates barely decay
+            const float ke = kf[i] * dn * cl;
+            const __bf16 keh = (__bf16)ke;
+            const uint16_t keb = __builtin_bit_cast(uint16_t, keh);
+            sKE[wv][0][32 * g + i][tok] = keb;
+            sKE[wv][1][32 * g + i][tok] = __builtin_bit_cast(uint16_t, (__bf16)(ke - (float)keh));
             if constexpr (KET) sKT[wv][lane][((i & 15) >> 2) * 8 + (i & 3) + 4 * (i >> 4)] = keb;
             const float kr = kf[i] * up, ki = kf[i] * dn, qr = qf[i] * up;
             kr_h[e] = (__bf16)kr;
@@ -243,11 +250,14 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        // lane (kc = tok, g): tiles 2p and 2p+1, channel 32p + kc (+16), tokens 4g..4g+3
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(&sKE[wv][32 * p + tok][4 * g]);
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(&sKE[wv][32 * p + 16 + tok][4 * g]);
-        const u32x4 x = {lo[0], lo[1], hi[0], hi[1]};
-        reinterpret_cast<u32x4 *>(u + kUnitBf16.ke + p * 1024)[lane] = x;
+        // lane (kc = tok, g): tiles 2p and 2p+1 (channels 32p + kc and 32p + 16 + kc),
+        // tokens 4g..4g+3, each tile's hi values then its lo values
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const u32x2 h2 = *reinterpret_cast<const u32x2 *>(&sKE[wv][0][32 * p + 16 * tt + tok][4 * g]);
+            const u32x2 l2 = *reinterpret_cast<const u32x2 *>(&sKE[wv][1][32 * p + 16 * tt + tok][4 * g]);
+            reinterpret_cast<u32x4 *>(u + kUnitBf16.ke + p * 2048)[2 * lane + tt] = u32x4{h2[0], h2[1], l2[0], l2[1]};
+        }
     }
     if constexpr (KET) {
         // lane (tok, g) owns k step g; its element group gp goes to destination lane tok + 16 gp
@@ -266,14 +276,14 @@ __global__ __launch_bounds__(64 * kK1MaxWaves) void k1_mfma(
 // value channels evolve independently, so consumers never exchange state; they
 // share each chunk's operands through LDS.
 //
-// The producers copy every chunk's 14848-byte workspace unit and the v rows of the
+// The producers copy every chunk's 18944-byte workspace unit and the v rows of the
 // workgroup's value columns straight from global memory into a ring of LDS slots
 // with 16-byte-per-lane global-to-LDS loads, several chunks ahead, and wait with
 // explicit counts of their own loads. One workgroup barrier per chunk publishes a
 // slot and recycles the previous one. The barrier is a bare s_barrier: a fenced
 // barrier would drain the prefetch queue every chunk.
 // ---------------------------------------------------------------------------
-constexpr int kVOff = 15 * 1024;  // v rows offset inside a slot
+constexpr int kVOff = 19 * 1024;  // v rows offset inside a slot
 static_assert(kUnitBf16.bytes <= (size_t)kVOff, "unit must fit below the v rows");
 
 // Workgroup shape for CONS consumer waves (8 / CONS workgroups per (sequence, head)).
@@ -290,7 +300,7 @@ template <int CONS> struct K2Shape {
     static constexpr int v_kb = CONS >= 2 ? CONS / 2 : 1;
     static constexpr int slot_kb = (kVOff / 1024 + v_kb + producers - 1) / producers * producers;
     static constexpr int slot_bytes = slot_kb * 1024;
-    static constexpr int slots = producers == 2 ? 6 : 8;
+    static constexpr int slots = producers == 2 ? 6 : 7;
     static constexpr int threads = 64 * (consumers + producers);
     static constexpr int kb_per_producer = slot_kb / producers;
     // chunks copied ahead of the recurrence: an output wave still reads the slot
@@ -409,19 +419,16 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                 }
             }
         };
-        // S^T <- Diag(gamma) S^T + K_end^T (E_hi + E_lo): [K_end | K_end] x [E_hi ; E_lo].
-        auto update = [&](const char *L, bf16x8 e_hl) {
+        // S^T <- Diag(gamma) S^T + K_end^T E, K_end = hi + lo and E = E_hi + E_lo:
+        // [hi | lo] x [E_hi ; E_hi] + [hi | lo] x [E_lo ; E_lo], two 16x16x32 products
+        auto update = [&](const char *L, bf16x4 e_h, bf16x4 e_l) {
+            const bf16x8 ehh = cat8(e_h, e_h), ell = cat8(e_l, e_l);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const u32x4 kq = *reinterpret_cast<const u32x4 *>(L + kUnitBf16.ke + p * 1024 + lane * 16);
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int t = 2 * p + hh;
-                    const bf16x4 kt = __builtin_bit_cast(bf16x4, hh ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]});
-                    const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kUnitBf16.gm + (16 * t + 4 * g) * 4);
-                    st[t] = mma32(cat8(kt, kt), e_hl, st[t] * gm);
-                    if constexpr (RS) st[t] = round_bf16x4(st[t]);
-                }
+            for (int t = 0; t < 8; ++t) {
+                const bf16x8 k8 = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.ke + (t >> 1) * 2048 + lane * 32 + (t & 1) * 16);
+                const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kUnitBf16.gm + (16 * t + 4 * g) * 4);
+                st[t] = mma32(k8, ell, mma32(k8, ehh, st[t] * gm));
+                if constexpr (RS) st[t] = round_bf16x4(st[t]);
             }
         };
         if (!out_wave) {
@@ -455,12 +462,11 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                 E = mma32(ab, cat8(eb_h, eb_h), E);
                 E = mma32(ab, cat8(eb_l, eb_l), E);
                 split4(E, e_h, e_l);
-                const bf16x8 e_hl = cat8(e_h, e_l);
                 // the output wave gets E in fp32 and splits it itself (a variant that handed
                 // over the bf16 hi/lo registers gave wrong outputs; it chained products of
                 // two shapes, which the note at mma16 explains)
                 ebuf[j & 1][wc][lane] = E;
-                update(L, e_hl);
+                update(L, e_h, e_l);
                 // the E tile is in LDS before the barrier publishes it
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 bar_sync();
@@ -488,7 +494,6 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                 }
                 bf16x4 e_h, e_l;
                 split4(ebuf[c & 1][wc][lane], e_h, e_l);
-                const bf16x8 e_hl = cat8(e_h, e_l);
                 // O = Q_b S^T + A^qk E
                 const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.aq + lane * 16);
                 f32x4 O = mma32(aq, cat8(e_h, e_h), xq);
@@ -503,7 +508,7 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
                     for (int r = 0; r < 4; ++r)
                         if (4 * g + r < len) orow[r * rstride] = __builtin_bit_cast(uint16_t, (__bf16)O[r]);
                 }
-                if (upd) update(L, e_hl);
+                if (upd) update(L, e_h, e_l);
             };
 #pragma unroll 1
             for (int j = 0; j < nch; ++j) {
@@ -573,19 +578,15 @@ __global__ __launch_bounds__(K2Shape<CONS>::threads) void k2_mfma(
             for (int r = 0; r < 4; ++r)
                 if (4 * g + r < len) orow[r * rstride] = __builtin_bit_cast(uint16_t, (__bf16)O[r]);
         }
-        // S^T <- Diag(gamma) S^T + K_end^T (E_hi + E_lo): [K_end | K_end] x [E_hi ; E_lo]
-        const bf16x8 e_hl = cat8(e_h, e_l);
+        // S^T <- Diag(gamma) S^T + K_end^T E, K_end = hi + lo and E = E_hi + E_lo:
+        // [hi | lo] x [E_hi ; E_hi] + [hi | lo] x [E_lo ; E_lo]
+        const bf16x8 ehh = cat8(e_h, e_h), ell = cat8(e_l, e_l);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const u32x4 kq = *reinterpret_cast<const u32x4 *>(L + kUnitBf16.ke + p * 1024 + lane * 16);
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int t = 2 * p + hh;
-                const bf16x4 kt = __builtin_bit_cast(bf16x4, hh ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]});
-                const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kUnitBf16.gm + (16 * t + 4 * g) * 4);
-                st[t] = mma32(cat8(kt, kt), e_hl, st[t] * gm);
-                if constexpr (RS) st[t] = round_bf16x4(st[t]);
-            }
+        for (int t = 0; t < 8; ++t) {
+            const bf16x8 k8 = *reinterpret_cast<const bf16x8 *>(L + kUnitBf16.ke + (t >> 1) * 2048 + lane * 32 + (t & 1) * 16);
+            const f32x4 gm = *reinterpret_cast<const f32x4 *>(L + kUnitBf16.gm + (16 * t + 4 * g) * 4);
+            st[t] = mma32(k8, ell, mma32(k8, ehh, st[t] * gm));
+            if constexpr (RS) st[t] = round_bf16x4(st[t]);
         }
         // this wave's reads of the slot are complete before it may be refilled
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -619,9 +620,9 @@ template <int CONS> struct KLShape {
     static constexpr int producers = 4;
     static constexpr int unit_kb = kVOff / 1024;                  // unit, then K_end in K_b order
     static constexpr int v_kb = 1;                                // v rows of 16 CONS columns
-    static constexpr int slot_kb = unit_kb + 4 + v_kb;            // 20
+    static constexpr int slot_kb = unit_kb + 4 + v_kb;            // 24
     static constexpr int slot_bytes = slot_kb * 1024;
-    static constexpr int slots = CONS == 1 ? 7 : 6;
+    static constexpr int slots = CONS == 1 ? 6 : 5;
     static constexpr int consumers = 4 * CONS;
     static constexpr int threads = 64 * (consumers + producers);
     static constexpr int kb_per_producer = slot_kb / producers;
@@ -783,16 +784,14 @@ __global__ __launch_bounds__(KLShape<CONS>::threads) void k2_look(
             const char *Lp = lds[cp % Sh::slots];
             bf16x4 e_h, e_l;
             split4(ebuf[cp & 1][wc][lane], e_h, e_l);
-            const bf16x8 e_hl = cat8(e_h, e_l);
+            const bf16x8 ehh = cat8(e_h, e_h), ell = cat8(e_l, e_l);
+            // K_end = hi + lo: [hi | lo] x [E_hi ; E_hi] + [hi | lo] x [E_lo ; E_lo]
 #pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-                const u32x4 kq = *reinterpret_cast<const u32x4 *>(Lp + kUnitBf16.ke + (2 * i + pp) * 1024 + lane * 16);
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int t = 2 * pp + hh;
-                    const bf16x4 kt = __builtin_bit_cast(bf16x4, hh ? u32x2{kq[2], kq[3]} : u32x2{kq[0], kq[1]});
-                    st[t] = mma32(cat8(kt, kt), e_hl, dec[t]);
-                }
+            for (int t = 0; t < 4; ++t) {
+                const int tg = 4 * i + t;  // the state tile of this wave's keys
+                const bf16x8 k8 =
+                    *reinterpret_cast<const bf16x8 *>(Lp + kUnitBf16.ke + (tg >> 1) * 2048 + lane * 32 + (tg & 1) * 16);
+                st[t] = mma32(k8, ell, mma32(k8, ehh, dec[t]));
             }
         };
 #pragma unroll 1

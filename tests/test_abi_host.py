@@ -64,16 +64,16 @@ def _layout(N, H, n_c, unit, look=False):
 def test_workspace_size_arithmetic(lib):
     # batch mode, one sequence of 64 tokens -> 4 chunks
     assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32) == _layout(1, 1, 4, 27136)
-    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_BF16) == _layout(1, 1, 4, 14848, look=True)
+    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_BF16) == _layout(1, 1, 4, 18944, look=True)
     # batch of 2 rows of 17 tokens -> 2 x 2 chunks
-    assert kda.workspace_size(2, 17, 2, 3) == _layout(2, 3, 4, 14848, look=True)
+    assert kda.workspace_size(2, 17, 2, 3) == _layout(2, 3, 4, 18944, look=True)
     # 95 pairs still take the look-ahead recurrence, 96 do not
-    assert kda.workspace_size(1, 160, 5, 19) == _layout(5, 19, (160 + 15 * 5) // 16, 14848, look=True)
-    assert kda.workspace_size(1, 160, 6, 16) == _layout(6, 16, (160 + 15 * 6) // 16, 14848)
+    assert kda.workspace_size(1, 160, 5, 19) == _layout(5, 19, (160 + 15 * 5) // 16, 18944, look=True)
+    assert kda.workspace_size(1, 160, 6, 16) == _layout(6, 16, (160 + 15 * 6) // 16, 18944)
     # the bf16-resident-state variant keeps the plain recurrence
-    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_BF16, bf16_resident_state=True) == _layout(1, 1, 4, 14848)
+    assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_BF16, bf16_resident_state=True) == _layout(1, 1, 4, 18944)
     # packed: 8 x 8192 tokens (bound (T + 15 N) / 16)
-    assert kda.workspace_size(1, 65536, 8, 32) == _layout(8, 32, (65536 + 15 * 8) // 16, 14848)
+    assert kda.workspace_size(1, 65536, 8, 32) == _layout(8, 32, (65536 + 15 * 8) // 16, 18944)
     # fp32 compute flag selects the fp32 unit size
     assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_BF16, fp32_compute=True) == _layout(1, 1, 4, 27136)
     # invalid descriptions report 0
@@ -186,13 +186,13 @@ def test_null_desc(lib):
 def test_path_flags_and_workspace(lib):
     # the single pass needs only the chunk map; without its flag the size covers the split path
     # ... plus the longest-first order of the sequences, [N] int32
-    fused = (_layout(8, 32, 0, 14848) + 4 * 8 + 127) // 128 * 128
+    fused = (_layout(8, 32, 0, 18944) + 4 * 8 + 127) // 128 * 128
     assert kda.workspace_size(1, 65536, 8, 32, path="fused") == fused
     assert kda.workspace_size(1, 65536, 8, 32, path="split") == kda.workspace_size(1, 65536, 8, 32)
-    assert kda.workspace_size(1, 65536, 8, 32, path="auto") == _layout(8, 32, (65536 + 15 * 8) // 16, 14848)
+    assert kda.workspace_size(1, 65536, 8, 32, path="auto") == _layout(8, 32, (65536 + 15 * 8) // 16, 18944)
     assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32, path="fused") == 0  # invalid: fp32 I/O
     # the token-by-token path also needs only the chunk map, for any dtype
-    assert kda.workspace_size(1, 65536, 8, 32, path="recurrent") == _layout(8, 32, 0, 14848)
+    assert kda.workspace_size(1, 65536, 8, 32, path="recurrent") == _layout(8, 32, 0, 18944)
     assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32, path="recurrent") == _layout(1, 1, 0, 27136)
     with pytest.raises(ValueError):
         kda.workspace_size(1, 64, 1, 1, path="both")
@@ -216,15 +216,15 @@ def test_segmented_path_workspace(lib):
     # C4: one sequence of 131072 tokens, H=32 -> 8192 chunks: segments of 1446 chunks, then 964
     assert kda.workspace_size(1, 131072, 1, 32, path="segmented") == _seg_layout(1, 32, 131072, 8192)
     # the automatic rule picks the segmented pass there; the size covers it and the split path
-    split = _layout(1, 32, 8192, 14848, look=True)
+    split = _layout(1, 32, 8192, 18944, look=True)
     assert kda.workspace_size(1, 131072, 1, 32) == max(split, _seg_layout(1, 32, 131072, 8192))
     # packed few-pair batch: n_c bound (T + 15 N) / 16
     n_c = (5000 + 15 * 3) // 16
     assert kda.workspace_size(1, 5000, 3, 2, path="segmented") == _seg_layout(3, 2, 5000, n_c)
     # 256 pairs: no segments needed, the size is the split path's
-    assert kda.workspace_size(1, 65536, 8, 32) == _layout(8, 32, (65536 + 15 * 8) // 16, 14848)
+    assert kda.workspace_size(1, 65536, 8, 32) == _layout(8, 32, (65536 + 15 * 8) // 16, 18944)
     # 32 pairs of 64 chunks: below the 128-chunk average the rule keeps the split path
-    assert kda.workspace_size(2, 1024, 2, 16) == _layout(2, 16, 128, 14848, look=True)
+    assert kda.workspace_size(2, 1024, 2, 16) == _layout(2, 16, 128, 18944, look=True)
     assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32, path="segmented") == 0  # invalid: fp32 I/O
 
 

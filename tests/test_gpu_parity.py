@@ -226,11 +226,14 @@ def test_guard_bytes_untouched(gpu):
 
 # ------------------------------------------------------------------ K1 intermediates
 def _decode_unit(raw: torch.Tensor):
-    """Unpack one bf16-path workspace unit (14848 bytes) into row-major tiles.
-    The fragment order is the recurrence kernel's matrix-core operand order."""
+    """Unpack one bf16-path workspace unit (18944 bytes) into row-major tiles.
+    The fragment order is the recurrence kernel's matrix-core operand order; K_end
+    is a bf16 hi/lo pair (2 KB per tile pair; per lane: tile 2p hi, lo, tile 2p+1 hi,
+    lo, four tokens each)."""
     u = raw.cpu()
     bf = lambda a, b: u[a:b].view(torch.bfloat16).float().view(4, 64, 8)  # noqa: E731
-    KB, QB, KE = bf(0, 4096), bf(4096, 8192), bf(8192, 12288)
+    KB, QB = bf(0, 4096), bf(4096, 8192)
+    KE = u[8192:16384].view(torch.bfloat16).float().view(4, 64, 2, 2, 4)  # pair, lane, tile, hi/lo, token
     kb = torch.zeros(16, 128)
     qb = torch.zeros(16, 128)
     ke = torch.zeros(16, 128)
@@ -241,19 +244,19 @@ def _decode_unit(raw: torch.Tensor):
                 ch = 32 * p + (4 * g + e if e < 4 else 16 + 4 * g + e - 4)
                 kb[t, ch] = KB[p, lane, e]
                 qb[t, ch] = QB[p, lane, e]
-                tok = 4 * g + (e % 4)
-                kch = 32 * p + t + (16 if e >= 4 else 0)
-                ke[tok, kch] = KE[p, lane, e]
+            for tt in range(2):
+                for e in range(4):
+                    ke[4 * g + e, 32 * p + 16 * tt + t] = KE[p, lane, tt, 0, e] + KE[p, lane, tt, 1, e]
     hl = lambda a, b: u[a:b].view(torch.bfloat16).float().view(64, 2, 4).sum(1)  # noqa: E731  hi + lo
-    ab = hl(12288, 13312)
-    aq = hl(13312, 14336)
+    ab = hl(16384, 17408)
+    aq = hl(17408, 18432)
     AB = torch.zeros(16, 16)
     AQ = torch.zeros(16, 16)
     for lane in range(64):
         for r in range(4):
             AB[lane % 16, 4 * (lane // 16) + r] = ab[lane, r]
             AQ[lane % 16, 4 * (lane // 16) + r] = aq[lane, r]
-    gm = u[14336:14848].view(torch.float32).clone()
+    gm = u[18432:18944].view(torch.float32).clone()
     return dict(Kb=kb, Qb=qb, Kend=ke, Ab=AB, Aqk=AQ, gamma=gm)
 
 
@@ -276,11 +279,14 @@ def test_k1_intermediates_against_chunked_oracle(gpu):
             for h in range(H):
                 it = inter[(n, h)][j]
                 L = it["Kb"].shape[0]
-                base = units + (h * n_c_max + chunk) * 14848
-                d = _decode_unit(ws[base:base + 14848])
-                for key, ref in (("Kb", it["Kb"]), ("Qb", s * it["Qbnd"]), ("Kend", it["Kend"])):
+                base = units + (h * n_c_max + chunk) * 18944
+                d = _decode_unit(ws[base:base + 18944])
+                # K_b and Q_b are one bf16 (2^-9 relative); K_end is a hi/lo pair, so it meets
+                # 2^-13, which one bf16 cannot
+                for key, ref, rel in (("Kb", it["Kb"], 2 ** -8), ("Qb", s * it["Qbnd"], 2 ** -8),
+                                      ("Kend", it["Kend"], 2 ** -13)):
                     got = d[key][:L].numpy()
-                    assert np.all(np.abs(got - ref) <= 2 ** -8 * np.abs(ref) + 1e-30), key
+                    assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-30), key
                     assert torch.all(d[key][L:] == 0), key + " padded rows"
                 ab_ref = it["Akk"] * it["beta"][None, :]
                 assert np.max(np.abs(d["Ab"][:L, :L].numpy() - ab_ref)) <= 1e-4 * np.max(np.abs(ab_ref))
