@@ -93,13 +93,7 @@ enum {
      * kda_fwd_prepare + kda_fwd_recur run. With fewer than 96 (sequence, head)
      * pairs (and without KDA_FLAG_BF16_RESIDENT_STATE) the recurrence runs in
      * look-ahead form and the workspace also holds 4096 B per (chunk, head);
-     * kda_fwd_workspace_size accounts for it. Accuracy limit: this path keeps
-     * the state-update key operand K_end = khat e^{G_last - G} in one bf16, so
-     * keys that stay strongly correlated over hundreds of tokens (cosine 0.96
-     * and above between all keys of a head) with little or no decay can exceed
-     * the bf16 bound on the final state (measured 2.1x at cosine 0.96 over 512
-     * tokens with lower_bound 0 and beta 1); the single-pass and segmented
-     * paths stay within it there (KDA_FLAG_FUSED, KDA_FLAG_SEGMENTED). */
+     * kda_fwd_workspace_size accounts for it. */
     KDA_FLAG_SPLIT = 2u,
     /* bf16-compute kda_fwd: run the single-pass kernel (one workgroup per
      * (sequence, head) prepares each chunk in on-chip memory and runs the
@@ -156,8 +150,8 @@ enum {
  * sequences average at least KDA_SEGMENTED_MIN_AVG_CHUNKS 16-token chunks
  * (chunk bound / num_seqs), else the single-pass kernel when
  * num_seqs * num_heads >= KDA_FUSED_MIN_PAIRS or the sequences average at
- * most KDA_FUSED_MAX_AVG_CHUNKS chunks, and the two-kernel path otherwise
- * (see KDA_FLAG_SPLIT for its accuracy limit); fp32 compute uses
+ * most KDA_FUSED_MAX_AVG_CHUNKS chunks, and the two-kernel path otherwise;
+ * fp32 compute uses
  * the fp32 two-kernel path. The thresholds are where each path measured
  * fastest on MI355X. The paths evaluate the same chunkwise equations and
  * agree to bf16 rounding; they are not bitwise identical (the single pass
@@ -166,7 +160,7 @@ enum {
 #define KDA_FUSED_MIN_PAIRS 96
 #define KDA_FUSED_MAX_AVG_CHUNKS 8
 #define KDA_SEGMENTED_MAX_PAIRS 128
-#define KDA_SEGMENTED_MIN_AVG_CHUNKS 128
+#define KDA_SEGMENTED_MIN_AVG_CHUNKS 96
 #define KDA_RECURRENT_MAX_AVG_TOKENS 4
 
 /*

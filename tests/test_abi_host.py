@@ -223,7 +223,7 @@ def test_segmented_path_workspace(lib):
     assert kda.workspace_size(1, 5000, 3, 2, path="segmented") == _seg_layout(3, 2, 5000, n_c)
     # 256 pairs: no segments needed, the size is the split path's
     assert kda.workspace_size(1, 65536, 8, 32) == _layout(8, 32, (65536 + 15 * 8) // 16, 18944)
-    # 32 pairs of 64 chunks: below the 128-chunk average the rule keeps the split path
+    # 32 pairs of 64 chunks: below the 96-chunk average the rule keeps the split path
     assert kda.workspace_size(2, 1024, 2, 16) == _layout(2, 16, 128, 18944, look=True)
     assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32, path="segmented") == 0  # invalid: fp32 I/O
 
