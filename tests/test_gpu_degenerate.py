@@ -116,3 +116,16 @@ def test_correlated_keys_without_decay(gpu, path, case):
     o, s = run_gpu(w, gpu, path=path)
     assert torch.isfinite(o.float()).all() and torch.isfinite(s.float()).all()
     compare(w, o, s, run_oracle(w), bf16_tol, f"correlated keys {case} {path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_correlated_keys_over_long_sequences(gpu, path):
+    """Keys with cosine ~0.96 over 512-token sequences, beta = 1 and no decay
+    (lower_bound 0): the state-update key operand K_end is rounded every chunk into
+    state directions that later keys never overwrite, which a one-bf16 K_end turned
+    into twice the bound on the final state; every path keeps it as a hi/lo pair."""
+    _banner(f"correlated keys over 512-token sequences, no decay, {path}")
+    w = workloads.make([512, 512, 300], 2, seed=88, init_std=0.02, beta_mean=1.0, lower_bound=0.0)
+    w = _with(w, k=_correlated_keys(w, 0.2, 89), beta_raw=torch.full_like(w.beta_raw, float("inf")))
+    o, s = run_gpu(w, gpu, path=path)
+    compare(w, o, s, run_oracle(w), bf16_tol, f"correlated keys 512 tokens {path}")
