@@ -123,7 +123,7 @@ extern "C" size_t kda_fwd_workspace_size(const kda_desc_t *desc)
             if (bf > b) b = bf;
         }
         if (s.path == kSeg) {
-            const size_t bs = kda::ws_layout_seg(desc->num_seqs, desc->num_heads, s.n_c_max, s.T_tot).total;
+            const size_t bs = kda::ws_layout_seg(desc->num_seqs, desc->num_heads, s.n_c_max).total;
             if (bs > b) b = bs;
         }
         if (b > best) best = b;
@@ -175,7 +175,7 @@ kda_status_t run(const void *q, const void *k, const void *v, const void *g_raw,
     if (!workspace) return KDA_ERR_WORKSPACE;
     const bool look =
         !no_units && kda::use_lookahead(N, H, s.f32_path, (desc->flags & KDA_FLAG_BF16_RESIDENT_STATE) != 0);
-    const WsLayout lay = path == kSeg     ? kda::ws_layout_seg(N, H, s.n_c_max, s.T_tot)
+    const WsLayout lay = path == kSeg     ? kda::ws_layout_seg(N, H, s.n_c_max)
                          : path == kFused ? kda::ws_layout_fused(N, H)
                                           : kda::ws_layout(N, H, no_units ? 0 : s.n_c_max, s.f32_path, look);
     if (workspace_bytes < lay.total || !aligned(workspace, KDA_WORKSPACE_ALIGN)) return KDA_ERR_WORKSPACE;

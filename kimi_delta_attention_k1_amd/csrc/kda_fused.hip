@@ -155,13 +155,13 @@ __global__ __launch_bounds__(f_threads<SEG>()) void kf_fused(
     // the address arithmetic built on it stay in scalar registers
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = blockIdx.x % H;
-    int n, nch, tb, seg = 0, gseg = 0;
+    int n, nch, tb, seg = 0, gseg = 0, cs = 0;  // cs: the segment's first chunk in its sequence
     if constexpr (SEG) {
         seg = blockIdx.x / H;
         if (seg >= seg_off[N]) return;  // past the last segment: uniform, before any barrier
         n = find_seq(seg_off, N, seg);
         gseg = seg - seg_off[n];
-        const int cs = seg_start(gseg, seg_len, seg_first);
+        cs = seg_start(gseg, seg_len, seg_first);
         nch = min(gseg == 0 ? seg_first : seg_len, chunk_off[n + 1] - chunk_off[n] - cs);
         tb = tok_off[n] + cs * kC;
     } else {
@@ -555,7 +555,6 @@ __global__ __launch_bounds__(f_threads<SEG>()) void kf_fused(
 #pragma unroll
             for (int t = 0; t < 8; ++t) st[u][t] = ld_state4(s0 + sbase + (int64_t)16 * kD * u + 16 * t);
     }
-    uint16_t *const obuf = MODE == 2 ? ybuf : out;
     if (ticks > 0) bar_sync();  // start: the stage-A waves have waited for chunk 0 in their rings
 #pragma unroll 1
     for (int tau = 0; tau < ticks; ++tau) {
@@ -628,7 +627,8 @@ __global__ __launch_bounds__(f_threads<SEG>()) void kf_fused(
             const bf16x4 aq_h = {aq[0], aq[1], aq[2], aq[3]}, aq_l = {aq[4], aq[5], aq[6], aq[7]};
             bf16x4 eh[2], el[2];
             // output row of this lane's token: value channels 32w + 16u + 4g .. +3 of tile u
-            uint16_t *orow = obuf + ((int64_t)(t0 + col) * H + h) * kD + 32 * cw + 4 * g;
+            uint16_t *orow = out + ((int64_t)(t0 + col) * H + h) * kD + 32 * cw + 4 * g;
+            u32x4 yv;  // MODE 2: y of this lane's token, both column tiles
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int vcol = 32 * cw + 16 * u + col;
@@ -662,7 +662,19 @@ __global__ __launch_bounds__(f_threads<SEG>()) void kf_fused(
                 O = mma16(e_h, aq_l, O);
                 O = mma16(e_l, aq_h, O);
                 const u32x2 ob = {pk_bf16(f32x2{O[0], O[1]}), pk_bf16(f32x2{O[2], O[3]})};
-                if (col < len) *reinterpret_cast<u32x2 *>(orow + 16 * u) = ob;
+                if constexpr (MODE == 2) {
+                    yv[2 * u] = ob[0];
+                    yv[2 * u + 1] = ob[1];
+                } else if (col < len) {
+                    *reinterpret_cast<u32x2 *>(orow + 16 * u) = ob;
+                }
+            }
+            if constexpr (MODE == 2) {
+                // the chunk's y tile: k step cw of the correction's operand, lane (token col,
+                // group g) holding channels 32 cw + 4 g + (0..3) and 32 cw + 16 + 4 g + (0..3);
+                // rows past the end are stored too and never used
+                const int64_t tile = (int64_t)(chunk_off[n] + cs + c) * H + h;
+                *reinterpret_cast<u32x4 *>(ybuf + (tile * kFCons + cw) * (64 * 8) + lane * 8) = yv;
             }
             // S^T <- Diag(gamma) S^T + K_end^T E', K_end = hi + lo and E' = eh + el:
             // [hi | lo] against [eh; eh] in one 16x16x32 product, then hi against el in a

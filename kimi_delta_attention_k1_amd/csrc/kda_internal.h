@@ -69,7 +69,10 @@ inline bool use_lookahead(int64_t N, int64_t H, bool f32_path, bool bf16_residen
 //   sfin    [seg_max][H][128][128]  fp32, segment's final state from S = 0 (seg 0: S_0)
 //   phi     [seg_max][H][128][128]  fp32, segment's key-space transfer
 //   sin     [seg_max][H][128][128]  fp32, true state entering the segment
-//   ybuf    [T_tot][H][128]         bf16, y_t = Phi_t (s qhat_t) within the segment
+//   ybuf    [n_c_max][H][4][64][8]  bf16, y_t = Phi_t (s qhat_t) within the segment: one
+//                                   4 KB tile per (chunk, head) in the order the correction's
+//                                   matrix-core operand takes it (k step, lane, 8 channels),
+//                                   so each of its loads reads 1 KB in one piece
 constexpr int64_t kSegTargetGroups = 256;
 constexpr int64_t kSegMinChunks = 16;
 inline int64_t seg_first_for(int64_t seg_len) { return seg_len + (seg_len + 1) / 2; }
@@ -131,7 +134,7 @@ inline WsLayout ws_layout_fused(int64_t N, int64_t H)
 }
 
 // layout of the segmented single pass (no units)
-inline WsLayout ws_layout_seg(int64_t N, int64_t H, int64_t n_c_max, int64_t T_tot)
+inline WsLayout ws_layout_seg(int64_t N, int64_t H, int64_t n_c_max)
 {
     WsLayout L = ws_layout(N, H, 0, false, false);
     L.n_c_max = n_c_max;
@@ -144,7 +147,7 @@ inline WsLayout ws_layout_seg(int64_t N, int64_t H, int64_t n_c_max, int64_t T_t
     L.phi = L.sfin + st;
     L.sin = L.phi + st;
     L.ybuf = L.sin + st;
-    L.total = L.ybuf + (size_t)T_tot * (size_t)H * kD * sizeof(uint16_t);
+    L.total = L.ybuf + (size_t)n_c_max * (size_t)H * kC * kD * sizeof(uint16_t);
     return L;
 }
 

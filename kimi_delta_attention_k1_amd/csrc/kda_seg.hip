@@ -147,17 +147,22 @@ constexpr int kCorrLd = kD + 8;            // padded LDS row (bf16): rows 4 bank
 // 2p and 2p + 1 then hold channels 32p + 8g + (0..3) and (4..7) in lane group g, so a
 // lane reads and writes eight consecutive output channels (16 bytes) at once.
 __device__ __forceinline__ int corr_row(int r) { return (r & ~31) + 16 * ((r >> 2) & 1) + 4 * ((r >> 3) & 3) + (r & 3); }
+// LDS column of key channel c = 32 ks + 16 u + 4 g + i: column 32 ks + 8 g + 4 u + i, the
+// order in which the single pass stores a y tile (lane group g of k step ks holds
+// channels 32 ks + 4 g + (0..3), then 32 ks + 16 + 4 g + (0..3))
+__device__ __forceinline__ int corr_col(int c) { return (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3); }
 
 // o_t += S_in y_t for every segment after the first. Workgroup (segment, head, j)
 // splits S_in once into bf16 hi and lo halves in LDS, then walks the segment's
-// token blocks j, j + gridDim.y, ... of 256 tokens: wave w takes 32 tokens and
-// forms (S_in y^T) for them as 16x16 tiles (rows: value channels in the order
-// corr_row gives, columns: tokens), so each lane ends with eight consecutive value
-// channels of one token.
+// token blocks j, j + gridDim.y, ... of 256 tokens: wave w takes 32 tokens (two
+// chunks) and forms (S_in y^T) for them as 16x16 tiles (rows: value channels in the
+// order corr_row gives, columns: tokens), so each lane ends with eight consecutive
+// value channels of one token. The y of a chunk is one 4 KB tile in operand order.
 __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__restrict__ out,
                                                                  const uint16_t *__restrict__ ybuf,
                                                                  const float *__restrict__ sin,
                                                                  const int32_t *__restrict__ tok_off,
+                                                                 const int32_t *__restrict__ chunk_off,
                                                                  const int32_t *__restrict__ seg_off, int N, int H,
                                                                  int seg_len, int seg_first)
 {
@@ -188,8 +193,8 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
         const u32x2 hi = {__builtin_amdgcn_perm(u[1], u[0], 0x07060302u), __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
         const f32x2 r01 = {x[0] - __uint_as_float(u[0] & 0xffff0000u), x[1] - __uint_as_float(u[1] & 0xffff0000u)};
         const f32x2 r23 = {x[2] - __uint_as_float(u[2] & 0xffff0000u), x[3] - __uint_as_float(u[3] & 0xffff0000u)};
-        *reinterpret_cast<u32x2 *>(&Shi[corr_row(r)][c]) = hi;
-        *reinterpret_cast<u32x2 *>(&Slo[corr_row(r)][c]) = u32x2{pk_bf16(r01), pk_bf16(r23)};
+        *reinterpret_cast<u32x2 *>(&Shi[corr_row(r)][corr_col(c)]) = hi;
+        *reinterpret_cast<u32x2 *>(&Slo[corr_row(r)][corr_col(c)]) = u32x2{pk_bf16(r01), pk_bf16(r23)};
     }
     __syncthreads();
 
@@ -204,13 +209,16 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
         uint16_t *orow[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const int t = tlo + 32 * w + 16 * tt + col;  // this lane's token (B column, D column)
+            const int t16 = tlo + 32 * w + 16 * tt;  // the chunk's first token
+            const int t = t16 + col;                 // this lane's token (B column, D column)
             live[tt] = t < te;
             const int tc = live[tt] ? t : tb;
-            const uint16_t *yrow = ybuf + ((int64_t)tc * H + h) * kD;
+            // the chunk's y tile (a chunk past the segment's end re-reads its first one)
+            const int ch = chunk_off[n] + ((t16 < te ? t16 : tb) - tok_off[n]) / kC;
+            const uint16_t *ytile = ybuf + ((int64_t)ch * H + h) * (kC * kD) + 8 * lane;
             orow[tt] = out + (int64_t)tc * rowst + (int64_t)h * kD;
 #pragma unroll
-            for (int ks = 0; ks < kD / 32; ++ks) yb[tt][ks] = *reinterpret_cast<const bf16x8 *>(yrow + 32 * ks + 8 * g);
+            for (int ks = 0; ks < kD / 32; ++ks) yb[tt][ks] = *reinterpret_cast<const bf16x8 *>(ytile + 64 * 8 * ks);
 #pragma unroll
             for (int p = 0; p < kD / 32; ++p) ov[tt][p] = *reinterpret_cast<const u32x4 *>(orow[tt] + 32 * p + 8 * g);
         }
@@ -277,6 +285,7 @@ template <typename TSt>
 static hipError_t launch_seg_finish_t(const Problem &p, hipStream_t s)
 {
     const int32_t *tok = reinterpret_cast<const int32_t *>(p.ws + p.lay.tok_off);
+    const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
     const int32_t *seg = reinterpret_cast<const int32_t *>(p.ws + p.lay.seg_off);
     const float *sfin = reinterpret_cast<const float *>(p.ws + p.lay.sfin);
     const float *phi = reinterpret_cast<const float *>(p.ws + p.lay.phi);
@@ -286,7 +295,7 @@ static hipError_t launch_seg_finish_t(const Problem &p, hipStream_t s)
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     const int64_t blocks = corr_blocks(p);
     hipLaunchKernelGGL(kseg_correct, dim3((unsigned)(p.lay.seg_max * p.H), (unsigned)blocks), dim3(64 * kCorrWaves),
-                       0, s, (uint16_t *)p.out, (const uint16_t *)(p.ws + p.lay.ybuf), (const float *)sin, tok, seg,
+                       0, s, (uint16_t *)p.out, (const uint16_t *)(p.ws + p.lay.ybuf), (const float *)sin, tok, chk, seg,
                        (int)p.N, p.H, (int)p.lay.seg_len, (int)p.lay.seg_first);
     return hipGetLastError();
 }
