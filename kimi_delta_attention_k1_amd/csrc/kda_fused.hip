@@ -142,7 +142,7 @@ __global__ __launch_bounds__(f_threads<SEG>()) void kf_fused(
     uint16_t *__restrict__ out, const int32_t *__restrict__ tok_off, const int32_t *__restrict__ chunk_off, int H,
     float lb, float scale, const int32_t *__restrict__ seg_off, int N, int seg_len, int seg_first,
     float *__restrict__ sfin,
-    float *__restrict__ phi, uint16_t *__restrict__ ybuf, const int32_t *__restrict__ order)
+    uint16_t *__restrict__ phi, uint16_t *__restrict__ ybuf, const int32_t *__restrict__ order)
 {
     constexpr int kPBytes = slot_bytes<CSR>();
     constexpr int NP = kFPrep, AW = kAW, NE = kNE;
@@ -705,13 +705,34 @@ __global__ __launch_bounds__(f_threads<SEG>()) void kf_fused(
 #pragma unroll
                 for (int t = 0; t < 8; ++t) st_state4(s1 + sbase + (int64_t)16 * kD * u + 16 * t, st[u][t]);
         }
-    } else {
-        float *const fin = MODE == 1 ? sfin : phi;
+    } else if constexpr (MODE == 1) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                *reinterpret_cast<f32x4 *>(fin + fbase + (int64_t)16 * kD * u + 16 * t) = st[u][t];
+                *reinterpret_cast<f32x4 *>(sfin + fbase + (int64_t)16 * kD * u + 16 * t) = st[u][t];
+    } else {
+        // Phi^T as the scan's matrix-core A operand, split into bf16 hi and lo: per
+        // (segment, head), key tile t and k step cw, 512 hi values then 512 lo ones; lane
+        // 16 (2u + col/8) + 4g + r of tile t holds channels 32 cw + 16 u + 8 (col/8) + 0..7
+        // of key 16t + 4g + r, this lane's value at element col % 8
+        uint16_t *const P = phi + ((int64_t)seg * H + h) * (2 * kD * kD) + cw * (2 * 512) + (col & 7);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                bf16x4 hi, lo;
+                split4t(st[u][t], hi, lo);
+                // whole vectors reinterpreted, then indexed: a bit cast of one element
+                // of a bf16 vector compiled to element 0 for every index (ROCm 7.2.0)
+                const i16x4 hb = __builtin_bit_cast(i16x4, hi), lb = __builtin_bit_cast(i16x4, lo);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    uint16_t *d = P + t * (4 * 2 * 512) + (16 * (2 * u + (col >> 3)) + 4 * g + r) * 8;
+                    d[0] = (uint16_t)hb[r];
+                    d[512] = (uint16_t)lb[r];
+                }
+            }
     }
     };
     if constexpr (SEG) {
@@ -737,7 +758,7 @@ static hipError_t launch_fused_t(const Problem &p, hipStream_t s)
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
     const int32_t *seg = SEG ? reinterpret_cast<const int32_t *>(p.ws + p.lay.seg_off) : nullptr;
     float *sfin = SEG ? reinterpret_cast<float *>(p.ws + p.lay.sfin) : nullptr;
-    float *phi = SEG ? reinterpret_cast<float *>(p.ws + p.lay.phi) : nullptr;
+    uint16_t *phi = SEG ? reinterpret_cast<uint16_t *>(p.ws + p.lay.phi) : nullptr;
     uint16_t *ybuf = SEG ? reinterpret_cast<uint16_t *>(p.ws + p.lay.ybuf) : nullptr;
     const int64_t groups = (SEG ? p.lay.seg_max : p.N) * p.H;
     hipLaunchKernelGGL((kf_fused<TSt, SG, SEG, CSR>), dim3((unsigned)groups), dim3(f_threads<SEG>()), 0, s,

@@ -67,7 +67,9 @@ inline bool use_lookahead(int64_t N, int64_t H, bool f32_path, bool bf16_residen
 // take about a third less time per chunk. Workspace after the chunk map:
 //   seg_off [N+1] int32             exclusive scan of segments per sequence
 //   sfin    [seg_max][H][128][128]  fp32, segment's final state from S = 0 (seg 0: S_0)
-//   phi     [seg_max][H][128][128]  fp32, segment's key-space transfer
+//   phi     [seg_max][H][8][4][2][64][8] bf16, segment's key-space transfer Phi, transposed
+//                                   and split into hi and lo halves, in the scan's
+//                                   matrix-core operand order (key tile, k step, half, lane)
 //   sin     [seg_max][H][128][128]  fp32, true state entering the segment
 //   ybuf    [n_c_max][H][4][64][8]  bf16, y_t = Phi_t (s qhat_t) within the segment: one
 //                                   4 KB tile per (chunk, head) in the order the correction's

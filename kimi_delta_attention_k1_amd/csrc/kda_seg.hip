@@ -10,133 +10,106 @@
 // state entering segment g:
 //   S at token t = S_in Phi_t + S0_t,      o_t = o0_t + S_in y_t,
 //   S_in(g+1) = S_in(g) Phi_g + S0_g,      S_in(0) = initial state.
-// kseg_scan walks that chain over the segments of each (sequence, head) with fp32
-// matrix-core products; kseg_correct adds S_in y_t to the outputs of every
+// kseg_scan walks that chain over the segments of each (sequence, head) with
+// split-bf16 matrix-core products; kseg_correct adds S_in y_t to the outputs of every
 // segment after the first.
 #include "kda_mfma_common.h"
 
 namespace kda {
 
-constexpr int kScanRows = 16;   // value rows per scan workgroup
-constexpr int kScanLd = kD + 4;  // padded LDS row (floats)
+constexpr int kScanRows = 16;   // value rows (state rows) per scan workgroup
+constexpr int kScanWaves = 8;   // wave w: key channels [16w, 16w + 16)
+constexpr int kScanDepth = 2;   // segments whose Phi and S0 tiles are in flight ahead of the chain
+constexpr int kScanLd = kD + 8; // padded LDS row (bf16)
 
-__device__ __forceinline__ f32x4 mma4f(float a, float b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-constexpr int kScanWaves = 8;    // one 16-column tile of the state rows each
-constexpr int kScanDepth = 3;    // segments whose Phi and S0 are in flight ahead of the chain
-constexpr int kScanPhiLd = kD + 16;  // padded LDS row of Phi (floats): the four k rows a
-                                     // B-operand read touches fall 16 banks apart
-
-// LDS column of state column k: the 32 columns 4i + g (i = 0..31) that one lane group g
-// of the 16x16x4 A operand reads are contiguous, so a lane fetches them 16 bytes at a time
-__device__ __forceinline__ int scan_col(int k) { return 32 * (k & 3) + (k >> 2); }
-
-// One workgroup (8 waves) per (sequence, head, 16 value rows). The state rows stay
-// in LDS; each step forms S Phi_g + S0_g: wave w owns key columns [16w, 16w+16) and
-// contracts over the 128 rows of Phi_g in 16x16x4 fp32 steps, with Phi_g and the S0_g
-// rows staged through LDS. Their 16-byte loads run kScanDepth segments ahead of the
-// chain (ten memory operations per lane and step, well within what the wait counter
-// tracks), into register buffers that the unrolled loop addresses statically.
+// One workgroup (8 waves) per (sequence, head, 16 value rows v). Each step forms the
+// transposed chain S^T <- Phi_g^T S^T + S0_g^T: wave w owns key channels [16w, 16w+16)
+// as the rows of a 16x16 tile whose columns are the 16 value rows. Phi_g^T is the A
+// operand, read straight from HBM as split-bf16 tiles the single pass stored in this
+// operand order (kScanDepth segments ahead of the chain); S^T is the B operand, the
+// previous step's tile in LDS as bf16 hi and lo halves, double-buffered so that one
+// barrier per step suffices. Three products per 32-channel k step (hi hi, lo hi,
+// hi lo) carry about 16 bits of each operand; the sums and S0 stay fp32. A lane ends
+// each step with four consecutive key channels of one value row: 16-byte stores of
+// S_in and of the final state.
 template <typename TSt>
 __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt *s1,
                                                              const int32_t *__restrict__ seg_off, int H,
                                                              const float *__restrict__ sfin,
-                                                             const float *__restrict__ phi, float *__restrict__ sin)
+                                                             const uint16_t *__restrict__ phi, float *__restrict__ sin)
 {
-    constexpr int kThreads = 64 * kScanWaves;
-    constexpr int kPhiLoads = kD * kD / 4 / kThreads;  // float4 loads of Phi per lane
-    static_assert(kPhiLoads * kThreads * 4 == kD * kD && kScanRows * kD == 4 * kThreads,
-                  "Phi in whole passes of float4 loads, the S0 rows in one");
-    __shared__ __attribute__((aligned(16))) float S[kScanRows][kScanLd];  // columns in scan_col order
-    __shared__ __attribute__((aligned(16))) float Ph[kD][kScanPhiLd];
-    __shared__ __attribute__((aligned(16))) float Zs[kScanRows][kScanLd];
+    __shared__ __attribute__((aligned(16))) uint16_t Sh[2][kScanRows][kScanLd];  // [buffer][v][key] hi
+    __shared__ __attribute__((aligned(16))) uint16_t Sl[2][kScanRows][kScanLd];  // lo
     const int n = blockIdx.x / H, h = blockIdx.x % H, r0 = blockIdx.y * kScanRows;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, g = lane >> 4;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
     const int first = seg_off[n], G = seg_off[n + 1] - first;
     const int64_t mat = (int64_t)kD * kD;
-    auto seg_off_of = [&](int sg) { return ((int64_t)sg * H + h) * mat; };
-    // this lane's 16-byte pieces: Phi element 4 (tid + it kThreads) and S0 row r0 + zr, columns zc..zc+3
-    const int zr = tid / (kD / 4), zc = 4 * (tid % (kD / 4));
-
-    // state entering segment 1: segment 0's run started from the initial state
-    for (int i = tid; i < kScanRows * kD; i += kThreads) {
-        const int r = i / kD, c = i % kD;
-        float x;
-        if (G > 0)
-            x = sfin[seg_off_of(first) + (int64_t)(r0 + r) * kD + c];
-        else
-            x = s0 ? ld_elem(s0, ((int64_t)n * H + h) * mat + (int64_t)(r0 + r) * kD + c) : 0.f;
-        S[r][scan_col(c)] = x;
-    }
-    f32x4 pb[kScanDepth][kPhiLoads];
-    f32x4 z[kScanDepth];
-    auto load_step = [&](int gi, f32x4(&pp)[kPhiLoads], f32x4 &zz) {
-        const f32x4 *P = reinterpret_cast<const f32x4 *>(phi + seg_off_of(first + gi));
+    // this lane's four state elements: value row r0 + col, key channels 16w + 4g .. +3
+    const int64_t eoff = (int64_t)(r0 + col) * kD + 16 * w + 4 * g;
+    auto sg_base = [&](int gi) { return ((int64_t)(first + gi) * H + h) * mat; };
+    // segment gi's Phi^T tiles of this wave: k step ks, hi then lo, 1 KB per wave
+    auto load_step = [&](int gi, bf16x8 (&ph)[4], bf16x8 (&pl)[4], f32x4 &z) {
+        const uint16_t *P = phi + 2 * sg_base(gi) + (int64_t)w * (4 * 2 * 512) + lane * 8;  // hi and lo: 2 per element
 #pragma unroll
-        for (int it = 0; it < kPhiLoads; ++it) pp[it] = P[tid + it * kThreads];
-        zz = *reinterpret_cast<const f32x4 *>(sfin + seg_off_of(first + gi) + (int64_t)(r0 + zr) * kD + zc);
+        for (int ks = 0; ks < 4; ++ks) {
+            ph[ks] = *reinterpret_cast<const bf16x8 *>(P + (2 * ks) * 512);
+            pl[ks] = *reinterpret_cast<const bf16x8 *>(P + (2 * ks + 1) * 512);
+        }
+        z = *reinterpret_cast<const f32x4 *>(sfin + sg_base(gi) + eoff);
     };
-    // loads past the last segment re-read it (clamped), so every loop iteration issues
-    // the same memory operations and the waits before a buffer's use stay exact
+    // the state entering segment 1: segment 0's run started from the initial state
+    f32x4 S;
+    if (G > 0)
+        S = *reinterpret_cast<const f32x4 *>(sfin + sg_base(0) + eoff);
+    else
+        S = s0 ? ld_state4(s0 + ((int64_t)n * H + h) * mat + eoff) : f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 ph[kScanDepth][4], pl[kScanDepth][4];
+    f32x4 z[kScanDepth];
+    // loads past the last segment re-read it (clamped): every step issues the same loads
     if (G > 1) {
 #pragma unroll
-        for (int d = 0; d < kScanDepth; ++d) load_step(min(1 + d, G - 1), pb[d], z[d]);
+        for (int d = 0; d < kScanDepth; ++d) load_step(min(1 + d, G - 1), ph[d], pl[d], z[d]);
+    }
+    // S as the next step's B operand: value row col, key channels 16w + 4g .. +3
+    auto put = [&](int buf, f32x4 x) {
+        bf16x4 hi, lo;
+        split4t_packed(x, hi, lo);
+        *reinterpret_cast<bf16x4 *>(&Sh[buf][col][16 * w + 4 * g]) = hi;
+        *reinterpret_cast<bf16x4 *>(&Sl[buf][col][16 * w + 4 * g]) = lo;
+    };
+    if (G > 1) {
+        *reinterpret_cast<f32x4 *>(sin + sg_base(1) + eoff) = S;
+        put(0, S);
     }
     __syncthreads();
-    auto step = [&](int gi, f32x4(&pp)[kPhiLoads], f32x4 &zz) {
-        // the previous step's reads of Ph and Zs ended at its barrier
+    auto step = [&](int gi, bf16x8 (&pa)[4], bf16x8 (&pb)[4], f32x4 &zz) {
+        const int buf = (gi - 1) & 1;
+        f32x4 a0 = zz, a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
 #pragma unroll
-        for (int it = 0; it < kPhiLoads; ++it) {
-            const int e = 4 * (tid + it * kThreads);
-            *reinterpret_cast<f32x4 *>(&Ph[e / kD][e % kD]) = pp[it];
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&Sh[buf][col][32 * ks + 8 * g]);
+            const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&Sl[buf][col][32 * ks + 8 * g]);
+            a0 = mma32(pa[ks], bh, a0);
+            a1 = mma32(pb[ks], bh, a1);
+            a2 = mma32(pa[ks], bl, a2);
         }
-        *reinterpret_cast<f32x4 *>(&Zs[zr][zc]) = zz;
-        load_step(min(gi + kScanDepth, G - 1), pp, zz);  // the buffers are free once stored
-        __syncthreads();  // Ph, Zs and the previous step's S rows are in place
-        {
-            f32x4 x;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = S[zr][scan_col(zc + j)];
-            *reinterpret_cast<f32x4 *>(sin + seg_off_of(first + gi) + (int64_t)(r0 + zr) * kD + zc) = x;
+        load_step(min(gi + kScanDepth, G - 1), pa, pb, zz);  // the buffers are free once used
+        S = a0 + (a1 + a2);
+        if (gi + 1 < G) {
+            *reinterpret_cast<f32x4 *>(sin + sg_base(gi + 1) + eoff) = S;
+            put(buf ^ 1, S);
         }
-        f32x4 a[kD / 16];  // A[row col][k = 4 ks + g] for ks = 0..31
-#pragma unroll
-        for (int q = 0; q < kD / 16; ++q) a[q] = *reinterpret_cast<const f32x4 *>(&S[col][32 * g + 4 * q]);
-        float b[kD / 4];  // B[k = 4 ks + g][column 16 w + col]
-#pragma unroll
-        for (int ks = 0; ks < kD / 4; ++ks) b[ks] = Ph[4 * ks + g][16 * w + col];
-        // four independent accumulation chains (k steps 4i + c go to chain c)
-        f32x4 acc[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < kD / 4; ++ks) acc[ks & 3] = mma4f(a[ks / 4][ks % 4], b[ks], acc[ks & 3]);
-        f32x4 zv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) zv[r] = Zs[4 * g + r][16 * w + col];
-        __syncthreads();  // every wave has read S, Ph and Zs
-        const f32x4 sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + zv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[4 * g + r][scan_col(16 * w + col)] = sum[r];
+        __syncthreads();  // the next step reads the other buffer; this one is rewritten after it
     };
-    static_assert(kScanDepth == 3, "the loop below is unrolled over the buffers");
+    static_assert(kScanDepth == 2, "the loop below is unrolled over the buffers");
     int gi = 1;
 #pragma unroll 1
-    for (; gi + 2 < G; gi += kScanDepth) {
-        step(gi, pb[0], z[0]);
-        step(gi + 1, pb[1], z[1]);
-        step(gi + 2, pb[2], z[2]);
+    for (; gi + 1 < G; gi += kScanDepth) {
+        step(gi, ph[0], pl[0], z[0]);
+        step(gi + 1, ph[1], pl[1], z[1]);
     }
-    if (gi < G) step(gi, pb[0], z[0]);
-    if (gi + 1 < G) step(gi + 1, pb[1], z[1]);
-    __syncthreads();  // the last step's S rows are in place
-    if (s1) {
-        for (int i = tid; i < kScanRows * kD; i += kThreads)
-            st_elem(s1, ((int64_t)n * H + h) * mat + (int64_t)(r0 + i / kD) * kD + i % kD, S[i / kD][scan_col(i % kD)]);
-    }
+    if (gi < G) step(gi, ph[0], pl[0], z[0]);
+    if (s1) st_state4(s1 + ((int64_t)n * H + h) * mat + eoff, S);
 }
 
 constexpr int kCorrWaves = 8;
@@ -288,7 +261,7 @@ static hipError_t launch_seg_finish_t(const Problem &p, hipStream_t s)
     const int32_t *chk = reinterpret_cast<const int32_t *>(p.ws + p.lay.chunk_off);
     const int32_t *seg = reinterpret_cast<const int32_t *>(p.ws + p.lay.seg_off);
     const float *sfin = reinterpret_cast<const float *>(p.ws + p.lay.sfin);
-    const float *phi = reinterpret_cast<const float *>(p.ws + p.lay.phi);
+    const uint16_t *phi = reinterpret_cast<const uint16_t *>(p.ws + p.lay.phi);
     float *sin = reinterpret_cast<float *>(p.ws + p.lay.sin);
     hipLaunchKernelGGL(kseg_scan<TSt>, dim3((unsigned)(p.N * p.H), kD / kScanRows), dim3(64 * kScanWaves), 0, s,
                        (const TSt *)p.s0, (TSt *)p.s1, seg, p.H, sfin, phi, sin);

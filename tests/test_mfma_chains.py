@@ -1,9 +1,11 @@
-"""Host-side check of the generated gfx950 code: no matrix-core product accumulates
-onto the result of a product of another shape within the wait states that gfx950
-needs between them (the rule and its measurement are in tests/mfma_chain_check.py).
-Compiles every kernel source to assembly with the library's own flags; needs hipcc."""
+"""Host-side checks of source forms that gfx950 code generation got wrong. No
+matrix-core product accumulates onto the result of a product of another shape within
+the wait states that gfx950 needs between them (the rule and its measurement are in
+tests/mfma_chain_check.py; compiles every kernel source to assembly with the library's
+own flags, needs hipcc), and no kernel bit-casts one element of a vector."""
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import tempfile
 
@@ -74,3 +76,25 @@ def test_no_mixed_shape_chain_in_generated_code():
             problems.append(f"{src} {fn[:60]}: '{writer}' then '{reader}' after {wait} wait states")
     assert n_mfma > 100  # the kernels were compiled and parsed
     assert not problems, f"mixed-shape MFMA chains closer than {MIN_WAIT} wait states:\n" + "\n".join(problems[:20])
+
+
+# ROCm 7.2.0's hipcc compiled __builtin_bit_cast(uint16_t, v[r]) on a bf16 vector v to
+# element 0 for every r; the kernels reinterpret whole vectors and index the result
+_BIT_CAST_OF_ELEMENT = re.compile(r"__builtin_bit_cast\s*\([^,()]+,\s*[A-Za-z_][\w.]*\s*\[")
+
+
+def test_checker_flags_an_element_bit_cast():
+    assert _BIT_CAST_OF_ELEMENT.search("d[0] = __builtin_bit_cast(uint16_t, hi[r]);")
+    assert not _BIT_CAST_OF_ELEMENT.search("const i16x4 hb = __builtin_bit_cast(i16x4, hi);")
+    assert not _BIT_CAST_OF_ELEMENT.search("x = __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));")
+
+
+def test_no_bit_cast_of_a_vector_element():
+    bad = []
+    for src in sorted(os.listdir(kbuild.CSRC)):
+        if src.endswith((".hip", ".h")):
+            with open(os.path.join(kbuild.CSRC, src)) as f:
+                for i, line in enumerate(f, 1):
+                    if _BIT_CAST_OF_ELEMENT.search(line):
+                        bad.append(f"{src}:{i}: {line.strip()}")
+    assert not bad, "bit cast of a vector element:\n" + "\n".join(bad)
