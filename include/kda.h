@@ -137,8 +137,10 @@ enum {
      * Doubleword page, section 4.1). A scan over the segments then forms each
      * segment's true incoming state and the final state, and a last kernel
      * adds the incoming state's contribution to the outputs. The workspace
-     * holds the chunk map, three fp32 [128][128] matrices per (segment, head)
-     * and a bf16 [B*T][H][128] buffer. Not valid with fp32 compute, another
+     * holds the chunk map, three 64 KiB [128][128] matrices per (segment, head)
+     * (the segment's final state from zero, its transfer as split bf16, the
+     * true incoming state) and 4 KiB of bf16 per (chunk, head) for the
+     * transfer applied to the queries. Not valid with fp32 compute, another
      * path flag or KDA_FLAG_BF16_RESIDENT_STATE, or for kda_fwd_prepare /
      * kda_fwd_recur. */
     KDA_FLAG_SEGMENTED = 64u
