@@ -10,14 +10,18 @@
 // observation for the chunked solve).
 //
 // Grid: one 128-thread workgroup per (sequence, head, 16-row value slice). Lane l of
-// wave w owns row 8w + l/8 of the slice and key channels [16 (l%8), 16 (l%8) + 16):
-// 16 fp32 state values in registers, loaded and stored as 64 contiguous bytes.
+// wave w owns rows 8w + 2i + l/32 (i = 0..3) of the slice at key channels
+// [4 (l%32), 4 (l%32) + 4): 16 fp32 state values in registers. A wave's eight rows are
+// 4 KB in one piece, and each of its four state loads and stores moves 1 KB of it in
+// one piece (lane l at byte 16 l, then 1 KB further), whole cache lines: with a lane's
+// 16 channels of one row as 64 contiguous bytes, each access touched 16-byte pieces of
+// 32 lines, and decode streamed the state 18% slower.
 // Tokens go in blocks of 8: the block's activations (q^ s, k^, alpha, beta and the
 // slice's v) are computed by all 128 threads at once into LDS, then the serial loop
-// applies the recurrence token by token with 8-lane reductions for S k and S q.
+// applies the recurrence token by token with 32-lane reductions for S k and S q.
 // With T = 1 (decode) the kernel is one pass over the state: 128 KiB of HBM traffic
 // per (sequence, head) for an fp32 state.
-#include "kda_internal.h"
+#include "kda_mfma_common.h"
 
 namespace kda {
 
@@ -53,29 +57,6 @@ template <> struct InVec<float> {
     }
 };
 
-template <typename T> __device__ __forceinline__ void ld_state16(const T *p, float *s);
-template <> __device__ __forceinline__ void ld_state16<float>(const float *p, float *s) { InVec<float>::load16(p, s); }
-template <> __device__ __forceinline__ void ld_state16<uint16_t>(const uint16_t *p, float *s)
-{
-    InVec<uint16_t>::load16(p, s);
-}
-template <typename T> __device__ __forceinline__ void st_state16(T *p, const float *s);
-template <> __device__ __forceinline__ void st_state16<float>(float *p, const float *s)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        reinterpret_cast<float4 *>(p)[i] = make_float4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
-}
-template <> __device__ __forceinline__ void st_state16<uint16_t>(uint16_t *p, const float *s)
-{
-    uint32_t u[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        u[i] = (uint32_t)f32_to_bf16_bits(s[2 * i]) | ((uint32_t)f32_to_bf16_bits(s[2 * i + 1]) << 16);
-    reinterpret_cast<uint4 *>(p)[0] = make_uint4(u[0], u[1], u[2], u[3]);
-    reinterpret_cast<uint4 *>(p)[1] = make_uint4(u[4], u[5], u[6], u[7]);
-}
-
 // sum over the 8 lanes l with equal l / 8 (lanes differ in bits 0-2)
 __device__ __forceinline__ float sum8(float x)
 {
@@ -84,6 +65,15 @@ __device__ __forceinline__ float sum8(float x)
     x += __shfl_xor(x, 4);
     return x;
 }
+// sum over the 32 lanes l with equal l / 32
+__device__ __forceinline__ float sum32(float x)
+{
+    x = sum8(x);
+    x += __shfl_xor(x, 8);
+    x += __shfl_xor(x, 16);
+    return x;
+}
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
 
 // sigmoid and exp from 2^x and a reciprocal (v_exp_f32, v_rcp_f32). The gate's
 // exponent lb sigmoid(g) log2(e) has magnitude below 15, so its rounding moves alpha
@@ -111,17 +101,14 @@ __global__ __launch_bounds__(kRThreads) void kr_recurrent(const TIn *__restrict_
     const int n = pair / H, h = pair % H;
     const int tb = tok_off[n], te = tok_off[n + 1];
 
-    // state: row r of this slice, key channels [16 cg, 16 cg + 16)
-    const int r = 8 * w + (lane >> 3), cg = lane & 7;
-    const int vrow = kRRows * slice + r;
-    const int64_t soff = (((int64_t)n * H + h) * kD + vrow) * kD + 16 * cg;
-    float s[16];
-    if (s0 != nullptr) {
-        ld_state16(s0 + soff, s);
-    } else {
+    // state: rows 8w + 2i + hr of this slice (s[i]), key channels [4 c4, 4 c4 + 4);
+    // row 8w + hr at channel 4 c4 is element 4 l of the wave's 4 KB, row 8w + 2i + hr
+    // 256 i elements further
+    const int hr = lane >> 5, c4 = lane & 31;
+    const int64_t soff = (((int64_t)n * H + h) * kD + kRRows * slice + 8 * w) * kD + 4 * lane;
+    f32x4 s[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 0.f;
-    }
+    for (int i = 0; i < 4; ++i) s[i] = s0 != nullptr ? ld_state4(s0 + soff + 2 * kD * i) : f32x4{0.f, 0.f, 0.f, 0.f};
 
     // activation work split: thread (at, ap) handles token at of the block, channels [16 ap, 16 ap + 16)
     const int at = tid >> 3, ap = tid & 7;
@@ -169,36 +156,37 @@ __global__ __launch_bounds__(kRThreads) void kr_recurrent(const TIn *__restrict_
         __syncthreads();
 #pragma unroll 1
         for (int j = 0; j < nb; ++j) {
-            float kv[16], av[16], qv[16];
+            const f32x4 av = *reinterpret_cast<const f32x4 *>(&sA[j][4 * c4]);
+            const f32x4 kv = *reinterpret_cast<const f32x4 *>(&sK[j][4 * c4]);
+            const f32x4 qv = *reinterpret_cast<const f32x4 *>(&sQ[j][4 * c4]);
+            float p[4], o[4];
 #pragma unroll
-            for (int i = 0; i < 16; i += 4) {
-                const float4 a = *reinterpret_cast<const float4 *>(&sA[j][16 * cg + i]);
-                const float4 b = *reinterpret_cast<const float4 *>(&sK[j][16 * cg + i]);
-                const float4 c = *reinterpret_cast<const float4 *>(&sQ[j][16 * cg + i]);
-                av[i] = a.x, av[i + 1] = a.y, av[i + 2] = a.z, av[i + 3] = a.w;
-                kv[i] = b.x, kv[i + 1] = b.y, kv[i + 2] = b.z, kv[i + 3] = b.w;
-                qv[i] = c.x, qv[i + 1] = c.y, qv[i + 2] = c.z, qv[i + 3] = c.w;
+            for (int i = 0; i < 4; ++i) {  // forget, then predict: (S Diag(alpha) k)[row]
+                s[i] *= av;
+                p[i] = dot4(s[i], kv);
             }
-            float p = 0.f;  // forget, then predict: (S Diag(alpha) k)[row]
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s[i] *= av[i];
-                p += s[i] * kv[i];
-            }
-            p = sum8(p);
-            const float e = sB[j] * (sV[j][r] - p);  // correct
-            float o = 0.f;  // write, then read
+            for (int i = 0; i < 4; ++i) p[i] = sum32(p[i]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s[i] += e * kv[i];
-                o += s[i] * qv[i];
+            for (int i = 0; i < 4; ++i) {
+                const float e = sB[j] * (sV[j][8 * w + 2 * i + hr] - p[i]);  // correct
+                s[i] += e * kv;                                               // write, then read
+                o[i] = dot4(s[i], qv);
             }
-            o = sum8(o);
-            if (cg == 0) st_elem(out, ((int64_t)(t0 + j) * H + h) * kD + vrow, o);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = sum32(o[i]);
+            if (c4 == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st_elem(out, ((int64_t)(t0 + j) * H + h) * kD + kRRows * slice + 8 * w + 2 * i + hr, o[i]);
+            }
         }
         __syncthreads();  // the next block overwrites the activations
     }
-    if (s1 != nullptr) st_state16(s1 + soff, s);
+    if (s1 != nullptr) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st_state4(s1 + soff + 2 * kD * i, s[i]);
+    }
 }
 
 template <typename TIn, typename TSt>
