@@ -101,14 +101,16 @@ __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt 
         }
         __syncthreads();  // the next step reads the other buffer; this one is rewritten after it
     };
-    static_assert(kScanDepth == 2, "the loop below is unrolled over the buffers");
+    // unrolled over the buffers, so each step addresses its own statically
     int gi = 1;
 #pragma unroll 1
-    for (; gi + 1 < G; gi += kScanDepth) {
-        step(gi, ph[0], pl[0], z[0]);
-        step(gi + 1, ph[1], pl[1], z[1]);
+    for (; gi + kScanDepth - 1 < G; gi += kScanDepth) {
+#pragma unroll
+        for (int d = 0; d < kScanDepth; ++d) step(gi + d, ph[d], pl[d], z[d]);
     }
-    if (gi < G) step(gi, ph[0], pl[0], z[0]);
+#pragma unroll
+    for (int d = 0; d + 1 < kScanDepth; ++d)
+        if (gi + d < G) step(gi + d, ph[d], pl[d], z[d]);
     if (s1) st_state4(s1 + ((int64_t)n * H + h) * mat + eoff, S);
 }
 
