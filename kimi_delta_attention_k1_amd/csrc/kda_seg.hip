@@ -116,7 +116,6 @@ __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt 
 
 constexpr int kCorrWaves = 8;
 constexpr int kCorrTok = 32 * kCorrWaves;  // tokens per workgroup
-constexpr int kCorrLd = kD + 8;            // padded LDS row (bf16): rows 4 banks apart
 
 // LDS row of value channel r = 32p + 8g + 4u + i: row 16 (2p + u) + 4g + i. Result tiles
 // 2p and 2p + 1 then hold channels 32p + 8g + (0..3) and (4..7) in lane group g, so a
@@ -126,6 +125,13 @@ __device__ __forceinline__ int corr_row(int r) { return (r & ~31) + 16 * ((r >> 
 // order in which the single pass stores a y tile (lane group g of k step ks holds
 // channels 32 ks + 4 g + (0..3), then 32 ks + 16 + 4 g + (0..3))
 __device__ __forceinline__ int corr_col(int c) { return (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3); }
+// LDS element of (row, column) in the unpadded bf16 S_in halves: the 16-byte pieces of a
+// row are XOR-swizzled by its low three bits, so eight lanes reading the same piece of
+// eight rows (an A-operand read) hit eight different 16-byte bank groups
+__device__ __forceinline__ int corr_lds(int row, int col) { return row * kD + ((((col >> 3) ^ row) & 7) | (col >> 3 & ~7)) * 8 + (col & 7); }
+// 16-byte piece `piece` (0..7) of token row `tr` (0..15) of a wave's output staging buffer
+// (half of each token's output row), swizzled the same way
+__device__ __forceinline__ int corr_stage(int tr, int piece) { return tr * 8 + ((piece ^ tr) & 7); }
 
 // o_t += S_in y_t for every segment after the first. Workgroup (segment, head, j)
 // splits S_in once into bf16 hi and lo halves in LDS, then walks the segment's
@@ -133,7 +139,7 @@ __device__ __forceinline__ int corr_col(int c) { return (c & ~31) + 8 * ((c >> 2
 // chunks) and forms (S_in y^T) for them as 16x16 tiles (rows: value channels in the
 // order corr_row gives, columns: tokens), so each lane ends with eight consecutive
 // value channels of one token. The y of a chunk is one 4 KB tile in operand order.
-__global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__restrict__ out,
+__global__ __launch_bounds__(64 * kCorrWaves, 4) void kseg_correct(uint16_t *__restrict__ out,
                                                                  const uint16_t *__restrict__ ybuf,
                                                                  const float *__restrict__ sin,
                                                                  const int32_t *__restrict__ tok_off,
@@ -141,8 +147,10 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
                                                                  const int32_t *__restrict__ seg_off, int N, int H,
                                                                  int seg_len, int seg_first)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t Shi[kD][kCorrLd];
-    __shared__ __attribute__((aligned(16))) uint16_t Slo[kD][kCorrLd];
+    // 2 x 32 KB of S_in halves and 2 KB of output staging per wave: 80 KB, two workgroups per CU
+    __shared__ __attribute__((aligned(16))) uint16_t Shi[kD * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t Slo[kD * kD];
+    __shared__ __attribute__((aligned(16))) u32x4 Ost[kCorrWaves][16 * 8];
     const int seg = blockIdx.x / H, h = blockIdx.x % H;
     if (seg >= seg_off[N]) return;
     const int n = find_seq(seg_off, N, seg), gi = seg - seg_off[n];
@@ -168,8 +176,8 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
         const u32x2 hi = {__builtin_amdgcn_perm(u[1], u[0], 0x07060302u), __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
         const f32x2 r01 = {x[0] - __uint_as_float(u[0] & 0xffff0000u), x[1] - __uint_as_float(u[1] & 0xffff0000u)};
         const f32x2 r23 = {x[2] - __uint_as_float(u[2] & 0xffff0000u), x[3] - __uint_as_float(u[3] & 0xffff0000u)};
-        *reinterpret_cast<u32x2 *>(&Shi[corr_row(r)][corr_col(c)]) = hi;
-        *reinterpret_cast<u32x2 *>(&Slo[corr_row(r)][corr_col(c)]) = u32x2{pk_bf16(r01), pk_bf16(r23)};
+        *reinterpret_cast<u32x2 *>(&Shi[corr_lds(corr_row(r), corr_col(c))]) = hi;
+        *reinterpret_cast<u32x2 *>(&Slo[corr_lds(corr_row(r), corr_col(c))]) = u32x2{pk_bf16(r01), pk_bf16(r23)};
     }
     __syncthreads();
 
@@ -179,24 +187,28 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
         // every load of the block's two token tiles is issued before any product, so
         // each wave keeps 2 x (512 B y + 256 B o) per lane-row in flight at once
         bf16x8 yb[2][kD / 32];
-        u32x4 ov[2][kD / 32];
-        bool live[2];
-        uint16_t *orow[2];
+        // the outputs as whole half rows: ov[tt][k] holds, for lane L, 16 bytes at byte
+        // 128 half + 16 (L % 8) of token t16 + 8k + L / 8 (rows past the end: the
+        // segment's first, never stored); the second half is loaded while the first
+        // half's products run
+        u32x4 ov[2][2];
+        uint16_t *orow[2][2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int t16 = tlo + 32 * w + 16 * tt;  // the chunk's first token
-            const int t = t16 + col;                 // this lane's token (B column, D column)
-            live[tt] = t < te;
-            const int tc = live[tt] ? t : tb;
             // the chunk's y tile (a chunk past the segment's end re-reads its first one)
             const int ch = chunk_off[n] + ((t16 < te ? t16 : tb) - tok_off[n]) / kC;
             const uint16_t *ytile = ybuf + ((int64_t)ch * H + h) * (kC * kD) + 8 * lane;
-            orow[tt] = out + (int64_t)tc * rowst + (int64_t)h * kD;
 #pragma unroll
             for (int ks = 0; ks < kD / 32; ++ks) yb[tt][ks] = *reinterpret_cast<const bf16x8 *>(ytile + 64 * 8 * ks);
 #pragma unroll
-            for (int p = 0; p < kD / 32; ++p) ov[tt][p] = *reinterpret_cast<const u32x4 *>(orow[tt] + 32 * p + 8 * g);
+            for (int k = 0; k < 2; ++k) {
+                const int t = t16 + 8 * k + (lane >> 3);
+                orow[tt][k] = out + (int64_t)(t < te ? t : tb) * rowst + (int64_t)h * kD + 8 * (lane & 7);
+                ov[tt][k] = *reinterpret_cast<const u32x4 *>(orow[tt][k]);
+            }
         }
+        u32x4 *const stage = Ost[w];
         // two halves of the value channels, 64 each: 32 accumulator registers per lane
         // rather than 64 keep the kernel under 128 VGPRs, so two workgroups share a CU
 #pragma unroll
@@ -211,8 +223,8 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {  // each S_in fragment pair serves both token tiles
                     const int j = 4 * half + jj;
-                    const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(&Shi[16 * j + col][32 * ks + 8 * g]);
-                    const bf16x8 al = *reinterpret_cast<const bf16x8 *>(&Slo[16 * j + col][32 * ks + 8 * g]);
+                    const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(&Shi[corr_lds(16 * j + col, 32 * ks + 8 * g)]);
+                    const bf16x8 al = *reinterpret_cast<const bf16x8 *>(&Slo[corr_lds(16 * j + col, 32 * ks + 8 * g)]);
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt) {
                         acc[tt][jj] = mma32(ah, yb[tt][ks], acc[tt][jj]);
@@ -221,22 +233,43 @@ __global__ __launch_bounds__(64 * kCorrWaves) void kseg_correct(uint16_t *__rest
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep one k-step's LDS fragments live at a time
             }
+            u32x4 on[2][2];  // the second half's rows, in flight during this half's epilogue
+            if (half == 0) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) on[tt][k] = *reinterpret_cast<const u32x4 *>(orow[tt][k] + 64);
+            }
+            // this half of each token's outputs, through the wave's staging buffer: in as
+            // whole half rows, out to the products' lanes (token col, channels 32p + 8g .. +7,
+            // bytes 64 pp + 16 g of the half row), back, and stored as whole half rows. A
+            // wave's LDS operations complete in order, so no wait is needed in between.
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                if (live[tt]) {
 #pragma unroll
-                    for (int pp = 0; pp < 2; ++pp) {
-                        const int p = 2 * half + pp;
-                        const u32x4 o = ov[tt][p];
-                        const f32x4 a0 = acc[tt][2 * pp], a1 = acc[tt][2 * pp + 1];
-                        const f32x2 c0 = {bf_lo(o[0]) + a0[0], bf_hi(o[0]) + a0[1]};
-                        const f32x2 c1 = {bf_lo(o[1]) + a0[2], bf_hi(o[1]) + a0[3]};
-                        const f32x2 c2 = {bf_lo(o[2]) + a1[0], bf_hi(o[2]) + a1[1]};
-                        const f32x2 c3 = {bf_lo(o[3]) + a1[2], bf_hi(o[3]) + a1[3]};
-                        *reinterpret_cast<u32x4 *>(orow[tt] + 32 * p + 8 * g) =
-                            u32x4{pk_bf16(c0), pk_bf16(c1), pk_bf16(c2), pk_bf16(c3)};
-                    }
+                for (int k = 0; k < 2; ++k) stage[corr_stage(8 * k + (lane >> 3), lane & 7)] = ov[tt][k];
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const u32x4 o = stage[corr_stage(col, 4 * pp + g)];
+                    const f32x4 a0 = acc[tt][2 * pp], a1 = acc[tt][2 * pp + 1];
+                    const f32x2 c0 = {bf_lo(o[0]) + a0[0], bf_hi(o[0]) + a0[1]};
+                    const f32x2 c1 = {bf_lo(o[1]) + a0[2], bf_hi(o[1]) + a0[3]};
+                    const f32x2 c2 = {bf_lo(o[2]) + a1[0], bf_hi(o[2]) + a1[1]};
+                    const f32x2 c3 = {bf_lo(o[3]) + a1[2], bf_hi(o[3]) + a1[3]};
+                    stage[corr_stage(col, 4 * pp + g)] = u32x4{pk_bf16(c0), pk_bf16(c1), pk_bf16(c2), pk_bf16(c3)};
                 }
+                const int t16 = tlo + 32 * w + 16 * tt;
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const u32x4 o = stage[corr_stage(8 * k + (lane >> 3), lane & 7)];
+                    if (t16 + 8 * k + (lane >> 3) < te) *reinterpret_cast<u32x4 *>(orow[tt][k] + 64 * half) = o;
+                }
+            }
+            if (half == 0) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) ov[tt][k] = on[tt][k];
             }
         }
     }
