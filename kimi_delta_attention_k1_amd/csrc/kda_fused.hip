@@ -535,8 +535,6 @@ __global__ __launch_bounds__(f_threads<SEG>()) void kf_fused(
     constexpr int MODE = decltype(mode_tag)::value;
     const int g = lane >> 4, col = lane & 15, sl = swz(lane);
     const int64_t sbase = (((int64_t)n * H + h) * kD + 32 * cw + col) * kD + 4 * g;
-    // segment states and transfers: [segment][head][128][128] fp32
-    const int64_t fbase = (((int64_t)seg * H + h) * kD + 32 * cw + col) * kD + 4 * g;
     f32x4 st[2][8];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -706,11 +704,13 @@ __global__ __launch_bounds__(f_threads<SEG>()) void kf_fused(
                 for (int t = 0; t < 8; ++t) st_state4(s1 + sbase + (int64_t)16 * kD * u + 16 * t, st[u][t]);
         }
     } else if constexpr (MODE == 1) {
+        // tile order: st[u][t] holds keys 16t + 4g .. +3 of value row 32 cw + 16 u + col
+        float *const F = sfin + ((int64_t)seg * H + h) * (kD * kD);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                *reinterpret_cast<f32x4 *>(sfin + fbase + (int64_t)16 * kD * u + 16 * t) = st[u][t];
+                *reinterpret_cast<f32x4 *>(F + state_tile(32 * cw + 16 * u + col, 16 * t + 4 * g)) = st[u][t];
     } else {
         // Phi^T as the scan's matrix-core A operand, split into bf16 hi and lo: per
         // (segment, head), key tile t and k step cw, 512 hi values then 512 lo ones; lane

@@ -66,16 +66,26 @@ inline bool use_lookahead(int64_t N, int64_t H, bool f32_path, bool bf16_residen
 // the first is L0 = L + L/2 long, because its workgroups skip the transfer run and
 // take about a third less time per chunk. Workspace after the chunk map:
 //   seg_off [N+1] int32             exclusive scan of segments per sequence
-//   sfin    [seg_max][H][128][128]  fp32, segment's final state from S = 0 (seg 0: S_0)
+//   sfin    [seg_max][H][128][128]  fp32, segment's final state from S = 0 (seg 0: S_0), in
+//                                   tile order (state_tile)
 //   phi     [seg_max][H][8][4][2][64][8] bf16, segment's key-space transfer Phi, transposed
 //                                   and split into hi and lo halves, in the scan's
 //                                   matrix-core operand order (key tile, k step, half, lane)
-//   sin     [seg_max][H][128][128]  fp32, true state entering the segment
+//   sin     [seg_max][H][128][128]  fp32, true state entering the segment, in tile order
 //   ybuf    [n_c_max][H][4][64][8]  bf16, y_t = Phi_t (s qhat_t) within the segment: one
 //                                   4 KB tile per (chunk, head) in the order the correction's
 //                                   matrix-core operand takes it (k step, lane, 8 channels),
 //                                   so each of its loads reads 1 KB in one piece
 constexpr int64_t kSegTargetGroups = 256;
+// Tile order of a [128][128] state in the workspace (element of value row v, key channel
+// k): 16-row slice v / 16, 16-key tile k / 16, then lane 16 ((k / 4) % 4) + v % 16 and
+// element k % 4, so four consecutive keys of one row are one 16-byte piece and each
+// (slice, tile) block is 1 KB: the single pass's consumer lanes and the scan's
+// matrix-core lanes each store or load a block in one access.
+__host__ __device__ inline int state_tile(int v, int k)
+{
+    return (((v >> 4) * 8 + (k >> 4)) * 64 + 16 * ((k >> 2) & 3) + (v & 15)) * 4 + (k & 3);
+}
 constexpr int64_t kSegMinChunks = 16;
 inline int64_t seg_first_for(int64_t seg_len) { return seg_len + (seg_len + 1) / 2; }
 inline int64_t seg_len_for(int64_t N, int64_t H, int64_t n_c_max)

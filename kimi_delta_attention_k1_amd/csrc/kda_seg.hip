@@ -45,7 +45,10 @@ __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt 
     const int first = seg_off[n], G = seg_off[n + 1] - first;
     const int64_t mat = (int64_t)kD * kD;
     // this lane's four state elements: value row r0 + col, key channels 16w + 4g .. +3
+    // row-major (initial and final state) and tile-order (S0 and S_in in the workspace)
+    // offsets of the same four elements
     const int64_t eoff = (int64_t)(r0 + col) * kD + 16 * w + 4 * g;
+    const int64_t toff = state_tile(r0 + col, 16 * w + 4 * g);
     auto sg_base = [&](int gi) { return ((int64_t)(first + gi) * H + h) * mat; };
     // segment gi's Phi^T tiles of this wave: k step ks, hi then lo, 1 KB per wave
     auto load_step = [&](int gi, bf16x8 (&ph)[4], bf16x8 (&pl)[4], f32x4 &z) {
@@ -55,12 +58,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt 
             ph[ks] = *reinterpret_cast<const bf16x8 *>(P + (2 * ks) * 512);
             pl[ks] = *reinterpret_cast<const bf16x8 *>(P + (2 * ks + 1) * 512);
         }
-        z = *reinterpret_cast<const f32x4 *>(sfin + sg_base(gi) + eoff);
+        z = *reinterpret_cast<const f32x4 *>(sfin + sg_base(gi) + toff);
     };
     // the state entering segment 1: segment 0's run started from the initial state
     f32x4 S;
     if (G > 0)
-        S = *reinterpret_cast<const f32x4 *>(sfin + sg_base(0) + eoff);
+        S = *reinterpret_cast<const f32x4 *>(sfin + sg_base(0) + toff);
     else
         S = s0 ? ld_state4(s0 + ((int64_t)n * H + h) * mat + eoff) : f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 ph[kScanDepth][4], pl[kScanDepth][4];
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt 
         *reinterpret_cast<bf16x4 *>(&Sl[buf][col][16 * w + 4 * g]) = lo;
     };
     if (G > 1) {
-        *reinterpret_cast<f32x4 *>(sin + sg_base(1) + eoff) = S;
+        *reinterpret_cast<f32x4 *>(sin + sg_base(1) + toff) = S;
         put(0, S);
     }
     __syncthreads();
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt 
         load_step(min(gi + kScanDepth, G - 1), pa, pb, zz);  // the buffers are free once used
         S = a0 + (a1 + a2);
         if (gi + 1 < G) {
-            *reinterpret_cast<f32x4 *>(sin + sg_base(gi + 1) + eoff) = S;
+            *reinterpret_cast<f32x4 *>(sin + sg_base(gi + 1) + toff) = S;
             put(buf ^ 1, S);
         }
         __syncthreads();  // the next step reads the other buffer; this one is rewritten after it
@@ -170,7 +173,10 @@ __global__ __launch_bounds__(64 * kCorrWaves, 4) void kseg_correct(uint16_t *__r
     for (int it = 0; it < kSplitIt; ++it) {
         const int i = tid + it * 64 * kCorrWaves;
         const f32x4 x = sx[it];
-        const int r = (4 * i) / kD, c = (4 * i) % kD;
+        // element 4i of the tile order: value row 16 y + L % 16, key channels 16 w + 4 (L / 16)
+        // .. +3 for i = (8 y + w) 64 + L
+        const int L = i & 63, yw = i >> 6;
+        const int r = 16 * (yw >> 3) + (L & 15), c = 16 * (yw & 7) + 4 * (L >> 4);
         const u32x4 u = __builtin_bit_cast(u32x4, x);
         // hi truncated (x - hi is exact in fp32), lo the remainder rounded
         const u32x2 hi = {__builtin_amdgcn_perm(u[1], u[0], 0x07060302u), __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
