@@ -30,8 +30,8 @@ constexpr int kScanLd = kD + 8; // padded LDS row (bf16)
 // previous step's tile in LDS as bf16 hi and lo halves, double-buffered so that one
 // barrier per step suffices. Three products per 32-channel k step (hi hi, lo hi,
 // hi lo) carry about 16 bits of each operand; the sums and S0 stay fp32. A lane ends
-// each step with four consecutive key channels of one value row: 16-byte stores of
-// S_in and of the final state.
+// each step with four consecutive key channels of one value row: S0 comes in and S_in
+// goes out as one 1 KB block per wave, the final state as 16-byte pieces.
 template <typename TSt>
 __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt *s1,
                                                              const int32_t *__restrict__ seg_off, int H,
@@ -44,9 +44,9 @@ __global__ __launch_bounds__(64 * kScanWaves) void kseg_scan(const TSt *s0, TSt 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
     const int first = seg_off[n], G = seg_off[n + 1] - first;
     const int64_t mat = (int64_t)kD * kD;
-    // this lane's four state elements: value row r0 + col, key channels 16w + 4g .. +3
-    // row-major (initial and final state) and tile-order (S0 and S_in in the workspace)
-    // offsets of the same four elements
+    // this lane's four state elements, value row r0 + col, key channels 16w + 4g .. +3:
+    // their offset in a row-major state (initial and final) and in the tile order of
+    // the workspace's S0 and S_in (one 1 KB block per wave)
     const int64_t eoff = (int64_t)(r0 + col) * kD + 16 * w + 4 * g;
     const int64_t toff = state_tile(r0 + col, 16 * w + 4 * g);
     auto sg_base = [&](int gi) { return ((int64_t)(first + gi) * H + h) * mat; };
@@ -131,7 +131,7 @@ __device__ __forceinline__ int corr_col(int c) { return (c & ~31) + 8 * ((c >> 2
 // LDS element of (row, column) in the unpadded bf16 S_in halves: the 16-byte pieces of a
 // row are XOR-swizzled by its low three bits, so eight lanes reading the same piece of
 // eight rows (an A-operand read) hit eight different 16-byte bank groups
-__device__ __forceinline__ int corr_lds(int row, int col) { return row * kD + ((((col >> 3) ^ row) & 7) | (col >> 3 & ~7)) * 8 + (col & 7); }
+__device__ __forceinline__ int corr_lds(int row, int col) { return row * kD + ((((col >> 3) ^ row) & 7) | ((col >> 3) & ~7)) * 8 + (col & 7); }
 // 16-byte piece `piece` (0..7) of token row `tr` (0..15) of a wave's output staging buffer
 // (half of each token's output row), swizzled the same way
 __device__ __forceinline__ int corr_stage(int tr, int piece) { return tr * 8 + ((piece ^ tr) & 7); }
