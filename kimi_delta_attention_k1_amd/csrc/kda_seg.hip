@@ -142,6 +142,7 @@ __device__ __forceinline__ int corr_stage(int tr, int piece) { return tr * 8 + (
 // chunks) and forms (S_in y^T) for them as 16x16 tiles (rows: value channels in the
 // order corr_row gives, columns: tokens), so each lane ends with eight consecutive
 // value channels of one token. The y of a chunk is one 4 KB tile in operand order.
+// at least four waves per SIMD (at most 128 VGPRs): two 8-wave workgroups per CU
 __global__ __launch_bounds__(64 * kCorrWaves, 4) void kseg_correct(uint16_t *__restrict__ out,
                                                                  const uint16_t *__restrict__ ybuf,
                                                                  const float *__restrict__ sin,
