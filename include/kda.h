@@ -162,7 +162,7 @@ enum {
 #define KDA_FUSED_MIN_PAIRS 96
 #define KDA_FUSED_MAX_AVG_CHUNKS 8
 #define KDA_SEGMENTED_MAX_PAIRS 128
-#define KDA_SEGMENTED_MIN_AVG_CHUNKS 96
+#define KDA_SEGMENTED_MIN_AVG_CHUNKS 64
 #define KDA_RECURRENT_MAX_AVG_TOKENS 4
 
 /*

@@ -48,7 +48,7 @@ FLAG_SEGMENTED = 64
 FUSED_MIN_PAIRS = 96
 FUSED_MAX_AVG_CHUNKS = 8
 SEGMENTED_MAX_PAIRS = 128
-SEGMENTED_MIN_AVG_CHUNKS = 96
+SEGMENTED_MIN_AVG_CHUNKS = 64
 RECURRENT_MAX_AVG_TOKENS = 4
 _PATH_FLAGS = {"auto": 0, "split": FLAG_SPLIT, "fused": FLAG_FUSED, "recurrent": FLAG_RECURRENT,
                "segmented": FLAG_SEGMENTED}

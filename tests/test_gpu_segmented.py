@@ -165,11 +165,11 @@ def test_stage_entry_points_compose_to_kda_fwd(gpu):
 
 
 @pytest.mark.parametrize("N,H,T,expect", [
-    (64, 2, 1536, "segmented"),  # 128 pairs, 96 chunks per sequence
+    (64, 2, 1024, "segmented"),  # 128 pairs, 64 chunks per sequence
     (43, 3, 2048, "fused"),      # 129 pairs: two segments per pair no longer fit one round
-    (32, 3, 1520, "fused"),      # 96 pairs, 95 chunks per sequence: too short to segment
-    (19, 5, 1520, "split"),      # 95 pairs, too short to segment
-    (19, 5, 1536, "segmented"),  # 95 pairs of 96 chunks
+    (32, 3, 1008, "fused"),      # 96 pairs, 63 chunks per sequence: too short to segment
+    (19, 5, 1008, "split"),      # 95 pairs, too short to segment
+    (19, 5, 1024, "segmented"),  # 95 pairs of 64 chunks
     (8, 4, 128, "fused"),        # 32 pairs of 8 chunks: short sequences take the single pass
     (8, 4, 144, "split"),        # 9 chunks per sequence
 ])
