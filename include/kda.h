@@ -128,7 +128,7 @@ enum {
     /* bf16-compute kda_fwd: run the segmented single pass, for few (sequence,
      * head) pairs over long sequences. Every sequence is cut into
      * max(2, 256 / (num_seqs * num_heads)) segments (from the average
-     * sequence; at least 16 chunks each, the first half again as long as the
+     * sequence; at least 8 chunks each, the first half again as long as the
      * others), so that about 256 (segment, head) workgroups, one per compute
      * unit, run at once. Each segment runs the single-pass kernel twice over the
      * same prepared chunks: from a zero state (the first segment: the initial

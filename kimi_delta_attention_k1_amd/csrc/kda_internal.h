@@ -86,7 +86,7 @@ __host__ __device__ inline int state_tile(int v, int k)
 {
     return (((v >> 4) * 8 + (k >> 4)) * 64 + 16 * ((k >> 2) & 3) + (v & 15)) * 4 + (k & 3);
 }
-constexpr int64_t kSegMinChunks = 16;
+constexpr int64_t kSegMinChunks = 8;
 inline int64_t seg_first_for(int64_t seg_len) { return seg_len + (seg_len + 1) / 2; }
 inline int64_t seg_len_for(int64_t N, int64_t H, int64_t n_c_max)
 {

@@ -202,10 +202,10 @@ def _seg_layout(N, H, T_tot, n_c):
     """Chunk map, segment offsets, three fp32 [128][128] matrices per (segment, head)
     and a bf16 [n_c][H][16][128] buffer. G = max(2, 256 // (N H)) segments per average
     sequence of A = ceil(n_c / N) chunks, the first 3/2 as long as the others:
-    L = max(16, (2 A + 2 G) // (2 G + 1)), at most n_c // L + N segments."""
+    L = max(8, (2 A + 2 G) // (2 G + 1)), at most n_c // L + N segments."""
     G = max(2, 256 // (N * H))
     A = -(-n_c // N)
-    L = max(16, (2 * A + 2 * G) // (2 * G + 1))
+    L = max(8, (2 * A + 2 * G) // (2 * G + 1))
     smax = n_c // L + N
     seg = _layout(N, H, 0, 0)
     sfin = (seg + 4 * (N + 1) + 127) // 128 * 128

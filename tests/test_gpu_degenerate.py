@@ -2,7 +2,7 @@
 infinite gate and beta inputs (sigmoid exactly 0 or 1), no decay, keys that
 point almost the same way, the pages' own head counts (H = 64, 96), and NULL
 vs explicit-zero initial states. The segmented pass gets sequences long enough
-for three segments (its segments are at least 16 chunks, the first 24), next to
+for three segments or more (its segments are at least 8 chunks, the first 12), next to
 a one-chunk sequence.
 
 beta_raw = -inf gives beta = 0: no write, so the state only decays and the

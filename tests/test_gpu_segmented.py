@@ -5,7 +5,7 @@ The segmented pass cuts each sequence into time segments, runs every segment
 from a zero state and from the identity (the segment's key-space transfer),
 then scans the segments and corrects the outputs; the result must meet the
 same bounds as every bf16 path (max|x_gpu - x_ref| <= 1e-2 max|x_ref| + 1e-3
-for o and the final state). Segments are 16 chunks long or more, so the small
+for o and the final state). Segments are 8 chunks long or more, so the small
 cases below already span several segments and ragged segment ends.
 """
 import numpy as np
@@ -63,12 +63,12 @@ def test_ragged_segments_and_empty_sequences(gpu, lb):
 
 
 def test_segment_counts_five_six_seven(gpu):
-    # 3 sequences x 2 heads: segments of L = 16 chunks after a first one of 24, so
-    # 84, 100 and 116 chunks make 5, 6 and 7 segments. The scan walks segments 1..G-1
-    # three at a time and then the one or two left over: 4, 5 and 6 steps cover a
-    # whole group plus a tail of one, plus a tail of two, and two whole groups.
-    _banner("segment counts 5, 6 and 7 (scan groups and tails), H=2, initial state")
-    w = workloads.make([1344, 1600, 1856], 2, seed=13, init_std=0.02, beta_mean=0.5)
+    # 3 sequences x 2 heads: segments of L = 8 chunks after a first one of 12, so
+    # 44, 52 and 60 chunks make 5, 6 and 7 segments. The scan walks segments 1..G-1
+    # two at a time and then the one left over: 4, 5 and 6 steps cover two pairs,
+    # two pairs and a tail of one, and three pairs.
+    _banner("segment counts 5, 6 and 7 (scan pairs and tails), H=2, initial state")
+    w = workloads.make([704, 832, 960], 2, seed=13, init_std=0.02, beta_mean=0.5)
     ref = run_oracle(w)
     o, s = run_gpu(w, gpu, path="segmented")
     compare(w, o, s, ref, bf16_tol, "segmented, 5/6/7 segments")
