@@ -180,7 +180,9 @@ def pick_path(kda, w, path):
     if w.T_tot <= kda.RECURRENT_MAX_AVG_TOKENS * w.N:
         return "recurrent"
     n_c = sum((L + 15) // 16 for L in w.seq_lens) if not w.packed else (w.T_tot + 15 * w.N) // 16
-    if w.N * w.H <= kda.SEGMENTED_MAX_PAIRS and n_c >= kda.SEGMENTED_MIN_AVG_CHUNKS * w.N:
+    pairs = w.N * w.H
+    seg_min = kda.SEGMENTED_MIN_AVG_CHUNKS_FEW_PAIRS if pairs <= kda.SEGMENTED_FEW_PAIRS else kda.SEGMENTED_MIN_AVG_CHUNKS
+    if pairs <= kda.SEGMENTED_MAX_PAIRS and n_c >= seg_min * w.N:
         return "segmented"
     if w.N * w.H >= kda.FUSED_MIN_PAIRS or n_c <= kda.FUSED_MAX_AVG_CHUNKS * w.N:
         return "fused"

@@ -150,7 +150,9 @@ enum {
  * seqlen; packed: T_tot / num_seqs), else, for bf16 compute, the segmented
  * single pass when num_seqs * num_heads <= KDA_SEGMENTED_MAX_PAIRS and the
  * sequences average at least KDA_SEGMENTED_MIN_AVG_CHUNKS 16-token chunks
- * (chunk bound / num_seqs), else the single-pass kernel when
+ * (chunk bound / num_seqs; KDA_SEGMENTED_MIN_AVG_CHUNKS_FEW_PAIRS up to
+ * KDA_SEGMENTED_FEW_PAIRS pairs), else the
+ * single-pass kernel when
  * num_seqs * num_heads >= KDA_FUSED_MIN_PAIRS or the sequences average at
  * most KDA_FUSED_MAX_AVG_CHUNKS chunks, and the two-kernel path otherwise;
  * fp32 compute uses
@@ -159,10 +161,12 @@ enum {
  * agree to bf16 rounding; they are not bitwise identical (the single pass
  * applies the L2 normalisation after its in-chunk products instead of
  * before). */
-#define KDA_FUSED_MIN_PAIRS 96
+#define KDA_FUSED_MIN_PAIRS 64
 #define KDA_FUSED_MAX_AVG_CHUNKS 8
 #define KDA_SEGMENTED_MAX_PAIRS 128
-#define KDA_SEGMENTED_MIN_AVG_CHUNKS 64
+#define KDA_SEGMENTED_MIN_AVG_CHUNKS 56
+#define KDA_SEGMENTED_FEW_PAIRS 80
+#define KDA_SEGMENTED_MIN_AVG_CHUNKS_FEW_PAIRS 40
 #define KDA_RECURRENT_MAX_AVG_TOKENS 4
 
 /*

@@ -16,7 +16,8 @@ an output correction; bf16 compute only), "recurrent" (the recurrence token by
 token, for decode and short sequences) or "auto" (the library's rule: recurrent
 up to RECURRENT_MAX_AVG_TOKENS tokens per sequence on average, else segmented
 up to SEGMENTED_MAX_PAIRS (sequence, head) pairs when the sequences average at
-least SEGMENTED_MIN_AVG_CHUNKS chunks, else fused from FUSED_MIN_PAIRS pairs on
+least SEGMENTED_MIN_AVG_CHUNKS chunks (SEGMENTED_MIN_AVG_CHUNKS_FEW_PAIRS up to
+SEGMENTED_FEW_PAIRS pairs), else fused from FUSED_MIN_PAIRS pairs on
 or when the sequences average at most FUSED_MAX_AVG_CHUNKS chunks, else split).
 
 Layouts follow the FlashKDA API (DocSearch FlashKDA digest, "flash_kda.fwd API
@@ -34,7 +35,8 @@ import os
 __all__ = ["fwd", "fwd_noalloc", "prepare_call", "Call", "workspace_size", "KdaError", "load_library", "library_path", "seqlens_flag",
            "HEAD_DIM", "CHUNK", "FLAG_FP32_COMPUTE", "FLAG_SPLIT", "FLAG_FUSED", "FLAG_RECURRENT", "FLAG_SCALAR_GATE",
            "FLAG_BF16_RESIDENT_STATE", "FLAG_SEGMENTED",
-           "FUSED_MIN_PAIRS", "FUSED_MAX_AVG_CHUNKS", "SEGMENTED_MAX_PAIRS", "SEGMENTED_MIN_AVG_CHUNKS", "RECURRENT_MAX_AVG_TOKENS"]
+           "FUSED_MIN_PAIRS", "FUSED_MAX_AVG_CHUNKS", "SEGMENTED_MAX_PAIRS", "SEGMENTED_MIN_AVG_CHUNKS",
+           "SEGMENTED_FEW_PAIRS", "SEGMENTED_MIN_AVG_CHUNKS_FEW_PAIRS", "RECURRENT_MAX_AVG_TOKENS"]
 
 HEAD_DIM = 128
 CHUNK = 16
@@ -45,10 +47,12 @@ FLAG_RECURRENT = 8
 FLAG_SCALAR_GATE = 16
 FLAG_BF16_RESIDENT_STATE = 32
 FLAG_SEGMENTED = 64
-FUSED_MIN_PAIRS = 96
+FUSED_MIN_PAIRS = 64
 FUSED_MAX_AVG_CHUNKS = 8
 SEGMENTED_MAX_PAIRS = 128
-SEGMENTED_MIN_AVG_CHUNKS = 64
+SEGMENTED_MIN_AVG_CHUNKS = 56
+SEGMENTED_FEW_PAIRS = 80
+SEGMENTED_MIN_AVG_CHUNKS_FEW_PAIRS = 40
 RECURRENT_MAX_AVG_TOKENS = 4
 _PATH_FLAGS = {"auto": 0, "split": FLAG_SPLIT, "fused": FLAG_FUSED, "recurrent": FLAG_RECURRENT,
                "segmented": FLAG_SEGMENTED}

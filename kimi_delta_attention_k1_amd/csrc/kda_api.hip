@@ -38,11 +38,14 @@ struct Shape {
 // Which kernels kda_fwd runs (the rule is stated with KDA_FUSED_MIN_PAIRS).
 // Segmented single pass without a flag: at most KDA_SEGMENTED_MAX_PAIRS pairs (two
 // segments per pair still fit one round of workgroups on the compute units) and
-// sequences of at least KDA_SEGMENTED_MIN_AVG_CHUNKS chunks on average.
+// sequences of at least KDA_SEGMENTED_MIN_AVG_CHUNKS chunks on average, or of
+// KDA_SEGMENTED_MIN_AVG_CHUNKS_FEW_PAIRS up to KDA_SEGMENTED_FEW_PAIRS pairs.
 bool seg_worth(const kda_desc_t *d, int64_t n_c_max)
 {
-    return d->num_seqs * (int64_t)d->num_heads <= KDA_SEGMENTED_MAX_PAIRS &&
-           n_c_max >= (int64_t)KDA_SEGMENTED_MIN_AVG_CHUNKS * d->num_seqs;
+    const int64_t pairs = d->num_seqs * (int64_t)d->num_heads;
+    const int64_t min_avg =
+        pairs <= KDA_SEGMENTED_FEW_PAIRS ? KDA_SEGMENTED_MIN_AVG_CHUNKS_FEW_PAIRS : KDA_SEGMENTED_MIN_AVG_CHUNKS;
+    return pairs <= KDA_SEGMENTED_MAX_PAIRS && n_c_max >= min_avg * d->num_seqs;
 }
 
 Path pick_path(const kda_desc_t *d, bool f32_path, int64_t T_tot, int64_t n_c_max)

@@ -223,11 +223,11 @@ def test_segmented_path_workspace(lib):
     assert kda.workspace_size(1, 5000, 3, 2, path="segmented") == _seg_layout(3, 2, 5000, n_c)
     # 256 pairs: no segments needed, the size is the split path's
     assert kda.workspace_size(1, 65536, 8, 32) == _layout(8, 32, (65536 + 15 * 8) // 16, 18944)
-    # 32 pairs of 63 chunks: below the 64-chunk average the rule keeps the split path;
-    # at 64 chunks it picks the segmented pass and the size covers both
-    assert kda.workspace_size(2, 1008, 2, 16) == _layout(2, 16, 126, 18944, look=True)
-    assert kda.workspace_size(2, 1024, 2, 16) == max(_layout(2, 16, 128, 18944, look=True),
-                                                      _seg_layout(2, 16, 2048, 128))
+    # 32 pairs of 39 chunks: below the 40-chunk average (up to 80 pairs) the rule
+    # keeps the split path; at 40 chunks it picks the segmented pass and the size covers both
+    assert kda.workspace_size(2, 624, 2, 16) == _layout(2, 16, 78, 18944, look=True)
+    assert kda.workspace_size(2, 640, 2, 16) == max(_layout(2, 16, 80, 18944, look=True),
+                                                     _seg_layout(2, 16, 1280, 80))
     assert kda.workspace_size(1, 64, 1, 1, kda.DTYPE_FP32, path="segmented") == 0  # invalid: fp32 I/O
 
 

@@ -165,11 +165,15 @@ def test_stage_entry_points_compose_to_kda_fwd(gpu):
 
 
 @pytest.mark.parametrize("N,H,T,expect", [
-    (64, 2, 1024, "segmented"),  # 128 pairs, 64 chunks per sequence
+    (64, 2, 896, "segmented"),   # 128 pairs, 56 chunks per sequence
+    (64, 2, 880, "fused"),       # 128 pairs, 55 chunks: too short to segment
     (43, 3, 2048, "fused"),      # 129 pairs: two segments per pair no longer fit one round
-    (32, 3, 1008, "fused"),      # 96 pairs, 63 chunks per sequence: too short to segment
-    (19, 5, 1008, "split"),      # 95 pairs, too short to segment
-    (19, 5, 1024, "segmented"),  # 95 pairs of 64 chunks
+    (27, 3, 896, "segmented"),   # 81 pairs of 56 chunks
+    (27, 3, 640, "fused"),       # 81 pairs of 40 chunks: above 80 pairs the threshold is 56
+    (20, 4, 640, "segmented"),   # 80 pairs of 40 chunks: up to 80 pairs it is 40
+    (20, 4, 624, "fused"),       # 80 pairs of 39 chunks: the single pass from 64 pairs on
+    (21, 3, 624, "split"),       # 63 pairs of 39 chunks
+    (21, 3, 640, "segmented"),   # 63 pairs of 40 chunks
     (8, 4, 128, "fused"),        # 32 pairs of 8 chunks: short sequences take the single pass
     (8, 4, 144, "split"),        # 9 chunks per sequence
 ])
