@@ -27,10 +27,11 @@ def np64(t: torch.Tensor) -> np.ndarray:
 
 def run_gpu(w, dev, *, state_dtype=torch.float32, fp32_compute=False, workspace=None, final=True,
             initial_state="from_workload", out=None, final_state=None, path="auto", beta=None,
-            bf16_resident_state=False):
+            bf16_resident_state=False, scale=None):
     """Run workload w on the GPU; returns (out [T_tot,H,128] tensor, final_state tensor or None).
     `path` selects the kernels ("auto", "split", "fused"); `beta` replaces the
-    device copy of beta_raw (same shape and values, e.g. at an odd address)."""
+    device copy of beta_raw (same shape and values, e.g. at an odd address);
+    `scale` is the read scale (None: 128^-1/2)."""
     q, k, v, g, b = (t.to(dev) for t in (w.q, w.k, w.v, w.g_raw, w.beta_raw))
     if beta is not None:
         b = beta
@@ -39,7 +40,8 @@ def run_gpu(w, dev, *, state_dtype=torch.float32, fp32_compute=False, workspace=
         s0 = s0.to(dev, state_dtype)
     if w.packed:
         cu = w.cu_seqlens().to(dev)
-        o, s = kda.fwd(q, k, v, g, b, lower_bound=w.lower_bound, initial_state=s0, output_final_state=final,
+        o, s = kda.fwd(q, k, v, g, b, lower_bound=w.lower_bound, scale=scale, initial_state=s0,
+                       output_final_state=final,
                        cu_seqlens=cu, fp32_compute=fp32_compute, workspace=workspace, out=out,
                        final_state=final_state, path=path, bf16_resident_state=bf16_resident_state)
     else:
@@ -47,7 +49,7 @@ def run_gpu(w, dev, *, state_dtype=torch.float32, fp32_compute=False, workspace=
         shp = (B, T, w.H, 128)
         gshp = shp if g.dim() == 3 else shp[:3]
         o, s = kda.fwd(q.view(shp), k.view(shp), v.view(shp), g.view(gshp), b.view(B, T, w.H),
-                       lower_bound=w.lower_bound, initial_state=s0, output_final_state=final,
+                       lower_bound=w.lower_bound, scale=scale, initial_state=s0, output_final_state=final,
                        fp32_compute=fp32_compute, workspace=workspace,
                        out=None if out is None else out.view(shp), final_state=final_state, path=path,
                        bf16_resident_state=bf16_resident_state)
@@ -63,16 +65,17 @@ def _gate(w):
     return g[..., None].expand(*g.shape, 128) if g.dim() == 2 else g
 
 
-def run_oracle(w, pairs=None, threads=0):
+def run_oracle(w, pairs=None, threads=0, scale=None):
     """fp64 token oracle on the whole workload (pairs=None) or on the listed
-    (sequence, head) pairs. Returns {(n, h): (o [L,128], S [128,128])}."""
+    (sequence, head) pairs, with read scale `scale` (None: 128^-1/2).
+    Returns {(n, h): (o [L,128], S [128,128])}."""
     offs = w.offsets()
     f = lambda t: t.to(torch.float32).numpy()  # noqa: E731  exact widening of bf16/fp32
     res = {}
     if pairs is None:
         o, S = oracle.token_forward(f(w.q), f(w.k), f(w.v), f(_gate(w)), f(w.beta_raw), offs,
                                     None if w.initial_state is None else w.initial_state.numpy(),
-                                    lower_bound=w.lower_bound, threads=threads)
+                                    lower_bound=w.lower_bound, scale=scale, threads=threads)
         for n in range(w.N):
             for h in range(w.H):
                 res[(n, h)] = (o[offs[n]:offs[n + 1], h], S[n, h])
@@ -86,7 +89,7 @@ def run_oracle(w, pairs=None, threads=0):
         sl = lambda t: f(t[a:e][:, hs])  # noqa: E731
         s0 = None if w.initial_state is None else w.initial_state[n][hs].numpy()[None]
         o, S = oracle.token_forward(sl(w.q), sl(w.k), sl(w.v), sl(_gate(w)), sl(w.beta_raw), [0, e - a], s0,
-                                    lower_bound=w.lower_bound, threads=threads)
+                                    lower_bound=w.lower_bound, scale=scale, threads=threads)
         for i, h in enumerate(hs):
             res[(n, h)] = (o[:, i], S[0, i])
     return res
