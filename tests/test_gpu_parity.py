@@ -303,3 +303,24 @@ def test_pair_counts_select_each_recurrence_shape(gpu, nseq, H):
     _banner(f"split path: {nseq} sequences x {H} heads = {nseq * H} pairs")
     w = workloads.make(None, H, seed=41 + nseq, init_std=0.02, lens_drawn=(1, 70, nseq))
     compare(w, *run_gpu(w, gpu, path="split"), run_oracle(w), bf16_tol, f"{nseq * H} pairs")
+
+
+@pytest.mark.parametrize("nseq,H,dtype", [(2, 2, torch.bfloat16), (25, 4, torch.bfloat16), (3, 2, torch.float32)])
+def test_stage_entry_points_compose_to_kda_fwd(gpu, nseq, H, dtype):
+    """kda_fwd_prepare followed by kda_fwd_recur gives kda_fwd's results bitwise on the
+    two-kernel path: the look-ahead recurrence (4 pairs), the consumer-wave one (100)
+    and the fp32 kernels (fp32 I/O)."""
+    _banner(f"split path staged vs whole: {nseq} x {H}, {dtype}")
+    w = workloads.make(None, H, seed=90 + nseq, dtype=dtype, init_std=0.02, lens_drawn=(1, 300, nseq))
+    args = [t.to(gpu) for t in (w.q, w.k, w.v, w.g_raw, w.beta_raw)]
+    cu = w.cu_seqlens().to(gpu)
+    s0 = w.initial_state.to(gpu)
+    whole = kda.prepare_call(*args, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu, path="split")
+    whole.run()
+    staged = kda.prepare_call(*args, lower_bound=w.lower_bound, initial_state=s0, cu_seqlens=cu, path="split")
+    staged.prepare()
+    staged.recur()
+    torch.cuda.synchronize(gpu)
+    assert torch.equal(whole.out, staged.out) and torch.equal(whole.final_state, staged.final_state)
+    tol = f32_tol if dtype == torch.float32 else bf16_tol
+    compare(w, staged.out, staged.final_state, run_oracle(w), tol, f"split staged {nseq}x{H}")
