@@ -9,12 +9,14 @@ already resident in HBM: the chunk map plus the single-pass kernel (path
 correction ("segmented"), or the chunk-parallel and recurrence kernels
 ("split"); "auto" is the library's own rule. Protocol of the FlashKDA
 benchmarks (review page, section 3): W untimed warmup steps, then R repeats of
-K timed steps, each repeat between two device synchronisations; ms_per_step is
-the median over the repeats. HIP events recorded on the launch stream around
-each kernel call give each kernel's duration per step inside the same timed
-region (the fused call's interval also holds the few-microsecond chunk map);
-per kernel the line reports the median over repeats of the per-repeat mean,
-and the median and minimum over all timed steps. The other path is then timed
+K timed steps (one kda_fwd call each), each repeat between two device
+synchronisations; ms_per_step is the median over the repeats. After each
+repeat the same K steps run again with HIP events recorded on the launch stream
+around each stage call, which give each kernel's duration per step (a call's
+interval also holds the few-microsecond chunk map and the launch gap); per
+kernel the line reports the median over repeats of the per-repeat mean, and the
+median and minimum over all instrumented steps. The events stay out of the
+wall-clock repeats, since each lengthens a short step. The other path is then timed
 the same way for comparison, and the extra workloads (default c4 and c5) get
 sub-records of the same form. Prints ONE JSON line. Headline workload c3 (8
 packed sequences x 8192 tokens, H=32, D=128, bf16), the metric's head count.
@@ -142,9 +144,12 @@ def _median(xs):
 
 
 def time_path(call, path, steps, warmup, repeats):
-    """Warm up, then time `repeats` runs of `steps` forwards on `path`. Returns the
-    wall ms per step of each repeat and, per kernel call, its event-measured ms of
-    every timed step (grouped by repeat)."""
+    """Warm up, then per repeat: `steps` plain forwards (one kda_fwd call each)
+    between two device synchronisations, then as many again with HIP events
+    around each stage call. Returns the wall ms per step of each plain run and,
+    per kernel call, its event-measured ms of every instrumented step (grouped by
+    repeat). The events stay out of the wall-clock runs: each is a timestamp the
+    stream stops for, which lengthens a short step by up to ~12% (C2)."""
     import torch
     if path in ("fused", "recurrent"):
         stages = [("kf_fused" if path == "fused" else "kr_recurrent", call.run)]
@@ -153,21 +158,23 @@ def time_path(call, path, steps, warmup, repeats):
     else:
         stages = [("k1_mfma", call.prepare), ("k2_mfma", call.recur)]
     for _ in range(warmup):
-        for _, fn in stages:
-            fn()
+        call.run()
     stream = torch.cuda.current_stream()
     walls, kern = [], {name: [] for name, _ in stages}
     for _ in range(repeats):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        for _ in range(steps):
+            call.run()
+        torch.cuda.synchronize()
+        walls.append((time.perf_counter() - t0) * 1e3 / steps)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
         for i in range(steps):
             ev[i][0].record(stream)
             for j, (_, fn) in enumerate(stages):
                 fn()
                 ev[i][j + 1].record(stream)
         torch.cuda.synchronize()
-        walls.append((time.perf_counter() - t0) * 1e3 / steps)
         for j, (name, _) in enumerate(stages):
             kern[name].append([e[j].elapsed_time(e[j + 1]) for e in ev])
     return walls, kern
